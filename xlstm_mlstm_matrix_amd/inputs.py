@@ -1,0 +1,240 @@
+"""Seeded synthetic inputs for the mLSTM cell workloads.
+
+This module only draws random numbers and casts them; it holds none of the
+cell's arithmetic, so the float64 oracle and the HIP path can both be fed from
+it without sharing any of the method.
+
+Recipe (every value is drawn in float64 from numpy's PCG64, then cast once to
+the I/O dtype; bf16 casts round to nearest even):
+
+* per (b, h) pair of a prefill workload a child generator seeded with
+  ``SeedSequence([seed, b, h])`` draws, in this order and in C order,
+  q[T, d_qk], k[T, d_qk], v[T, d_v], i_pre[T], f_raw[T], o_pre[T, d_v],
+  then C0[d_qk, d_v], n0[d_qk], m0 (when the workload has an initial state);
+* k is multiplied by 1/sqrt(d_qk) and the log forget gate input is
+  f_pre = logsigmoid(f_raw), i.e. the forget gate handed to the cell is already
+  in log space (the cell itself applies exp, never a sigmoid);
+* a decode workload draws step t's inputs from ``SeedSequence([seed, 1, t])``
+  (so any single step is reproducible alone) and its initial state from
+  ``SeedSequence([seed, 0])``.
+
+Because the draws are per (b, h) (prefill) or per step (decode), a subset of
+the pairs or steps can be regenerated without drawing the rest, which is how
+the oracle is fed a bounded sample of a large workload.
+"""
+from __future__ import annotations
+
+import math
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "workload", "gen_prefill", "gen_decode_state",
+           "gen_decode_step", "to_io_dtype", "logsigmoid"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: shapes, I/O dtype and input distributions."""
+    name: str
+    seed: int
+    kind: str                  # "prefill" or "decode"
+    B: int
+    H: int
+    T: int                     # tokens (prefill) or consecutive steps (decode)
+    d_qk: int
+    d_v: int
+    chunk: int                 # prefill chunk length (0 for decode)
+    io: str                    # "f32" or "bf16": dtype of q, k, v, o_pre and h
+    i_mean: float
+    i_std: float
+    f_mean: float              # f_pre = logsigmoid(N(f_mean, f_std))
+    f_std: float
+    init_state: Optional[Dict[str, Tuple[str, float, float]]] = None
+    # init_state entries: name -> ("normal", mean, std) | ("uniform", lo, hi) | ("zero", 0, 0)
+    description: str = ""
+
+
+WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
+    Workload("tiny_f32", 1, "prefill", 1, 1, 64, 16, 16, 16, "f32",
+             0.0, 1.0, 3.0, 1.0, None,
+             "Tiny mLSTM fwd, fp32: B=1 H=1 T=64 d_qk=d_v=16 chunk=16, zero initial state"),
+    Workload("small_f32", 2, "prefill", 4, 4, 1024, 64, 64, 64, "f32",
+             0.0, 1.0, 3.0, 1.0,
+             {"C0": ("normal", 0.0, 0.1), "n0": ("normal", 0.0, 0.1), "m0": ("zero", 0.0, 0.0)},
+             "Small mLSTM fwd, fp32: B=4 H=4 T=1024 d_qk=d_v=64 chunk=64, random initial state"),
+    Workload("prefill_7b_bf16", 3, "prefill", 8, 8, 4096, 256, 512, 64, "bf16",
+             -2.0, 1.0, 4.0, 1.5, None,
+             "7B-layer-shaped prefill, bf16 I/O, fp32 state: B=8 H=8 T=4096 d_qk=256 d_v=512 chunk=64"),
+    Workload("prefill_long_bf16", 4, "prefill", 1, 8, 65536, 256, 512, 128, "bf16",
+             -2.0, 1.0, 4.0, 1.5, None,
+             "Long-context prefill, bf16 I/O, fp32 state: B=1 H=8 T=65536 d_qk=256 d_v=512 chunk=128"),
+    Workload("decode_bf16", 5, "decode", 256, 8, 1024, 256, 512, 0, "bf16",
+             -2.0, 1.0, 4.0, 1.5,
+             {"C0": ("normal", 0.0, 0.05), "n0": ("normal", 0.0, 0.05), "m0": ("uniform", -1.0, 1.0)},
+             "Recurrent decode, bf16 q/k/v, fp32 state: B=256 H=8 d_qk=256 d_v=512, 1024 steps"),
+]}
+
+
+def workload(name: str, **override) -> Workload:
+    """Return a named workload, optionally with some fields replaced (e.g. a
+    reduced B for a parity test)."""
+    w = WORKLOADS[name]
+    if override:
+        d = dict(w.__dict__)
+        d.update(override)
+        w = Workload(**d)
+    return w
+
+
+def logsigmoid(x: np.ndarray) -> np.ndarray:
+    """log(1/(1+e^{-x})) evaluated without overflow, in float64.
+
+    Part of the input recipe (the forget-gate input is drawn as the log of a
+    sigmoid), not of the cell."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))
+
+
+def to_io_dtype(x: np.ndarray, io: str):
+    """Cast a float64 array to the workload's I/O dtype.
+
+    Returns a torch CPU tensor (float32 or bfloat16, the latter rounded to
+    nearest even from the float32 value; float64 -> float32 is itself RNE and
+    float32 -> bfloat16 RNE of it is what every consumer sees)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if io == "f32":
+        return t
+    if io == "bf16":
+        return t.to(torch.bfloat16)
+    raise ValueError(f"unknown io dtype {io!r}")
+
+
+def _draw_state(rng: np.random.Generator, spec, shape):
+    kind, a, b = spec
+    if kind == "normal":
+        return rng.normal(a, b, size=shape)
+    if kind == "uniform":
+        return rng.uniform(a, b, size=shape)
+    if kind == "zero":
+        return np.zeros(shape)
+    raise ValueError(kind)
+
+
+def _draw_pair(w: Workload, b: int, h: int, T: int):
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, b, h])))
+    q = rng.standard_normal((T, w.d_qk))
+    k = rng.standard_normal((T, w.d_qk)) * (1.0 / math.sqrt(w.d_qk))
+    v = rng.standard_normal((T, w.d_v))
+    i_pre = rng.normal(w.i_mean, w.i_std, size=T)
+    f_pre = logsigmoid(rng.normal(w.f_mean, w.f_std, size=T))
+    o_pre = rng.standard_normal((T, w.d_v))
+    st = None
+    if w.init_state is not None:
+        C0 = _draw_state(rng, w.init_state["C0"], (w.d_qk, w.d_v))
+        n0 = _draw_state(rng, w.init_state["n0"], (w.d_qk,))
+        m0 = _draw_state(rng, w.init_state["m0"], ())
+        st = (C0, n0, np.float64(m0))
+    return q, k, v, i_pre, f_pre, o_pre, st
+
+
+def gen_prefill(w: Workload, pairs: Optional[Sequence[Tuple[int, int]]] = None,
+                T: Optional[int] = None, threads: int = 8):
+    """Draw a prefill workload.
+
+    Returns a dict of torch CPU tensors: q, k [P, T, d_qk], v, o_pre [P, T, d_v]
+    in the I/O dtype, i_pre, f_pre [P, T] float32, and C0 [P, d_qk, d_v], n0
+    [P, d_qk], m0 [P] float32 (None when the workload starts from the zero
+    state), where P runs over ``pairs`` (default: every (b, h) in b-major
+    order, so P = B*H and a reshape to [B, H, ...] is free).  ``T`` truncates
+    the sequence (the first T tokens of each pair are identical to those of
+    the full workload)."""
+    import torch
+    if pairs is None:
+        pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    T = w.T if T is None else T
+    P = len(pairs)
+    cast = torch.bfloat16 if w.io == "bf16" else torch.float32
+    out = {
+        "q": torch.empty((P, T, w.d_qk), dtype=cast),
+        "k": torch.empty((P, T, w.d_qk), dtype=cast),
+        "v": torch.empty((P, T, w.d_v), dtype=cast),
+        "i_pre": torch.empty((P, T), dtype=torch.float32),
+        "f_pre": torch.empty((P, T), dtype=torch.float32),
+        "o_pre": torch.empty((P, T, w.d_v), dtype=cast),
+    }
+    has_state = w.init_state is not None
+    if has_state:
+        out["C0"] = torch.empty((P, w.d_qk, w.d_v), dtype=torch.float32)
+        out["n0"] = torch.empty((P, w.d_qk), dtype=torch.float32)
+        out["m0"] = torch.empty((P,), dtype=torch.float32)
+
+    def work(p):
+        b, h = pairs[p]
+        q, k, v, i_pre, f_pre, o_pre, st = _draw_pair(w, b, h, w.T)
+        out["q"][p] = to_io_dtype(q[:T], w.io)
+        out["k"][p] = to_io_dtype(k[:T], w.io)
+        out["v"][p] = to_io_dtype(v[:T], w.io)
+        out["o_pre"][p] = to_io_dtype(o_pre[:T], w.io)
+        out["i_pre"][p] = torch.from_numpy(i_pre[:T].astype(np.float32))
+        out["f_pre"][p] = torch.from_numpy(f_pre[:T].astype(np.float32))
+        if has_state:
+            out["C0"][p] = torch.from_numpy(st[0].astype(np.float32))
+            out["n0"][p] = torch.from_numpy(st[1].astype(np.float32))
+            out["m0"][p] = float(np.float32(st[2]))
+
+    if threads > 1 and P > 1:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(work, range(P)))
+    else:
+        for p in range(P):
+            work(p)
+    if not has_state:
+        out["C0"] = out["n0"] = out["m0"] = None
+    return out
+
+
+def gen_decode_state(w: Workload, B: Optional[int] = None):
+    """Initial state of a decode workload: C0 [B,H,d_qk,d_v], n0 [B,H,d_qk],
+    m0 [B,H], float32 torch CPU tensors (``B`` may reduce the batch; the
+    first B rows equal those of the full workload)."""
+    import torch
+    B = w.B if B is None else B
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 0])))
+    C0 = torch.empty((B, w.H, w.d_qk, w.d_v), dtype=torch.float32)
+    n0 = torch.empty((B, w.H, w.d_qk), dtype=torch.float32)
+    m0 = torch.empty((B, w.H), dtype=torch.float32)
+    # drawn batch row by batch row so a reduced B is a prefix of the full draw
+    for b in range(B):
+        C0[b] = torch.from_numpy(_draw_state(rng, w.init_state["C0"], (w.H, w.d_qk, w.d_v)).astype(np.float32))
+        n0[b] = torch.from_numpy(_draw_state(rng, w.init_state["n0"], (w.H, w.d_qk)).astype(np.float32))
+        m0[b] = torch.from_numpy(np.asarray(_draw_state(rng, w.init_state["m0"], (w.H,))).astype(np.float32))
+    return C0, n0, m0
+
+
+def gen_decode_step(w: Workload, t: int, B: Optional[int] = None):
+    """Inputs of decode step t: q, k [B,H,d_qk], v, o_pre [B,H,d_v] in the I/O
+    dtype, i_pre, f_pre [B,H] float32 (torch CPU tensors).  A reduced ``B``
+    is a prefix of the full step's batch."""
+    import torch
+    B = w.B if B is None else B
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 1, t])))
+    H = w.H
+    q = np.empty((B, H, w.d_qk)); k = np.empty((B, H, w.d_qk)); v = np.empty((B, H, w.d_v))
+    i_pre = np.empty((B, H)); f_pre = np.empty((B, H)); o_pre = np.empty((B, H, w.d_v))
+    for b in range(B):  # batch row by batch row: a reduced B is a prefix
+        q[b] = rng.standard_normal((H, w.d_qk))
+        k[b] = rng.standard_normal((H, w.d_qk)) * (1.0 / math.sqrt(w.d_qk))
+        v[b] = rng.standard_normal((H, w.d_v))
+        i_pre[b] = rng.normal(w.i_mean, w.i_std, size=H)
+        f_pre[b] = logsigmoid(rng.normal(w.f_mean, w.f_std, size=H))
+        o_pre[b] = rng.standard_normal((H, w.d_v))
+    return {
+        "q": to_io_dtype(q, w.io), "k": to_io_dtype(k, w.io), "v": to_io_dtype(v, w.io),
+        "i_pre": torch.from_numpy(i_pre.astype(np.float32)),
+        "f_pre": torch.from_numpy(f_pre.astype(np.float32)),
+        "o_pre": to_io_dtype(o_pre, w.io),
+    }
