@@ -1,0 +1,280 @@
+"""Benchmark of the mLSTM cell forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one chunkwise forward pass (mlstm_fwd_chunkwise) over the
+7B-layer-shaped prefill workload: B=8 H=8 T=4096 d_qk=256 d_v=512 chunk=64,
+bf16 I/O, float32 state, synthetic seeded inputs already resident in HBM.
+`value` is prefill tokens/s (B*T per step).  The same JSON line also carries
+the decode workload (B=256 H=8, 1024 consecutive in-place mlstm_step calls)
+and the long-context prefill (B=1 H=8 T=65536 chunk=128), each with its own
+roofline, and the float64 oracle timed on the host cores over a bounded
+sample (`cpu_baseline`).
+
+Kernel times come from HIP events recorded on the stream the library
+launches on (torch's current stream).  Rooflines use algorithmic work:
+  prefill flops per token-head  (L+1)(d_qk+d_v) + 4 d_qk d_v + 4 d_qk
+  prefill bytes per token-head  2(2 d_qk + 2 d_v) + 2 d_v + 8   (bf16 q,k,v,o~ in, h out, f32 gates)
+  decode bytes per pair-step    8(d_qk d_v + d_qk + 1) + 2(2 d_qk + 2 d_v) + 8
+against MI355X peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["xlstm_mlstm_matrix_amd/csrc/prefill_kernel.hpp", "xlstm_mlstm_matrix_amd/csrc/prefill.hip",
+                  "xlstm_mlstm_matrix_amd/csrc/step.hip"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def src_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_work(w):
+    L, dk, dv = w.chunk, w.d_qk, w.d_v
+    th = w.B * w.H * w.T
+    flops = th * ((L + 1) * (dk + dv) + 4 * dk * dv + 4 * dk)
+    io_bytes = th * (2 * (2 * dk + 2 * dv) + 2 * dv + 8)
+    state_bytes = w.B * w.H * (dk * dv + dk + 1) * 4  # final state written
+    return flops, io_bytes + state_bytes
+
+
+def decode_work(w):
+    dk, dv = w.d_qk, w.d_v
+    pairs = w.B * w.H
+    state = pairs * 8 * (dk * dv + dk + 1)
+    io = pairs * (2 * (2 * dk + 2 * dv) + 8)
+    return state, state + io
+
+
+def traffic_record(name):
+    """Measured HBM bytes per launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha") != src_hash(KERNEL_SOURCES):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    def __init__(self, torch):
+        self.torch = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.torch.cuda.synchronize()
+        self.a.record(self.torch.cuda.current_stream())
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record(self.torch.cuda.current_stream())
+        self.torch.cuda.synchronize()
+        self.ms = self.a.elapsed_time(self.b)
+
+
+def bench_prefill(torch, I, binding, name, steps, warmup, variant="auto"):
+    w = I.workload(name)
+    t0 = time.time()
+    d = I.gen_prefill(w, threads=16)
+    g = {k: (v.cuda().reshape(w.B, w.H, *v.shape[1:]) if v is not None else None) for k, v in d.items()}
+    del d
+    log(f"{name}: inputs ready in {time.time() - t0:.1f}s")
+    args = [g[k] for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")]
+    h = torch.empty((w.B, w.H, w.T, w.d_v), dtype=args[0].dtype, device="cuda")
+    C = torch.empty((w.B, w.H, w.d_qk, w.d_v), device="cuda")
+    n = torch.empty((w.B, w.H, w.d_qk), device="cuda")
+    m = torch.empty((w.B, w.H), device="cuda")
+    io = binding.BF16 if w.io == "bf16" else binding.F32
+    ws = torch.empty(max(1, binding.workspace_size(w.B, w.H, w.T, w.d_qk, w.d_v, w.chunk, io, variant)),
+                     dtype=torch.uint8, device="cuda")
+
+    def run():
+        binding.fwd_chunkwise(*args, chunk=w.chunk, variant=variant, h=h, C_T=C, n_T=n, m_T=m,
+                              workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    with Timer(torch) as tm:
+        for _ in range(steps):
+            run()
+    ms = tm.ms / steps
+    flops, nbytes = prefill_work(w)
+    tokens = w.B * w.T
+    log(f"{name}: {ms:.3f} ms/step, {tokens / ms * 1e3:.3e} tokens/s, "
+        f"{flops / ms / 1e9:.1f} TFLOP/s, {nbytes / ms / 1e6:.0f} GB/s")
+    return w, ms, flops, nbytes, (g, h, C, n, m)
+
+
+def bench_decode(torch, I, binding, warmup_passes=1):
+    w = I.workload("decode_bf16")
+    t0 = time.time()
+    C0, n0, m0 = (x.cuda() for x in I.gen_decode_state(w, threads=16))
+    steps = {}
+    chunk = 128
+    parts = {k: [] for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")}
+    for s0 in range(0, w.T, chunk):
+        st = I.gen_decode_steps(w, range(s0, min(w.T, s0 + chunk)), threads=16)
+        for k in parts:
+            parts[k].append(st[k].cuda())
+    steps = {k: torch.cat(v) for k, v in parts.items()}
+    log(f"decode: inputs ready in {time.time() - t0:.1f}s")
+    C, n, m = C0.clone(), n0.clone(), m0.clone()
+    h = torch.empty((w.B, w.H, w.d_v), dtype=torch.bfloat16, device="cuda")
+    keys = ("q", "k", "v", "i_pre", "f_pre", "o_pre")
+
+    def one_pass():
+        for t in range(w.T):
+            binding.step(*(steps[k][t] for k in keys), C, n, m, h=h, C_out=C, n_out=n, m_out=m)
+
+    for _ in range(warmup_passes):
+        one_pass()
+    C.copy_(C0); n.copy_(n0); m.copy_(m0)
+    with Timer(torch) as tm:
+        one_pass()
+    ms = tm.ms / w.T
+    state_bytes, total_bytes = decode_work(w)
+    log(f"decode: {ms:.4f} ms/step, state {state_bytes / ms / 1e6:.0f} GB/s, "
+        f"total {total_bytes / ms / 1e6:.0f} GB/s, {w.B / ms * 1e3:.3e} tokens/s")
+    return w, ms, state_bytes, total_bytes
+
+
+def cpu_baseline(I, pairs_sample):
+    """The float64 oracle on the host cores over a bounded sample of the
+    prefill workload: `pairs_sample` (b, h) pairs, full sequence each."""
+    import oracle
+    w = I.workload("prefill_7b_bf16")
+    d = I.gen_prefill(w, pairs=pairs_sample, threads=16)
+    cores = len(os.sched_getaffinity(0))
+    threads = min(cores, len(pairs_sample))
+    orc = oracle.load()
+    t0 = time.time()
+    orc.forward(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"], threads=threads)
+    dt = time.time() - t0
+    frac = len(pairs_sample) / (w.B * w.H)
+    tokens_per_s = (w.B * w.T) * frac / dt   # the sample's share of the workload's tokens
+    log(f"cpu oracle: {len(pairs_sample)} pairs x {w.T} tokens in {dt:.2f}s on {threads} threads")
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(pairs_sample)} of {w.B * w.H} (batch, head) pairs of the 7B-layer prefill "
+                      f"workload, full T={w.T} each, float64 sequential recurrence, OpenMP over pairs; "
+                      f"rate = sampled tokens x (pairs sampled / all pairs) / wall time "
+                      f"({dt:.2f} s wall)",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-pairs", type=int, default=16)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the mLSTM path has no "
+              "multi-GPU component in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from xlstm_mlstm_matrix_amd import binding, inputs as I
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: 3 x 1 GiB device copies done")
+        del src, dst
+
+    w, ms, flops, nbytes, _keep = bench_prefill(torch, I, binding, "prefill_7b_bf16", args.steps, args.warmup)
+    del _keep
+    torch.cuda.empty_cache()
+    tflops = flops / ms / 1e9
+    gbs = nbytes / ms / 1e6
+    rec = {
+        "metric": "mLSTM prefill tokens/s (7B-layer-shaped, chunkwise, bf16 I/O, fp32 state)",
+        "value": w.B * w.T / ms * 1e3,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, distributions of the workload spec)",
+        "config": {"workload": "prefill B=8 H=8 T=4096 d_qk=256 d_v=512 chunk=64 bf16 I/O fp32 state",
+                   "global_batch": w.B, "seq_len": w.T, "heads": w.H, "d_qk": w.d_qk, "d_v": w.d_v,
+                   "chunk": w.chunk, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": traffic_record("prefill_7b"),
+                     "kernel": "mlstm_chunk_kernel (fused chunkwise forward)",
+                     "mfma": {"achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                              "frac": tflops / PEAK_BF16_TFLOPS},
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes},
+    }
+
+    if not args.no_long:
+        try:
+            wl, msl, fl, bl, _keep = bench_prefill(torch, I, binding, "prefill_long_bf16",
+                                                  max(3, args.steps // 4), 1)
+            del _keep
+            torch.cuda.empty_cache()
+            rec["long_context"] = {
+                "workload": "prefill B=1 H=8 T=65536 d_qk=256 d_v=512 chunk=128 bf16 I/O (segmented schedule)",
+                "ms_per_step": msl, "tokens_per_s": wl.B * wl.T / msl * 1e3,
+                "mfma_frac": fl / msl / 1e9 / PEAK_BF16_TFLOPS, "hbm_frac": bl / msl / 1e6 / PEAK_HBM_GBS}
+        except Exception as e:  # reported, not hidden
+            rec["long_context"] = {"error": str(e)}
+            log(f"long context: {e}")
+
+    if not args.no_decode:
+        wd, msd, sb, tb = bench_decode(torch, I, binding)
+        rec["decode"] = {
+            "workload": "decode B=256 H=8 d_qk=256 d_v=512, 1024 in-place mlstm_step calls, bf16 I/O fp32 state",
+            "ms_per_step": msd, "tokens_per_s": wd.B / msd * 1e3,
+            "state_GBs": sb / msd / 1e6,
+            "roofline": {"bound": "hbm", "achieved": tb / msd / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": tb / msd / 1e6 / PEAK_HBM_GBS, "traffic": traffic_record("decode"),
+                         "kernel": "mlstm_step_kernel", "algorithmic_bytes_per_launch": tb}}
+
+    if not args.no_cpu:
+        Pn = max(1, args.cpu_pairs)
+        sample = [(p // 8, p % 8) for p in range(0, 64, max(1, 64 // Pn))][:Pn]
+        rec["cpu_baseline"] = cpu_baseline(I, sample)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+/*
+ * mlstm.h -- C ABI of the MI355X (gfx950) mLSTM cell forward library.
+ *
+ * The operation is the mLSTM cell of xLSTM: exponential input and forget
+ * gates in log space with the stabilizer m_t = max(f~_t + m_{t-1}, i~_t)
+ * (xLSTM note, section "sLSTM"), the matrix memory C_t = f_t C_{t-1} +
+ * i_t v_t k_t^T, the normalizer n_t = f_t n_{t-1} + i_t k_t and the read-out
+ * h_t = o_t * C_t q_t / max(|n_t^T q_t|, 1) with o_t = sigmoid(o~_t) (same
+ * note, section "mLSTM (matrix LSTM)" and its example recurrent step).  The
+ * library keeps the state in stabilized variables:
+ *
+ *   C'_t = C_t e^{-m_t}  [d_qk x d_v, key index first],
+ *   n'_t = n_t e^{-m_t}  [d_qk],   m_t,
+ *
+ * and evaluates the read-out as sigmoid(o~_t) * C'^T q / max(|n'^T q|, e^{-m_t}),
+ * which equals the unstabilized formula exactly.  f~ is the log of the forget
+ * gate: the library applies exp to it and nothing else (no sigmoid).
+ *
+ * Two entry points compute it:
+ *   mlstm_fwd_chunkwise -- a whole sequence, chunkwise-parallel (prefill);
+ *   mlstm_step          -- one token of the recurrence (decode).
+ *
+ * Conventions shared by every call:
+ *  - All tensor pointers are DEVICE pointers (HIP memory on the current
+ *    device), dense, C-contiguous, in the layouts given per argument.  The
+ *    caller owns every buffer; the library allocates nothing, keeps no state
+ *    between calls and never synchronizes: work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the null stream) and the call returns at once.
+ *  - q, k, v, o_pre and h have the I/O dtype `io` (float32 or bfloat16);
+ *    i_pre, f_pre and the state (C, n, m) are always float32.
+ *  - Arguments are validated on the host before any device work.  An invalid
+ *    call returns an error status and enqueues nothing.  A HIP launch error
+ *    returns MLSTM_ERR_HIP.  No exception crosses the ABI.
+ *  - Supported shapes: 1 <= d_qk <= 256 and 1 <= d_v <= 512, both multiples
+ *    of 16; chunk in {16, 32, 64, 128}; any T >= 1; B, H >= 1.
+ */
+#ifndef MLSTM_H
+#define MLSTM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLSTM_F32 = 0,   /* float32 */
+    MLSTM_BF16 = 1   /* bfloat16 (outputs rounded to nearest even) */
+} mlstm_dtype_t;
+
+typedef enum {
+    MLSTM_OK = 0,
+    MLSTM_ERR_NULL = 1,        /* a required pointer is NULL */
+    MLSTM_ERR_SHAPE = 2,       /* a size is <= 0 or the byte sizes overflow */
+    MLSTM_ERR_UNSUPPORTED = 3, /* valid but not implemented: d_qk, d_v, chunk, dtype */
+    MLSTM_ERR_STATE_ARGS = 4,  /* initial or final state given only in part */
+    MLSTM_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the query says */
+    MLSTM_ERR_ALIAS = 6,       /* buffers overlap in a way the call does not allow */
+    MLSTM_ERR_HIP = 7          /* the HIP runtime reported an error */
+} mlstm_status_t;
+
+/* Kernel strategy of the chunkwise forward (the result is the same up to
+ * rounding; only the schedule differs). */
+typedef enum {
+    MLSTM_VARIANT_AUTO = 0,    /* chosen from the shape (what mlstm_fwd_chunkwise does) */
+    MLSTM_VARIANT_FUSED = 1,   /* one pass; each workgroup walks all chunks of its sequence */
+    MLSTM_VARIANT_SEGSCAN = 2  /* sequence split into segments: local states, a scan over
+                                  segments, then the fused pass seeded per segment */
+} mlstm_variant_t;
+
+/* Human-readable name of a status (static string, never NULL). */
+const char *mlstm_status_string(mlstm_status_t s);
+
+/* Library version string (static). */
+const char *mlstm_version(void);
+
+/*
+ * Bytes of device workspace mlstm_fwd_chunkwise needs for this shape with
+ * MLSTM_VARIANT_AUTO (written to *bytes; 0 means none).  Host-only: touches
+ * no device.  The segment-scan variant keeps one float32 state per segment
+ * boundary in it.
+ */
+mlstm_status_t mlstm_fwd_chunkwise_workspace_size(int B, int H, int T, int d_qk, int d_v,
+                                                  int chunk, mlstm_dtype_t io, size_t *bytes);
+
+/* As above for an explicit variant. */
+mlstm_status_t mlstm_fwd_chunkwise_workspace_size_variant(int B, int H, int T, int d_qk,
+                                                          int d_v, int chunk, mlstm_dtype_t io,
+                                                          mlstm_variant_t variant,
+                                                          size_t *bytes);
+
+/*
+ * Chunkwise-parallel forward over a whole sequence (prefill).
+ *
+ *  q, k      [B, H, T, d_qk]  io dtype   queries, keys (no scaling applied)
+ *  v         [B, H, T, d_v]   io dtype   values
+ *  i_pre     [B, H, T]        float32    input-gate pre-activation i~ (i = e^{i~})
+ *  f_pre     [B, H, T]        float32    log forget gate f~ (f = e^{f~})
+ *  o_pre     [B, H, T, d_v]   io dtype   output-gate pre-activation o~
+ *  C0, n0, m0  [B, H, d_qk, d_v], [B, H, d_qk], [B, H]  float32: initial
+ *            stabilized state, or all three NULL for the zero state
+ *            (C = 0, n = 0, m = 0).
+ *  h         [B, H, T, d_v]   io dtype   output (written)
+ *  C_T, n_T, m_T  same shapes as C0, n0, m0: final stabilized state, or all
+ *            three NULL when not wanted.  C_T may be exactly C0 (same pointer;
+ *            likewise n_T/n0, m_T/m0): the state is then updated in place.
+ *  chunk     chunk length L of the chunkwise form (16, 32, 64 or 128).
+ *  workspace device buffer of at least the queried size (may be NULL when
+ *            the query gives 0); its contents on entry are irrelevant.
+ *
+ * Errors: NULL input/output pointer -> MLSTM_ERR_NULL; state triples given
+ * in part -> MLSTM_ERR_STATE_ARGS; h overlapping any input, or a partial
+ * overlap between state buffers -> MLSTM_ERR_ALIAS; workspace too small ->
+ * MLSTM_ERR_WORKSPACE.
+ */
+mlstm_status_t mlstm_fwd_chunkwise(const void *q, const void *k, const void *v,
+                                   const float *i_pre, const float *f_pre, const void *o_pre,
+                                   const float *C0, const float *n0, const float *m0,
+                                   void *h, float *C_T, float *n_T, float *m_T,
+                                   int B, int H, int T, int d_qk, int d_v, int chunk,
+                                   mlstm_dtype_t io, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
+/* mlstm_fwd_chunkwise with an explicit kernel strategy (for tests and
+ * measurement; AUTO is what mlstm_fwd_chunkwise uses). */
+mlstm_status_t mlstm_fwd_chunkwise_variant(const void *q, const void *k, const void *v,
+                                           const float *i_pre, const float *f_pre,
+                                           const void *o_pre, const float *C0, const float *n0,
+                                           const float *m0, void *h, float *C_T, float *n_T,
+                                           float *m_T, int B, int H, int T, int d_qk, int d_v,
+                                           int chunk, mlstm_dtype_t io, mlstm_variant_t variant,
+                                           void *workspace, size_t workspace_bytes,
+                                           void *stream);
+
+/*
+ * One step of the recurrence for B*H independent cells (decode).
+ *
+ *  q, k      [B, H, d_qk]  io dtype;   v, o_pre [B, H, d_v]  io dtype
+ *  i_pre, f_pre [B, H]     float32
+ *  C_in, n_in, m_in  [B, H, d_qk, d_v], [B, H, d_qk], [B, H] float32: state
+ *            before the token, or all three NULL for the zero state
+ *  h         [B, H, d_v]   io dtype (written)
+ *  C_out, n_out, m_out  state after the token (required).  Each may be
+ *            exactly the matching *_in pointer (in-place update, the usual
+ *            decode loop); any other overlap is MLSTM_ERR_ALIAS.
+ */
+mlstm_status_t mlstm_step(const void *q, const void *k, const void *v,
+                          const float *i_pre, const float *f_pre, const void *o_pre,
+                          const float *C_in, const float *n_in, const float *m_in,
+                          void *h, float *C_out, float *n_out, float *m_out,
+                          int B, int H, int d_qk, int d_v, mlstm_dtype_t io, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLSTM_H */

@@ -1,0 +1,187 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/mlstm.h declares, and rejects invalid calls on the host with the
+exact status before touching any device.
+
+Pointers passed here are fake addresses: the library never dereferences a
+pointer on the host, and every call below fails validation, so no HIP call is
+made."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from xlstm_mlstm_matrix_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mlstm.h")
+
+OK, NULL, SHAPE, UNSUP, STATE, WS, ALIAS = 0, 1, 2, 3, 4, 5, 6
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mlstm_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from xlstm_mlstm_matrix_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) == 7, names
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(mlstm_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    assert set(names) == set(B.SIGNATURES), "binding signatures out of step with the header"
+    for n in names:
+        getattr(lib, n)
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert B.status_string(s).startswith(B.STATUS[s])
+    assert "unknown" in B.status_string(99)
+    assert lib.mlstm_version().decode().startswith("mlstm-gfx950")
+
+
+def ws(*args, variant=0):
+    n = ctypes.c_size_t(12345)
+    s = B.lib().mlstm_fwd_chunkwise_workspace_size_variant(*args, variant, ctypes.byref(n))
+    return s, n.value
+
+
+def test_workspace_query(lib):
+    s, n = ws(8, 8, 4096, 256, 512, 64, B.BF16)
+    assert s == OK and n > 0
+    # the fused schedule keeps only a copy of n0/m0 (B*H*(d_qk+1) floats, padded)
+    s, nf = ws(8, 8, 4096, 256, 512, 64, B.BF16, variant=1)
+    assert s == OK and nf == (64 * 257 + 63) // 64 * 64 * 4
+    # the segmented schedule holds per-segment states
+    s, nseg = ws(8, 8, 4096, 256, 512, 64, B.BF16, variant=2)
+    assert s == OK and nseg > nf + 64 * (256 * 512) * 4
+    assert ws(0, 8, 4096, 256, 512, 64, B.BF16)[0] == SHAPE
+    assert ws(1, 1, 0, 64, 64, 64, B.F32)[0] == SHAPE
+    assert ws(1, 1, 64, 24, 64, 64, B.F32)[0] == UNSUP      # d_qk not a multiple of 16
+    assert ws(1, 1, 64, 64, 528, 64, B.F32)[0] == UNSUP     # d_v > 512
+    assert ws(1, 1, 64, 272, 64, 64, B.F32)[0] == UNSUP     # d_qk > 256
+    assert ws(1, 1, 64, 64, 64, 48, B.F32)[0] == UNSUP      # chunk not supported
+    assert ws(1, 1, 64, 64, 64, 64, 7)[0] == UNSUP          # dtype
+    assert ws(1, 1, 64, 64, 64, 64, B.F32, variant=9)[0] == UNSUP
+    assert B.lib().mlstm_fwd_chunkwise_workspace_size(1, 1, 64, 64, 64, 64, 0, None) == NULL
+
+
+class Fake:
+    """Fake device addresses laid out far apart (never dereferenced)."""
+
+    def __init__(self):
+        self.next = 1 << 40
+
+    def __call__(self, nbytes):
+        a = self.next
+        self.next += (nbytes + (1 << 20)) // (1 << 20) * (1 << 20) + (1 << 20)
+        return a
+
+
+def fwd_args(B_=2, H=3, T=70, dk=64, dv=64, chunk=32, io=B.F32, state=True, out_state=True):
+    fa = Fake()
+    es = 2 if io == B.BF16 else 4
+    P = B_ * H
+    a = dict(q=fa(P * T * dk * es), k=fa(P * T * dk * es), v=fa(P * T * dv * es),
+             i=fa(P * T * 4), f=fa(P * T * 4), o=fa(P * T * dv * es),
+             C0=fa(P * dk * dv * 4) if state else None, n0=fa(P * dk * 4) if state else None,
+             m0=fa(P * 4) if state else None, h=fa(P * T * dv * es),
+             CT=fa(P * dk * dv * 4) if out_state else None, nT=fa(P * dk * 4) if out_state else None,
+             mT=fa(P * 4) if out_state else None)
+    s, n = ws(B_, H, T, dk, dv, chunk, io)
+    assert s == OK
+    a.update(ws=fa(n), wsn=n, dims=(B_, H, T, dk, dv, chunk, io))
+    return a
+
+
+def call_fwd(a, variant=0):
+    return B.lib().mlstm_fwd_chunkwise_variant(
+        a["q"], a["k"], a["v"], a["i"], a["f"], a["o"], a["C0"], a["n0"], a["m0"],
+        a["h"], a["CT"], a["nT"], a["mT"], *a["dims"], variant, a["ws"], a["wsn"], None)
+
+
+def test_fwd_validation(lib):
+    for key in ("q", "k", "v", "i", "f", "o", "h"):
+        a = fwd_args(); a[key] = None
+        assert call_fwd(a) == NULL, key
+    a = fwd_args(); a["dims"] = (2, 3, 0, 64, 64, 32, B.F32)
+    assert call_fwd(a) == SHAPE
+    a = fwd_args(); a["dims"] = (2, 3, 70, 64, 64, 24, B.F32)
+    assert call_fwd(a) == UNSUP
+    a = fwd_args(); a["n0"] = None
+    assert call_fwd(a) == STATE
+    a = fwd_args(); a["mT"] = None
+    assert call_fwd(a) == STATE
+    a = fwd_args(); a["ws"] = None
+    assert call_fwd(a) == WS
+    a = fwd_args(); a["wsn"] -= 4
+    assert call_fwd(a) == WS
+    # aliasing: h over an input, partial overlap of state buffers, workspace over an input
+    a = fwd_args(); a["h"] = a["v"] + 64
+    assert call_fwd(a) == ALIAS
+    a = fwd_args(); a["CT"] = a["C0"] + 4
+    assert call_fwd(a) == ALIAS
+    a = fwd_args(); a["nT"] = a["C0"]
+    assert call_fwd(a) == ALIAS
+    a = fwd_args(); a["ws"] = a["q"]
+    assert call_fwd(a) == ALIAS
+    a = fwd_args(); a["h"] = a["CT"]
+    assert call_fwd(a) == ALIAS
+
+
+def step_args(B_=4, H=2, dk=64, dv=128, io=B.BF16, state=True):
+    fa = Fake()
+    es = 2 if io == B.BF16 else 4
+    P = B_ * H
+    a = dict(q=fa(P * dk * es), k=fa(P * dk * es), v=fa(P * dv * es), i=fa(P * 4), f=fa(P * 4),
+             o=fa(P * dv * es), C=fa(P * dk * dv * 4) if state else None,
+             n=fa(P * dk * 4) if state else None, m=fa(P * 4) if state else None,
+             h=fa(P * dv * es), Co=fa(P * dk * dv * 4), no=fa(P * dk * 4), mo=fa(P * 4),
+             dims=(B_, H, dk, dv, io))
+    return a
+
+
+def call_step(a):
+    return B.lib().mlstm_step(a["q"], a["k"], a["v"], a["i"], a["f"], a["o"], a["C"], a["n"], a["m"],
+                              a["h"], a["Co"], a["no"], a["mo"], *a["dims"], None)
+
+
+def test_step_validation(lib):
+    for key in ("q", "k", "v", "i", "f", "o", "h", "Co", "no", "mo"):
+        a = step_args(); a[key] = None
+        assert call_step(a) == NULL, key
+    a = step_args(); a["dims"] = (0, 2, 64, 128, B.BF16)
+    assert call_step(a) == SHAPE
+    a = step_args(); a["dims"] = (4, 2, 40, 128, B.BF16)
+    assert call_step(a) == UNSUP
+    a = step_args(); a["dims"] = (4, 2, 64, 128, 5)
+    assert call_step(a) == UNSUP
+    a = step_args(); a["m"] = None
+    assert call_step(a) == STATE
+    a = step_args(); a["Co"] = a["C"] + 16
+    assert call_step(a) == ALIAS
+    a = step_args(); a["h"] = a["o"]
+    assert call_step(a) == ALIAS
+    a = step_args(); a["no"] = a["Co"] + 8
+    assert call_step(a) == ALIAS
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(Exception):
+        B.fwd_chunkwise(x, x, x, torch.zeros(1, 1, 4), torch.zeros(1, 1, 4), x)

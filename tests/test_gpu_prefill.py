@@ -1,0 +1,175 @@
+"""GPU parity of the chunkwise forward (mlstm_fwd_chunkwise) against the
+float64 oracle, on the seeded workloads and their edge cases."""
+import numpy as np
+import pytest
+import torch
+
+from tests import parity as PT
+from xlstm_mlstm_matrix_amd import binding, inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+def case(name, pairs=None, T=None, **override):
+    w = I.workload(name, **override)
+    return w, I.gen_prefill(w, pairs=pairs, T=T)
+
+
+def test_tiny_f32():
+    """B=1 H=1 T=64 d_qk=d_v=16 chunk=16 float32, zero initial state."""
+    w, d = case("tiny_f32")
+    PT.compare_fwd(PT.run_gpu_fwd(d, w.chunk), PT.run_oracle(d), "f32", "tiny_f32")
+
+
+def test_small_f32():
+    """B=4 H=4 T=1024 d=64 chunk=64 float32 with a random initial state (every pair)."""
+    w, d = case("small_f32")
+    PT.compare_fwd(PT.run_gpu_fwd(d, w.chunk), PT.run_oracle(d), "f32", "small_f32")
+
+
+@pytest.mark.parametrize("T", [1, 15, 61, 64, 65, 200, 512])
+def test_7b_shapes_ragged(T):
+    """d_qk=256, d_v=512 bf16 at lengths that end mid-chunk or inside one chunk."""
+    w, d = case("prefill_7b_bf16", pairs=[(0, 0), (5, 3)], T=T)
+    PT.compare_fwd(PT.run_gpu_fwd(d, 64, variant="fused"), PT.run_oracle(d), "bf16", f"7b T={T}")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunk_invariance_bf16(chunk):
+    """The chunk length is a schedule choice only: every chunk matches the oracle."""
+    w, d = case("prefill_7b_bf16", pairs=[(1, 2)], T=300)
+    PT.compare_fwd(PT.run_gpu_fwd(d, chunk, variant="fused"), PT.run_oracle(d), "bf16", f"chunk {chunk}")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunk_invariance_f32(chunk):
+    w, d = case("small_f32", pairs=[(0, 1), (3, 3)], T=333)
+    PT.compare_fwd(PT.run_gpu_fwd(d, chunk, variant="fused"), PT.run_oracle(d), "f32", f"f32 chunk {chunk}")
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 48), (64, 64), (96, 160), (128, 128), (256, 512)])
+def test_head_dims(dk, dv):
+    """Supported head dimensions (multiples of 16), both I/O dtypes."""
+    for io in ("f32", "bf16"):
+        w, d = case("prefill_7b_bf16", pairs=[(2, 2)], T=130, d_qk=dk, d_v=dv, io=io)
+        PT.compare_fwd(PT.run_gpu_fwd(d, 32, variant="fused"), PT.run_oracle(d), io, f"{io} dk={dk} dv={dv}")
+
+
+def test_segscan_equals_oracle():
+    """The segmented schedule (local states, scan, seeded pass) on bf16."""
+    w, d = case("prefill_7b_bf16", pairs=[(0, 1), (4, 4)], T=1000)
+    gpu = PT.run_gpu_fwd(d, 64, variant="segscan")
+    ref = PT.run_oracle(d)
+    PT.compare_fwd(gpu, ref, "bf16", "segscan")
+    fused = PT.run_gpu_fwd(d, 64, variant="fused")
+    PT.compare_fwd(fused, ref, "bf16", "fused (same inputs)")
+
+
+def test_segscan_with_initial_state_f32():
+    w, d = case("small_f32", pairs=[(1, 1), (2, 0)], T=900)
+    PT.compare_fwd(PT.run_gpu_fwd(d, 32, variant="segscan"), PT.run_oracle(d), "f32", "segscan f32 + state")
+
+
+def test_state_carry():
+    """fwd(x[:t0]) then fwd(x[t0:], state) equals fwd(x) and the oracle."""
+    w, d = case("small_f32", pairs=[(0, 0), (1, 3)], T=700)
+    ref = PT.run_oracle(d)
+    t0 = 257
+    first = {k: (v[:, :t0].contiguous() if v is not None and v.dim() >= 2 and k not in ("C0", "n0") else v)
+             for k, v in d.items()}
+    first["m0"] = d["m0"]
+    h1, C1, n1, m1 = PT.run_gpu_fwd(first, 64)
+    second = {k: (v[:, t0:].contiguous() if v is not None and v.dim() >= 2 and k not in ("C0", "n0") else v)
+              for k, v in d.items()}
+    second["C0"], second["n0"], second["m0"] = C1.cpu(), n1.cpu(), m1.cpu()
+    h2, C2, n2, m2 = PT.run_gpu_fwd(second, 64)
+    PT.compare_fwd((torch.cat([h1, h2], dim=1), C2, n2, m2), ref, "f32", "split at 257")
+
+
+def test_inplace_state_bitwise_and_deterministic():
+    """C_T == C0 (in place) gives bitwise the same result as separate buffers,
+    and repeated runs are bitwise identical."""
+    w = I.workload("small_f32")
+    d = PT.cuda(I.gen_prefill(w, pairs=[(0, 0), (1, 1), (2, 2)], T=300))
+    add = lambda t: t.unsqueeze(0)
+    args = [add(d[k]) for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")]
+    C0, n0, m0 = add(d["C0"]), add(d["n0"]), add(d["m0"])
+    for variant in ("fused", "segscan"):
+        h1, (C1, n1, m1) = binding.fwd_chunkwise(*args, C0, n0, m0, chunk=64, variant=variant)
+        h2, (C2, n2, m2) = binding.fwd_chunkwise(*args, C0, n0, m0, chunk=64, variant=variant)
+        Ci, ni, mi = C0.clone(), n0.clone(), m0.clone()
+        h3, _ = binding.fwd_chunkwise(*args, Ci, ni, mi, chunk=64, variant=variant,
+                                      C_T=Ci, n_T=ni, m_T=mi)
+        torch.cuda.synchronize()
+        for a, b in ((h1, h2), (C1, C2), (n1, n2), (m1, m2), (h1, h3), (C1, Ci), (n1, ni), (m1, mi)):
+            assert torch.equal(a, b), variant
+
+
+def test_outputs_fully_written():
+    """Outputs pre-filled with NaN come back finite (no element left unwritten)."""
+    w, d = case("prefill_7b_bf16", pairs=[(3, 3)], T=77)
+    g = PT.cuda(d)
+    add = lambda t: t.unsqueeze(0)
+    h = torch.full((1, 1, 77, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    C = torch.full((1, 1, 256, 512), float("nan"), device="cuda")
+    n = torch.full((1, 1, 256), float("nan"), device="cuda")
+    m = torch.full((1, 1), float("nan"), device="cuda")
+    binding.fwd_chunkwise(*[add(g[k]) for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")],
+                          chunk=64, h=h, C_T=C, n_T=n, m_T=m)
+    torch.cuda.synchronize()
+    for t in (h, C, n, m):
+        assert torch.isfinite(t).all()
+
+
+def test_input_gate_spikes():
+    """Input-gate pre-activations of +-50 (e^50 overflows nothing in the
+    stabilized form) and a forget gate near 1."""
+    w, d = case("prefill_7b_bf16", pairs=[(0, 0), (1, 1)], T=150)
+    i = d["i_pre"].clone()
+    i[:, 10] = 50.0
+    i[:, 90] = 45.0
+    i[:, 100:110] = -50.0
+    d["i_pre"] = i
+    d["f_pre"][:, 120:] = -1e-4
+    PT.compare_fwd(PT.run_gpu_fwd(d, 64, variant="fused"), PT.run_oracle(d), "bf16", "spikes")
+
+
+def test_linear_attention_special_case():
+    """i~ = f~ = 0 from the zero state: num = tril(Q K^T) V (unnormalized causal
+    linear attention), checked on the GPU against that closed form directly."""
+    w, d = case("small_f32", pairs=[(0, 0)], T=96)
+    d["i_pre"].zero_()
+    d["f_pre"].zero_()
+    d["C0"] = d["n0"] = d["m0"] = None
+    h, C, n, m = PT.run_gpu_fwd(d, 32, variant="fused")
+    q, k, v, o = (d[x][0].double().numpy() for x in ("q", "k", "v", "o_pre"))
+    A = np.tril(q @ k.T)
+    den = np.maximum(np.abs(A.sum(axis=1)), 1.0)
+    num = PT.to_np(h) / (1.0 / (1.0 + np.exp(-o))) * den[:, None]
+    assert PT.row_relerr(num, A @ v) <= PT.TOL["f32"]
+    assert float(m.abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("variant", ["fused", "segscan"])
+def test_7b_full_size_sampled(variant):
+    """The whole 7B-layer-shaped workload (B=8 H=8 T=4096 d_qk=256 d_v=512
+    chunk=64 bf16) in one launch; the oracle checks three sampled pairs
+    element by element, and every pair's final stabilizer is checked against
+    its closed form from the gates."""
+    w = I.workload("prefill_7b_bf16")
+    print(f"[case] 7b full size, variant={variant}", flush=True)
+    d = I.gen_prefill(w)
+    g = PT.cuda(d)
+    shp = lambda t: t.reshape(w.B, w.H, *t.shape[1:])
+    h, (C, n, m) = binding.fwd_chunkwise(*[shp(g[k]) for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")],
+                                         chunk=w.chunk, variant=variant)
+    torch.cuda.synchronize()
+    assert torch.isfinite(h).all() and torch.isfinite(C).all()
+    m_ref = PT.m_closed_form(d["i_pre"].double().numpy(), d["f_pre"].double().numpy())
+    assert np.max(np.abs(PT.to_np(m).reshape(-1) - m_ref)) <= PT.TOL_M["bf16"]
+    sample = [(0, 0), (3, 5), (7, 7)]
+    idx = [b * w.H + hh for b, hh in sample]
+    sub = {k: (v[idx] if v is not None else None) for k, v in d.items()}
+    ref = PT.run_oracle(sub)
+    flat = lambda t: t.reshape(w.B * w.H, *t.shape[2:])[idx]
+    PT.compare_fwd((flat(h), flat(C), flat(n), flat(m)), ref, "bf16", f"7b full, sampled pairs {sample}")

@@ -1,0 +1,186 @@
+"""Python binding of the C ABI in ``include/mlstm.h`` (ctypes).
+
+Argument marshalling only: tensors are torch device tensors (torch supplies
+device memory and the current stream); every step of the computation runs in
+the HIP library.  There is no fallback: if ``libmlstm.so`` is missing or
+fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmlstm.so")
+
+F32, BF16 = 0, 1
+VARIANTS = {"auto": 0, "fused": 1, "segscan": 2}
+STATUS = {0: "MLSTM_OK", 1: "MLSTM_ERR_NULL", 2: "MLSTM_ERR_SHAPE", 3: "MLSTM_ERR_UNSUPPORTED",
+          4: "MLSTM_ERR_STATE_ARGS", 5: "MLSTM_ERR_WORKSPACE", 6: "MLSTM_ERR_ALIAS",
+          7: "MLSTM_ERR_HIP"}
+
+# exported entry points and their C signatures (kept in step with include/mlstm.h)
+_vp, _fp, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
+_i = ctypes.c_int
+SIGNATURES = {
+    "mlstm_status_string": (ctypes.c_char_p, [_i]),
+    "mlstm_version": (ctypes.c_char_p, []),
+    "mlstm_fwd_chunkwise_workspace_size": (_i, [_i] * 7 + [ctypes.POINTER(_sz)]),
+    "mlstm_fwd_chunkwise_workspace_size_variant": (_i, [_i] * 8 + [ctypes.POINTER(_sz)]),
+    "mlstm_fwd_chunkwise": (_i, [_vp] * 13 + [_i] * 7 + [_vp, _sz, _vp]),
+    "mlstm_fwd_chunkwise_variant": (_i, [_vp] * 13 + [_i] * 8 + [_vp, _sz, _vp]),
+    "mlstm_step": (_i, [_vp] * 13 + [_i] * 5 + [_vp]),
+}
+
+
+class MlstmError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} "
+                               "(run python -m xlstm_mlstm_matrix_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def status_string(s: int) -> str:
+    return lib().mlstm_status_string(int(s)).decode()
+
+
+def _check(s: int):
+    if s != 0:
+        raise MlstmError(s, status_string(s))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _io(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"I/O tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _req(t, name, dtype=None, device=None):
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _stream(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_size(B, H, T, d_qk, d_v, chunk, io: int, variant: str = "auto") -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().mlstm_fwd_chunkwise_workspace_size_variant(
+        B, H, T, d_qk, d_v, chunk, io, VARIANTS[variant], ctypes.byref(n)))
+    return n.value
+
+
+def fwd_chunkwise(q, k, v, i_pre, f_pre, o_pre, C0=None, n0=None, m0=None, *, chunk: int = 64,
+                  return_state: bool = True, variant: str = "auto", h=None, C_T=None, n_T=None,
+                  m_T=None, workspace=None):
+    """Chunkwise forward over whole sequences.
+
+    q, k [B,H,T,d_qk], v, o_pre [B,H,T,d_v] (float32 or bfloat16, one dtype);
+    i_pre, f_pre [B,H,T] float32; optional (C0 [B,H,d_qk,d_v], n0 [B,H,d_qk],
+    m0 [B,H]) float32.  Returns h, or (h, (C_T, n_T, m_T)) with
+    ``return_state``.  Output buffers may be passed in (C_T may be C0 for an
+    in-place state update)."""
+    import torch
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    io_t = q.dtype
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("o_pre", o_pre)):
+        _req(t, name, io_t, dev)
+    for name, t in (("i_pre", i_pre), ("f_pre", f_pre), ("C0", C0), ("n0", n0), ("m0", m0)):
+        _req(t, name, torch.float32, dev)
+    if h is None:
+        h = torch.empty((B, H, T, dv), dtype=io_t, device=dev)
+    if return_state and C_T is None:
+        C_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        n_T = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+        m_T = torch.empty((B, H), dtype=torch.float32, device=dev)
+    io = _io(q)
+    nbytes = workspace_size(B, H, T, dk, dv, chunk, io, variant)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mlstm_fwd_chunkwise_variant(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(o_pre),
+        _ptr(C0), _ptr(n0), _ptr(m0), _ptr(h), _ptr(C_T), _ptr(n_T), _ptr(m_T),
+        B, H, T, dk, dv, chunk, io, VARIANTS[variant],
+        _ptr(workspace), ws_len, _stream(dev)))
+    if return_state:
+        return h, (C_T, n_T, m_T)
+    return h
+
+
+def step(q, k, v, i_pre, f_pre, o_pre, C=None, n=None, m=None, *, h=None, C_out=None,
+         n_out=None, m_out=None, inplace: bool = True):
+    """One recurrent step for B*H cells.
+
+    q, k [B,H,d_qk], v, o_pre [B,H,d_v]; i_pre, f_pre [B,H]; state (C [B,H,d_qk,
+    d_v], n [B,H,d_qk], m [B,H]) float32 or None for the zero state.  With
+    ``inplace`` (default) and a state given, the state tensors are updated in
+    place.  Returns (h, C_out, n_out, m_out)."""
+    import torch
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    io_t = q.dtype
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("o_pre", o_pre)):
+        _req(t, name, io_t, dev)
+    for name, t in (("i_pre", i_pre), ("f_pre", f_pre), ("C", C), ("n", n), ("m", m)):
+        _req(t, name, torch.float32, dev)
+    if h is None:
+        h = torch.empty((B, H, dv), dtype=io_t, device=dev)
+    if C_out is None:
+        if inplace and C is not None:
+            C_out, n_out, m_out = C, n, m
+        else:
+            C_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+            n_out = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+            m_out = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _check(lib().mlstm_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(o_pre),
+        _ptr(C), _ptr(n), _ptr(m), _ptr(h), _ptr(C_out), _ptr(n_out), _ptr(m_out),
+        B, H, dk, dv, _io(q), _stream(dev)))
+    return h, C_out, n_out, m_out

@@ -1,0 +1,60 @@
+"""Build the gfx950 HIP library ``libmlstm.so`` in-tree with hipcc.
+
+    python -m xlstm_mlstm_matrix_amd.build      # or build() from Python
+
+Every source is compiled for gfx950 only.  Packed fp32 instructions are
+switched off (``-packed-fp32-ops``); the host pass warns that it does not know
+the feature, which is harmless.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libmlstm.so")
+OBJDIR = os.path.join(ROOT, "_build")
+
+SOURCES = ["api.cpp", "step.hip", "prefill.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror", "-Wno-unused-command-line-argument",
+         f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", INCLUDE, "-I", CSRC]
+
+
+def _compile(src: str) -> str:
+    out = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "not a recognized feature for this target"
+    err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{err}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link ``libmlstm.so`` (always rebuilds)."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

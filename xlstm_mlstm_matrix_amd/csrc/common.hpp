@@ -1,0 +1,76 @@
+// common.hpp -- internal types and device helpers of the gfx950 mLSTM library.
+// Not part of the public ABI (that is include/mlstm.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlstm {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// e^x through the hardware base-2 exponential: e^x = 2^(x * log2(e)).
+__device__ __forceinline__ float exp_e(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// logistic function 1 / (1 + e^{-x}); saturates to exactly 0 or 1, no NaN.
+__device__ __forceinline__ float sigmoid(float x) {
+    return 1.0f / (1.0f + exp_e(-x));
+}
+
+// I/O element <-> float.  bf16 -> float is exact; float -> bf16 rounds to
+// nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+// Arguments of the chunkwise forward kernels (one struct, passed by value).
+struct FwdArgs {
+    const void *q, *k, *v;         // [BH, T, d_qk] x2, [BH, T, d_v]   io dtype
+    const float *ig, *fg;          // [BH, T]
+    const void *o;                 // [BH, T, d_v]                     io dtype
+    const float *C0, *n0, *m0;     // initial state (segment 0), NULL = zero
+    void *h;                       // [BH, T, d_v]                     io dtype
+    float *CT, *nT, *mT;           // final state, NULL = not wanted
+    const float *seg_in;           // incoming state per segment (segmented schedule) or NULL
+    float *seg_out;                // local state per segment (state-only pass) or NULL
+    int BH, T, dk, dv;
+    int seg_len;                   // tokens per segment (multiple of the chunk), T if one segment
+    int nseg;                      // segments per sequence
+    int ntile;                     // value-column tiles per sequence
+    int nseg_out;                  // segments whose local state is produced (state-only pass)
+};
+
+// Layout of one segment state record in the workspace (float32):
+//   C' [d_qk][d_v], n' [d_qk], m, g (sum of log forget gates over the segment)
+__host__ __device__ inline size_t seg_state_floats(int dk, int dv) {
+    return (size_t)dk * dv + dk + 2;
+}
+
+struct StepArgs {
+    const void *q, *k, *v;         // [BH, d_qk] x2, [BH, d_v]
+    const float *ig, *fg;          // [BH]
+    const void *o;                 // [BH, d_v]
+    const float *C_in, *n_in, *m_in;
+    void *h;
+    float *C_out, *n_out, *m_out;
+    int BH, dk, dv;
+};
+
+// Launchers (defined in the .hip files).  Return hipSuccess or the launch error.
+hipError_t launch_step(const StepArgs &a, int io_bf16, hipStream_t s);
+hipError_t launch_fused(const FwdArgs &a, int io_bf16, int chunk, int state_only, hipStream_t s);
+hipError_t launch_seg_combine(const FwdArgs &a, float *ws, hipStream_t s);
+
+// Tiling choices shared by the planner and the launchers.
+int prefill_dkp(int dk);                 // d_qk padded to the kernel's compile-time width
+int prefill_bv(int io_bf16, int dk, int dv, int chunk);  // value columns per workgroup
+bool prefill_supported(int io_bf16, int dk, int dv, int chunk);  // tiles fit in LDS
+
+}  // namespace mlstm

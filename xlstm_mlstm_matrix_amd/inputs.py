@@ -14,9 +14,9 @@ the I/O dtype; bf16 casts round to nearest even):
 * k is multiplied by 1/sqrt(d_qk) and the log forget gate input is
   f_pre = logsigmoid(f_raw), i.e. the forget gate handed to the cell is already
   in log space (the cell itself applies exp, never a sigmoid);
-* a decode workload draws step t's inputs from ``SeedSequence([seed, 1, t])``
-  (so any single step is reproducible alone) and its initial state from
-  ``SeedSequence([seed, 0])``.
+* a decode workload draws tensor j of step t from ``SeedSequence([seed, 1, t,
+  j])`` (so any single step is reproducible alone) and batch row b of its
+  initial state from ``SeedSequence([seed, 0, b])``.
 
 Because the draws are per (b, h) (prefill) or per step (decode), a subset of
 the pairs or steps can be regenerated without drawing the rest, which is how
@@ -197,44 +197,63 @@ def gen_prefill(w: Workload, pairs: Optional[Sequence[Tuple[int, int]]] = None,
     return out
 
 
-def gen_decode_state(w: Workload, B: Optional[int] = None):
+_DECODE_TENSORS = {"q": 0, "k": 1, "v": 2, "i_pre": 3, "f_pre": 4, "o_pre": 5}
+
+
+def _rng(*key):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
+
+
+def gen_decode_state(w: Workload, B: Optional[int] = None, threads: int = 8):
     """Initial state of a decode workload: C0 [B,H,d_qk,d_v], n0 [B,H,d_qk],
-    m0 [B,H], float32 torch CPU tensors (``B`` may reduce the batch; the
-    first B rows equal those of the full workload)."""
+    m0 [B,H], float32 torch CPU tensors.  Batch row b is drawn (C0, then n0,
+    then m0) from its own generator ``SeedSequence([seed, 0, b])``, so a
+    reduced ``B`` is a prefix of the full workload."""
     import torch
     B = w.B if B is None else B
-    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 0])))
     C0 = torch.empty((B, w.H, w.d_qk, w.d_v), dtype=torch.float32)
     n0 = torch.empty((B, w.H, w.d_qk), dtype=torch.float32)
     m0 = torch.empty((B, w.H), dtype=torch.float32)
-    # drawn batch row by batch row so a reduced B is a prefix of the full draw
-    for b in range(B):
+
+    def row(b):
+        rng = _rng(w.seed, 0, b)
         C0[b] = torch.from_numpy(_draw_state(rng, w.init_state["C0"], (w.H, w.d_qk, w.d_v)).astype(np.float32))
         n0[b] = torch.from_numpy(_draw_state(rng, w.init_state["n0"], (w.H, w.d_qk)).astype(np.float32))
         m0[b] = torch.from_numpy(np.asarray(_draw_state(rng, w.init_state["m0"], (w.H,))).astype(np.float32))
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(row, range(B)))
     return C0, n0, m0
 
 
 def gen_decode_step(w: Workload, t: int, B: Optional[int] = None):
     """Inputs of decode step t: q, k [B,H,d_qk], v, o_pre [B,H,d_v] in the I/O
-    dtype, i_pre, f_pre [B,H] float32 (torch CPU tensors).  A reduced ``B``
-    is a prefix of the full step's batch."""
+    dtype, i_pre, f_pre [B,H] float32 (torch CPU tensors).  Each tensor of
+    each step comes from its own generator ``SeedSequence([seed, 1, t, j])``
+    (j = 0..5 for q, k, v, i_pre, f_pre, o_pre), drawn in C order, so a
+    reduced ``B`` is a prefix of the full step's batch."""
     import torch
     B = w.B if B is None else B
-    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 1, t])))
     H = w.H
-    q = np.empty((B, H, w.d_qk)); k = np.empty((B, H, w.d_qk)); v = np.empty((B, H, w.d_v))
-    i_pre = np.empty((B, H)); f_pre = np.empty((B, H)); o_pre = np.empty((B, H, w.d_v))
-    for b in range(B):  # batch row by batch row: a reduced B is a prefix
-        q[b] = rng.standard_normal((H, w.d_qk))
-        k[b] = rng.standard_normal((H, w.d_qk)) * (1.0 / math.sqrt(w.d_qk))
-        v[b] = rng.standard_normal((H, w.d_v))
-        i_pre[b] = rng.normal(w.i_mean, w.i_std, size=H)
-        f_pre[b] = logsigmoid(rng.normal(w.f_mean, w.f_std, size=H))
-        o_pre[b] = rng.standard_normal((H, w.d_v))
+    j = _DECODE_TENSORS
+    q = _rng(w.seed, 1, t, j["q"]).standard_normal((B, H, w.d_qk))
+    k = _rng(w.seed, 1, t, j["k"]).standard_normal((B, H, w.d_qk)) * (1.0 / math.sqrt(w.d_qk))
+    v = _rng(w.seed, 1, t, j["v"]).standard_normal((B, H, w.d_v))
+    i_pre = _rng(w.seed, 1, t, j["i_pre"]).normal(w.i_mean, w.i_std, size=(B, H))
+    f_pre = logsigmoid(_rng(w.seed, 1, t, j["f_pre"]).normal(w.f_mean, w.f_std, size=(B, H)))
+    o_pre = _rng(w.seed, 1, t, j["o_pre"]).standard_normal((B, H, w.d_v))
     return {
         "q": to_io_dtype(q, w.io), "k": to_io_dtype(k, w.io), "v": to_io_dtype(v, w.io),
         "i_pre": torch.from_numpy(i_pre.astype(np.float32)),
         "f_pre": torch.from_numpy(f_pre.astype(np.float32)),
         "o_pre": to_io_dtype(o_pre, w.io),
     }
+
+
+def gen_decode_steps(w: Workload, steps: Sequence[int], B: Optional[int] = None, threads: int = 8):
+    """Several decode steps stacked on a leading step axis (dict of torch CPU
+    tensors of shape [S, B, H, ...]), drawn in parallel threads."""
+    import torch
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        parts = list(ex.map(lambda t: gen_decode_step(w, t, B), steps))
+    return {key: torch.stack([p[key] for p in parts]) for key in parts[0]}
