@@ -105,7 +105,7 @@ template <int L, int DKP, int BV, bool SO>
 hipError_t run_bf16(const FwdArgs &a, hipStream_t s) {
     static_assert(Bf16Cfg<L, DKP, BV>::LDS_BYTES <= kLdsBudget, "LDS budget");
     const int gseg = SO ? a.nseg - 1 : a.nseg;
-    dim3 grid((unsigned)(a.BH * gseg * a.ntile)), block(256);
+    dim3 grid((unsigned)(a.BH * gseg * a.ntile)), block(Bf16Cfg<L, DKP, BV>::NTH);
     hipLaunchKernelGGL((mlstm_bf16_kernel<L, DKP, BV, SO>), grid, block, 0, s, a);
     return hipGetLastError();
 }

@@ -9,29 +9,29 @@
 //   P_ij = (q_i.k_j) e^{u_j - r_i} (j <= i),
 //   C' <- e^{m-r_L} C' + sum_j e^{u_j-r_L} k_j v_j^T, n' likewise, m <- b_L + r_L.
 //
-// This is the bf16 schedule built around two gfx950 features:
-//  * global -> LDS copies (global_load_lds, 16 bytes per lane) stage Q, K and
-//    V without passing through registers; K and V are double buffered (the
-//    next chunk streams in during the whole current chunk), Q is reloaded
-//    once the current chunk's d_qk loop is done with it;
-//  * the LDS transpose read (ds_read_b64_tr_b16) produces MFMA fragments of
-//    K^T and V^T (token index along k) straight from the row-major tiles, so
-//    nothing is ever written transposed.
-// Tiles are row-major with 16-byte granules XOR-swizzled per row (granule
-// g of row r lives at g ^ swz(r)), which keeps the 16-row fragment reads,
-// the transpose reads and the copies free of bank conflicts.
-//
-// Work split: one workgroup = one (pair, segment, BV value columns); 4
-// wavefronts, each owning BV/4 columns of the d_qk x BV state C' in
-// registers (float32, MFMA accumulator layout).  Per chunk:
-//   O^T  = C'^T Q^T        C' split into bf16 high + bf16 remainder (2 MFMAs),
-//                          so the carried state keeps ~16 bits in the read-out
-//   S^T  = K Q^T           causal 16x16 tiles spread over the wavefronts
-//   qn   = Q n'            (one 16-token tile per wavefront, n' split too)
-//   P    = S (x) decay     -> LDS (bf16);  O^T += V^T P^T;  h written
-//   C'   = decay C' + K^T (w (x) V),  n' = decay n' + K^T w  (w split)
-// The chunk's gate quantities are computed one chunk ahead by wavefront 0
-// into a double-buffered table, so a chunk needs two workgroup barriers.
+// Schedule (one workgroup = one (pair, segment, BV value columns), 8
+// wavefronts, two per SIMD so one can issue MFMAs while the other does
+// VALU/LDS work):
+//  * wavefront w = (p, hf): p = w & 3 owns BV/4 value columns, hf = w >> 2
+//    owns half of the d_qk rows of the state C' (float32, registers, MFMA
+//    accumulator layout).  The read-out C'^T Q^T is split over the two
+//    halves (split-K) and the partial sums are exchanged through LDS; each
+//    wavefront of the pair then finishes half of the chunk's token tiles;
+//  * Q, K, V are staged with global->LDS copies (16 B per lane) into
+//    row-major tiles whose 16-byte granules are XOR-swizzled per row; K is
+//    double buffered (next chunk's K lands during the whole chunk), V and Q
+//    are reloaded as soon as the current chunk is done with them;
+//  * K^T and V^T fragments (token index along the MFMA k) come from the LDS
+//    transpose read (ds_read_b64_tr_b16) of the row-major tiles;
+//  * the read-out splits C' into a bf16 high part and a bf16 remainder (two
+//    MFMAs), so the carried state keeps ~16 significant bits in it;
+//  * the decay of the carried state is applied lazily: C' is held as
+//    C'/sigma and sigma (a product of per-chunk decays) is folded into the
+//    read-out scale and the update weights, renormalised when it gets small;
+//  * gate quantities of the next chunk are computed by one wavefront with
+//    DPP scans into a double-buffered table; q.n' is a small VALU dot
+//    product spread over all threads; n' is updated with MFMAs;
+//  * two workgroup barriers per chunk.
 #pragma once
 
 #include "prefill_kernel.hpp"
@@ -44,33 +44,39 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 template <int L_, int DKP_, int BV_>
 struct Bf16Cfg {
-    static constexpr int L = L_, DKP = DKP_, BV = BV_, NW = 4, NTH = 256;
-    static constexpr int LP = L < 32 ? 32 : L;       // token rows held (k of 32 for the MFMA)
-    static constexpr int NT = L / 16, NCT = NT * (NT + 1) / 2, MYT = (NCT + NW - 1) / NW;
-    static constexpr int NAT = DKP / 16, NKS = DKP / 32, NJS = LP / 32;
-    static constexpr int WC = BV / NW, NBT = WC / 16;
-    static constexpr int QG = DKP / 8;                // 16-byte granules per Q/K row
-    static constexpr int VG = BV / 8;                 // granules per V row
-    static constexpr int PG = LP / 8;                 // granules per P row
-    static constexpr int NA_W = NAT / NW;             // n' tiles per wavefront
+    static constexpr int L = L_, DKP = DKP_, BV = BV_;
+    static constexpr int NW = 8, NTH = 512;
+    static constexpr int LP = L < 32 ? 32 : L;        // token rows held (MFMA k of 32)
+    static constexpr int NT = L / 16;                 // 16-token tiles per chunk
+    static constexpr int NCT = NT * (NT + 1) / 2;     // causal tiles of S
+    static constexpr int MYT = (NCT + NW - 1) / NW;   // S tiles per wavefront (max)
+    static constexpr int NAT = DKP / 16;              // 16-row tiles of C'
+    static constexpr int NAH = NAT / 2;               // ... per d_qk half
+    static constexpr int NKS = DKP / 32, NKH = NKS / 2;
+    static constexpr int NJS = LP / 32;
+    static constexpr int WC = BV / 4;                 // value columns per wavefront pair
+    static constexpr int NBT = WC / 16;
+    static constexpr int NF = NT >= 2 ? NT / 2 : 1;   // token tiles each wavefront finishes
+    static constexpr int QG = DKP / 8, VG = BV / 8, PG = LP / 8;  // granules per row
+    static constexpr int NNW = (NAH + 3) / 4;         // n' tiles per wavefront (max)
+    static constexpr int GT_FLOATS = 5 * LP + LP + 8; // u r s floor w | w hi/lo (bf16 pairs) | scalars
     static constexpr size_t LDS_BYTES =
-        2 * ((size_t)LP * DKP + 2 * (size_t)LP * DKP + 2 * (size_t)LP * BV + (size_t)L * LP) +
-        4 * (2 * (5 * (size_t)LP + 4) + NCT * 16 + L + DKP);
+        2 * ((size_t)LP * DKP * 3 + (size_t)LP * BV + (size_t)L * LP) +
+        16 * (size_t)NW * NF * NBT * 64 + 4 * (2 * (size_t)GT_FLOATS + NCT * 16 + L + DKP) + 16;
+    static_assert(QG >= 8 && VG >= 8, "swizzle needs 8 granules per row");
     static_assert(NBT >= 1 && WC % 16 == 0, "whole 16-column tiles per wavefront");
-    static_assert(NAT % NW == 0, "n' tiles spread evenly");
+    static_assert(NKH >= 1, "d_qk split in two halves");
     static_assert(L <= 64, "one token per lane in the gate scan");
 };
 
-// granule swizzle: within each aligned group of 8 granules of a row
+// row swizzle of the 16-byte granules (XOR within aligned groups of 8)
+__device__ __forceinline__ int swz8(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 template <int GPR>
-__device__ __forceinline__ int swz(int row) {
-    constexpr int m = GPR < 8 ? GPR - 1 : 7;
-    return (((row & 3) << 1) | ((row >> 2) & 1)) & m;
-}
+__device__ __forceinline__ int swzg(int row) { return GPR >= 8 ? swz8(row) : (swz8(row) & (GPR - 1)); }
 // element offset of (row, col) in a swizzled row-major bf16 tile with GPR granules per row
 template <int GPR>
 __device__ __forceinline__ int sw_off(int row, int col) {
-    return row * GPR * 8 + ((((col >> 3) ^ swz<GPR>(row))) << 3) + (col & 7);
+    return row * GPR * 8 + (((col >> 3) ^ swzg<GPR>(row)) << 3) + (col & 7);
 }
 
 __device__ __forceinline__ bf16x4 tr_read(const bf16 *p) {
@@ -80,6 +86,7 @@ __device__ __forceinline__ bf16x4 tr_read(const bf16 *p) {
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+__device__ __forceinline__ bf16x4 ld4(const bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
 
 // split 8 floats into bf16 high parts and bf16 remainders
 __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
@@ -91,27 +98,62 @@ __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
     }
 }
 
+// inclusive scans over the 64 lanes of a wavefront with DPP: shifts of 1, 2,
+// 4, 8 inside each row of 16 lanes, then the row totals carried forward with
+// the row broadcasts of lane 15 and lane 31.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_mov(float identity, float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(x), CTRL,
+                                                      ROWMASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_scan_add(float x) {
+    x += dpp_mov<0x111, 0xf>(0.0f, x);  // row_shr:1
+    x += dpp_mov<0x112, 0xf>(0.0f, x);  // row_shr:2
+    x += dpp_mov<0x114, 0xf>(0.0f, x);  // row_shr:4
+    x += dpp_mov<0x118, 0xf>(0.0f, x);  // row_shr:8
+    x += dpp_mov<0x142, 0xa>(0.0f, x);  // row_bcast:15 into rows 1, 3
+    x += dpp_mov<0x143, 0xc>(0.0f, x);  // row_bcast:31 into rows 2, 3
+    return x;
+}
+__device__ __forceinline__ float wave_scan_max(float x) {
+    const float ni = -INFINITY;
+    x = fmaxf(x, dpp_mov<0x111, 0xf>(ni, x));
+    x = fmaxf(x, dpp_mov<0x112, 0xf>(ni, x));
+    x = fmaxf(x, dpp_mov<0x114, 0xf>(ni, x));
+    x = fmaxf(x, dpp_mov<0x118, 0xf>(ni, x));
+    x = fmaxf(x, dpp_mov<0x142, 0xa>(ni, x));
+    x = fmaxf(x, dpp_mov<0x143, 0xc>(ni, x));
+    return x;
+}
+
 template <int L, int DKP, int BV, bool STATE_ONLY>
-__global__ __launch_bounds__(256, 1) void mlstm_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
     using Cfg = Bf16Cfg<L, DKP, BV>;
     constexpr int NW = Cfg::NW, NTH = Cfg::NTH, LP = Cfg::LP, NT = Cfg::NT, NCT = Cfg::NCT;
-    constexpr int MYT = Cfg::MYT, NAT = Cfg::NAT, NKS = Cfg::NKS, NJS = Cfg::NJS, WC = Cfg::WC;
-    constexpr int NBT = Cfg::NBT, QG = Cfg::QG, VG = Cfg::VG, PG = Cfg::PG, NA_W = Cfg::NA_W;
+    constexpr int MYT = Cfg::MYT, NAH = Cfg::NAH, NKH = Cfg::NKH, NJS = Cfg::NJS;
+    constexpr int WC = Cfg::WC, NBT = Cfg::NBT, NF = Cfg::NF, QG = Cfg::QG, VG = Cfg::VG;
+    constexpr int PG = Cfg::PG, NNW = Cfg::NNW, GTF = Cfg::GT_FLOATS;
+    constexpr float kRenorm = 8.6736174e-19f;  // 2^-60: renormalise the lazy state scale below this
 
     __shared__ __attribute__((aligned(16))) bf16 Qs[LP * DKP];
     __shared__ __attribute__((aligned(16))) bf16 Ks[2][LP * DKP];
-    __shared__ __attribute__((aligned(16))) bf16 Vs[2][LP * BV];
+    __shared__ __attribute__((aligned(16))) bf16 Vs[LP * BV];
     __shared__ __attribute__((aligned(16))) bf16 Ps[L * LP];
-    // gate tables, double buffered: u, r, s, floor, w [LP] and 4 scalars
-    __shared__ __attribute__((aligned(16))) float gt[2][5 * LP + 4];
+    __shared__ __attribute__((aligned(16))) f32x4 Xch[NW][NF * NBT][64];
+    // gate tables (double buffered): u, r, s, floor, w [LP] floats, w as bf16
+    // high/low pairs [LP], then scalars (m after, decay, sum f~)
+    __shared__ __attribute__((aligned(16))) float gt[2][GTF];
     __shared__ float den_part[NCT * 16];
     __shared__ float qn[L];
     __shared__ __attribute__((aligned(16))) float nsh[DKP];
+    __shared__ __attribute__((aligned(16))) uint4 zero16;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int p = wave & 3, hf = wave >> 2;
     const int l16 = lane & 15, g4 = lane >> 4;
+    const int te = l16 >> 2, tq = l16 & 3;  // transpose-read source row / column quad
 
     const int nwg = gridDim.x;
     int logical = blockIdx.x;
@@ -127,37 +169,38 @@ __global__ __launch_bounds__(256, 1) void mlstm_bf16_kernel(FwdArgs a) {
     const int t_end = min(t_begin + a.seg_len, T);
     const int nchunks = (t_end - t_begin + L - 1) / L;
     const int col0 = tile * BV;
-    const int wcol0 = wave * WC;
+    const int wc0 = p * WC;  // first column of this wavefront pair (tile-local)
     const int bv_here = min(BV, dv - col0);
 
     const bf16 *qg = static_cast<const bf16 *>(a.q) + (size_t)bh * T * dk;
     const bf16 *kg = static_cast<const bf16 *>(a.k) + (size_t)bh * T * dk;
-    const bf16 *vg = static_cast<const bf16 *>(a.v) + (size_t)bh * T * dv;
+    const bf16 *vg = static_cast<const bf16 *>(a.v) + (size_t)bh * T * dv + col0;
     const bf16 *og = static_cast<const bf16 *>(a.o) + (size_t)bh * T * dv;
     bf16 *hg = static_cast<bf16 *>(a.h) + (size_t)bh * T * dv;
     const float *igg = a.ig + (size_t)bh * T;
     const float *fgg = a.fg + (size_t)bh * T;
 
-    // ---- zero all tiles once (padding columns/rows and P's upper tiles stay zero)
+    // ---- zero every tile once: padding rows/columns and P's upper tiles stay zero
     {
-        uint4 *p;
-        p = reinterpret_cast<uint4 *>(Qs);
-        for (int e = tid; e < LP * DKP / 8; e += NTH) p[e] = make_uint4(0, 0, 0, 0);
-        p = reinterpret_cast<uint4 *>(&Ks[0][0]);
-        for (int e = tid; e < 2 * LP * DKP / 8; e += NTH) p[e] = make_uint4(0, 0, 0, 0);
-        p = reinterpret_cast<uint4 *>(&Vs[0][0]);
-        for (int e = tid; e < 2 * LP * BV / 8; e += NTH) p[e] = make_uint4(0, 0, 0, 0);
-        p = reinterpret_cast<uint4 *>(Ps);
-        for (int e = tid; e < L * LP / 8; e += NTH) p[e] = make_uint4(0, 0, 0, 0);
-        for (int e = tid; e < 2 * (5 * LP + 4); e += NTH) (&gt[0][0])[e] = 0.0f;
+        uint4 z = make_uint4(0, 0, 0, 0);
+        uint4 *q4 = reinterpret_cast<uint4 *>(Qs);
+        for (int e = tid; e < LP * DKP / 8; e += NTH) q4[e] = z;
+        uint4 *k4 = reinterpret_cast<uint4 *>(&Ks[0][0]);
+        for (int e = tid; e < 2 * LP * DKP / 8; e += NTH) k4[e] = z;
+        uint4 *v4 = reinterpret_cast<uint4 *>(Vs);
+        for (int e = tid; e < LP * BV / 8; e += NTH) v4[e] = z;
+        uint4 *p4 = reinterpret_cast<uint4 *>(Ps);
+        for (int e = tid; e < L * LP / 8; e += NTH) p4[e] = z;
+        for (int e = tid; e < 2 * GTF; e += NTH) (&gt[0][0])[e] = 0.0f;
+        if (tid == 0) zero16 = z;
     }
 
-    // ---- initial state
+    // ---- initial state (C' in this wavefront's half of d_qk, its pair's columns)
     const size_t rec = seg_state_floats(dk, dv);
     const float *Cs = nullptr, *ns = nullptr;
     float m_prev = 0.0f;
     if (STATE_ONLY) {
-        m_prev = -1e30f;
+        m_prev = -1e30f;  // "no past": the first chunk's stabilizer comes from its own gates
     } else if (a.seg_in) {
         const float *r = a.seg_in + ((size_t)bh * a.nseg + seg) * rec;
         Cs = r;
@@ -168,61 +211,59 @@ __global__ __launch_bounds__(256, 1) void mlstm_bf16_kernel(FwdArgs a) {
         ns = a.n0 + (size_t)bh * dk;
         m_prev = a.m0[bh];
     }
-    f32x4 Cr[NAT][NBT];
+    const int arow0 = hf * (DKP / 2);  // first d_qk row of this wavefront's half
+    f32x4 Cr[NAH][NBT];
 #pragma unroll
-    for (int at = 0; at < NAT; ++at)
+    for (int at = 0; at < NAH; ++at)
 #pragma unroll
         for (int bt = 0; bt < NBT; ++bt) {
-            const int b = col0 + wcol0 + 16 * bt + l16;
+            const int b = col0 + wc0 + 16 * bt + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 16 * at + 4 * g4 + r;
+                const int row = arow0 + 16 * at + 4 * g4 + r;
                 Cr[at][bt][r] = (Cs && row < dk && b < dv) ? Cs[(size_t)row * dv + b] : 0.0f;
             }
         }
-    // n' tiles owned by this wavefront (a-tiles wave*NA_W ...), MFMA layout, column 0
-    f32x4 Nr[NA_W];
+    // n' tiles kept by this wavefront: tiles arow0/16 + p + 4x (column 0 of an MFMA tile)
+    f32x4 Nr[NNW];
 #pragma unroll
-    for (int x = 0; x < NA_W; ++x) {
+    for (int x = 0; x < NNW; ++x) {
+        const int tl = p + 4 * x;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = 16 * (wave * NA_W + x) + 4 * g4 + r;
-            Nr[x][r] = (ns && l16 == 0 && row < dk) ? ns[row] : 0.0f;
+            const int row = arow0 + 16 * tl + 4 * g4 + r;
+            Nr[x][r] = (ns && tl < NAH && l16 == 0 && row < dk) ? ns[row] : 0.0f;
         }
     }
     for (int e = tid; e < DKP; e += NTH) nsh[e] = (ns && e < dk) ? ns[e] : 0.0f;
+    float sigma = 1.0f;  // C' (and n' tiles) are held divided by sigma
 
-    // ---- global -> LDS copies (16 bytes per lane, 64 consecutive granules per instruction)
-    // Physical granule p of a tile -> (row, logical granule); the lane fetches
-    // the logical granule so that the LDS image is the swizzled layout.
-    auto copy_tile = [&](bf16 *dst, const bf16 *src, int ld, int gpr_log2, int cols_valid_g,
-                         int rows, int tc) {
-        const int total = rows << gpr_log2;     // granules in the tile
+    // ---- global -> LDS copies.  Physical granule g of a tile is (row, gl)
+    // with gl = (g % gpr) ^ swz(row); each lane of a copy instruction fetches
+    // the granule that belongs at its LDS slot.
+    auto copy_tile = [&](bf16 *dst, const bf16 *src, int ld, int gpr_log2, int valid_g, int rows, int tc) {
+        const int total = rows << gpr_log2;
         const int gpr = 1 << gpr_log2;
         for (int blk = wave * 64; blk < total; blk += NW * 64) {
-            const int p = blk + lane;
-            const int row = p >> gpr_log2;
-            const int pg = p & (gpr - 1);
-            const int m = (gpr < 8 ? gpr - 1 : 7);
-            const int gl = pg ^ ((((row & 3) << 1) | ((row >> 2) & 1)) & m);
+            const int pgr = blk + lane;
+            const int row = pgr >> gpr_log2;
+            const int gl = (pgr & (gpr - 1)) ^ swz8(row);
             const int t = min(tc + row, t_end - 1);
-            if (gl < cols_valid_g)
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(src + (size_t)t * ld + gl * 8),
-                    (lds_void *)(dst + blk * 8), 16, 0, 0);
+            if (gl < valid_g)
+                __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)t * ld + gl * 8),
+                                                 (lds_void *)(dst + blk * 8), 16, 0, 0);
         }
     };
-    constexpr int QGL = QG == 4 ? 2 : QG == 8 ? 3 : QG == 16 ? 4 : 5;
+    constexpr int QGL = QG == 8 ? 3 : QG == 16 ? 4 : 5;
     constexpr int VGL = VG == 8 ? 3 : 4;
     static_assert((1 << QGL) == QG && (1 << VGL) == VG, "power-of-two tiles");
     const int dk_g = dk >> 3, bv_g = bv_here >> 3;
     auto copy_q = [&](int c) { copy_tile(Qs, qg, dk, QGL, dk_g, L, t_begin + c * L); };
-    auto copy_kv = [&](int c, int buf) {
-        copy_tile(Ks[buf], kg, dk, QGL, dk_g, L, t_begin + c * L);
-        copy_tile(Vs[buf], vg + col0, dv, VGL, bv_g, L, t_begin + c * L);
-    };
+    auto copy_k = [&](int c) { copy_tile(Ks[c & 1], kg, dk, QGL, dk_g, L, t_begin + c * L); };
+    auto copy_v = [&](int c) { copy_tile(Vs, vg, dv, VGL, bv_g, L, t_begin + c * L); };
 
-    // ---- gates (wavefront 0; one token per lane)
+    // ---- gates (wavefront NW-1; one token per lane)
+    constexpr int GW = NW - 1;
     float gf = 0.0f, gi = -INFINITY;
     auto load_gates = [&](int c) {
         const int t = t_begin + c * L + lane;
@@ -233,37 +274,33 @@ __global__ __launch_bounds__(256, 1) void mlstm_bf16_kernel(FwdArgs a) {
         gi = ok ? i : -INFINITY;
     };
     auto gate_prep = [&](float m_before, float *G) {
-        float b = gf;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(b, off, 64);
-            if (lane >= off) b += y;
-        }
+        const float b = wave_scan_add(gf);
         const float u = gi - b;
-        float pm = u;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(pm, off, 64);
-            if (lane >= off) pm = fmaxf(pm, y);
-        }
+        const float pm = wave_scan_max(u);
         const float r = fmaxf(m_before, pm);
         const float r_last = __shfl(r, L - 1, 64);
         const float b_last = __shfl(b, L - 1, 64);
         if (lane < L) {
+            const float w = exp_e(u - r_last);
             G[lane] = u;
             G[LP + lane] = r;
             G[2 * LP + lane] = exp_e(m_before - r);
             G[3 * LP + lane] = exp_e(-(b + r));
-            G[4 * LP + lane] = exp_e(u - r_last);
+            G[4 * LP + lane] = w;
+            const bf16 whi = (bf16)w;
+            const bf16 wlo = (bf16)(w - (float)whi);
+            bf16 *W2 = reinterpret_cast<bf16 *>(&G[5 * LP]);
+            W2[lane] = whi;
+            W2[LP + lane] = wlo;
         }
         if (lane == 0) {
-            G[5 * LP + 0] = b_last + r_last;          // stabilizer after the chunk
-            G[5 * LP + 1] = exp_e(m_before - r_last); // decay of the carried state
-            G[5 * LP + 2] = b_last;                   // sum of log forget gates
+            G[6 * LP + 0] = b_last + r_last;          // stabilizer after the chunk
+            G[6 * LP + 1] = exp_e(m_before - r_last); // decay of the carried state
+            G[6 * LP + 2] = b_last;                   // sum of the chunk's log forget gates
         }
     };
 
-    // causal tiles of S owned by this wavefront
+    // ---- causal S tiles of this wavefront: t = wave + NW x
     int tjt[MYT], tit[MYT];
     bool tok[MYT];
 #pragma unroll
@@ -275,13 +312,41 @@ __global__ __launch_bounds__(256, 1) void mlstm_bf16_kernel(FwdArgs a) {
         tit[x] = it;
         tjt[x] = t - it * (it + 1) / 2;
     }
+    // token tiles this wavefront finishes (balanced causal work between the pair)
+    // (NT = 4: tiles {0, 3} and {1, 2}; NT = 2: one each; NT = 1: the first half only)
+    auto fin_it = [&](int h, int f) -> int {
+        if (NT == 4) return h == 0 ? (f == 0 ? 0 : 3) : (f == 0 ? 1 : 2);
+        if (NT == 2) return h;
+        return h == 0 ? 0 : -1;
+    };
+    // register tile it of an array indexed by a wave-uniform runtime value
+    auto pick = [&](const f32x4(&arr)[NT], int it) -> f32x4 {
+        f32x4 r = arr[0];
+#pragma unroll
+        for (int k = 1; k < NT; ++k)
+            if (it == k) r = arr[k];
+        return r;
+    };
+
+    // ---- per-lane LDS offsets (loop invariant)
+    const int s16 = swz8(l16);                 // swizzle of rows 16 t + l16
+    // Q / K fragment for k-step ks: rows 16 t + l16, columns 32 ks + 4 g4 (+16)
+    int qkoff[2][2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            qkoff[par][hh] = l16 * DKP + (((((par << 2) | ((g4 >> 1) + 2 * hh)) ^ s16)) << 3) + 4 * (g4 & 1);
+    // transpose reads: rows 32 js + 8 g4 + te (+4), columns c0 + 4 tq
+    const int trow0 = (8 * g4 + te), trow1 = trow0 + 4;
 
     float g_total = 0.0f;
     if (nchunks > 0) {
         __syncthreads();  // zeroing done before the copies land
         if (!STATE_ONLY) copy_q(0);
-        copy_kv(0, 0);
-        if (wave == 0) {
+        copy_k(0);
+        copy_v(0);
+        if (wave == GW) {
             load_gates(0);
             gate_prep(m_prev, gt[0]);
         }
@@ -290,157 +355,178 @@ __global__ __launch_bounds__(256, 1) void mlstm_bf16_kernel(FwdArgs a) {
     __syncthreads();
 
     for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        const float *G = gt[buf];
+        const float *G = gt[c & 1];
         const int tc = t_begin + c * L;
-        const float m_next = G[5 * LP + 0], s_last = G[5 * LP + 1];
-        g_total += G[5 * LP + 2];
+        const float m_next = G[6 * LP + 0], s_last = G[6 * LP + 1];
+        g_total += G[6 * LP + 2];
         const bool more = c + 1 < nchunks;
-        const bf16 *K = Ks[buf];
-        const bf16 *V = Vs[buf];
+        const bf16 *K = Ks[c & 1];
 
-        // output-gate inputs of this chunk (rows clamped into the segment)
-        uint2 orw[NT][NBT];
+        // output-gate inputs of the token tiles this wavefront finishes
+        uint2 orw[NF][NBT];
         if (!STATE_ONLY) {
 #pragma unroll
-            for (int it = 0; it < NT; ++it)
+            for (int f = 0; f < NF; ++f) {
+                const int it = fin_it(hf, f);
 #pragma unroll
                 for (int bt = 0; bt < NBT; ++bt) {
-                    const int t = min(tc + 16 * it + l16, t_end - 1);
-                    const int b = min(col0 + wcol0 + 16 * bt + 4 * g4, dv - 4);
-                    orw[it][bt] = *reinterpret_cast<const uint2 *>(og + (size_t)t * dv + b);
+                    const int t = min(tc + 16 * max(it, 0) + l16, t_end - 1);
+                    const int b = min(col0 + wc0 + 16 * bt + 4 * g4, dv - 4);
+                    orw[f][bt] = *reinterpret_cast<const uint2 *>(og + (size_t)t * dv + b);
                 }
+            }
         }
         if (more) {
-            if (wave == 0) load_gates(c + 1);
-            copy_kv(c + 1, buf ^ 1);
+            if (wave == GW) load_gates(c + 1);
+            copy_k(c + 1);
         }
 
         f32x4 Ot[NBT][NT];
-        f32x4 St[MYT];
-        f32x4 Qn = {0.f, 0.f, 0.f, 0.f};
         if (!STATE_ONLY) {
+            // q.n' for every token (VALU, all threads): n' of the previous state
+            {
+                constexpr int PARTS = NTH / L;
+                constexpr int SPAN = DKP / PARTS;  // >= 2
+                const int i = tid / PARTS, part = tid % PARTS;
+                float acc = 0.0f;
+                if constexpr (SPAN >= 8) {
+#pragma unroll
+                    for (int e = 0; e < SPAN / 8; ++e) {
+                        const int col = part * SPAN + 8 * e;
+                        const bf16x8 qv = *reinterpret_cast<const bf16x8 *>(&Qs[sw_off<QG>(i, col)]);
+                        const f32x4 n0 = *reinterpret_cast<const f32x4 *>(&nsh[col]);
+                        const f32x4 n1 = *reinterpret_cast<const f32x4 *>(&nsh[col + 4]);
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            acc = fmaf((float)qv[x], n0[x], acc);
+                            acc = fmaf((float)qv[x + 4], n1[x], acc);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < SPAN; ++e) {
+                        const int col = part * SPAN + e;
+                        acc = fmaf((float)Qs[sw_off<QG>(i, col)], nsh[col], acc);
+                    }
+                }
+#pragma unroll
+                for (int off = 1; off < PARTS && off < 64; off <<= 1) acc += __shfl_xor(acc, off, 64);
+                if (part == 0) qn[i] = acc;
+            }
+
+            // O^T partial over this half of d_qk: C'^T Q^T (C' split hi + lo)
 #pragma unroll
             for (int bt = 0; bt < NBT; ++bt)
 #pragma unroll
                 for (int it = 0; it < NT; ++it) Ot[bt][it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int x = 0; x < MYT; ++x) St[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-            // ---- loop over d_qk: O^T = C'^T Q^T, S^T = K Q^T, qn = Q n'
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                // keep one k-step's fragments live at a time
-                __builtin_amdgcn_sched_barrier(0);
+            for (int kk = 0; kk < NKH; ++kk) {
+                __builtin_amdgcn_sched_barrier(0);  // bound the live fragments to one k-step
+                const int ks = hf * NKH + kk;  // global k-step (wave-uniform)
                 bf16x8 ach[NBT], acl[NBT];
 #pragma unroll
                 for (int bt = 0; bt < NBT; ++bt) {
-                    const float x[8] = {Cr[2 * ks][bt][0], Cr[2 * ks][bt][1], Cr[2 * ks][bt][2],
-                                        Cr[2 * ks][bt][3], Cr[2 * ks + 1][bt][0], Cr[2 * ks + 1][bt][1],
-                                        Cr[2 * ks + 1][bt][2], Cr[2 * ks + 1][bt][3]};
+                    const float x[8] = {Cr[2 * kk][bt][0], Cr[2 * kk][bt][1], Cr[2 * kk][bt][2],
+                                        Cr[2 * kk][bt][3], Cr[2 * kk + 1][bt][0], Cr[2 * kk + 1][bt][1],
+                                        Cr[2 * kk + 1][bt][2], Cr[2 * kk + 1][bt][3]};
                     split8(x, ach[bt], acl[bt]);
                 }
-                // n' as a 16-row operand with only row 0 non-zero (this wavefront's token tile)
-                bf16x8 anh, anl;
-                {
-                    const f32x4 n0 = *reinterpret_cast<const f32x4 *>(&nsh[32 * ks + 4 * g4]);
-                    const f32x4 n1 = *reinterpret_cast<const f32x4 *>(&nsh[32 * ks + 16 + 4 * g4]);
-                    const float z = l16 == 0 ? 1.0f : 0.0f;
-                    const float x[8] = {n0[0] * z, n0[1] * z, n0[2] * z, n0[3] * z,
-                                        n1[0] * z, n1[1] * z, n1[2] * z, n1[3] * z};
-                    split8(x, anh, anl);
-                }
+                const int kb = (ks >> 1) << 6;  // granule block of 8 (64 elements)
+                const int par = ks & 1;
 #pragma unroll
                 for (int it = 0; it < NT; ++it) {
-                    const int i = 16 * it + l16;
-                    const bf16x8 bq = cat8(
-                        *reinterpret_cast<const bf16x4 *>(&Qs[sw_off<QG>(i, 32 * ks + 4 * g4)]),
-                        *reinterpret_cast<const bf16x4 *>(&Qs[sw_off<QG>(i, 32 * ks + 16 + 4 * g4)]));
+                    const bf16 *q0 = Qs + 16 * it * DKP + kb;
+                    const bf16x8 bq = cat8(ld4(q0 + qkoff[par][0]), ld4(q0 + qkoff[par][1]));
 #pragma unroll
                     for (int bt = 0; bt < NBT; ++bt) {
                         Ot[bt][it] = mfma(ach[bt], bq, Ot[bt][it]);
                         Ot[bt][it] = mfma(acl[bt], bq, Ot[bt][it]);
                     }
-                    if (it == (wave % NT)) {
-                        Qn = mfma(anh, bq, Qn);
-                        Qn = mfma(anl, bq, Qn);
-                    }
+                }
+            }
+            // causal S tiles over all of d_qk
+            f32x4 St[MYT];
 #pragma unroll
-                    for (int x = 0; x < MYT; ++x) {
-                        if (tok[x] && tit[x] == it) {
-                            const int j = 16 * tjt[x] + l16;
-                            const bf16x8 ak = cat8(
-                                *reinterpret_cast<const bf16x4 *>(&K[sw_off<QG>(j, 32 * ks + 4 * g4)]),
-                                *reinterpret_cast<const bf16x4 *>(&K[sw_off<QG>(j, 32 * ks + 16 + 4 * g4)]));
-                            St[x] = mfma(ak, bq, St[x]);
-                        }
+            for (int x = 0; x < MYT; ++x) {
+                St[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (tok[x]) {
+                    const bf16 *q0 = Qs + 16 * tit[x] * DKP;
+                    const bf16 *k0 = K + 16 * tjt[x] * DKP;
+#pragma unroll
+                    for (int ks = 0; ks < 2 * NKH; ++ks) {
+                        if ((ks & 3) == 0) __builtin_amdgcn_sched_barrier(0);
+                        const int kb = (ks >> 1) << 6, par = ks & 1;
+                        const bf16x8 bq = cat8(ld4(q0 + kb + qkoff[par][0]), ld4(q0 + kb + qkoff[par][1]));
+                        const bf16x8 ak = cat8(ld4(k0 + kb + qkoff[par][0]), ld4(k0 + kb + qkoff[par][1]));
+                        St[x] = mfma(ak, bq, St[x]);
                     }
                 }
             }
-            // gates of the next chunk (wavefront 0), into the other table
-            if (more && wave == 0) gate_prep(m_next, gt[buf ^ 1]);
+            // next chunk's gate table (one wavefront)
+            if (more && wave == GW) gate_prep(m_next, gt[(c + 1) & 1]);
 
-            // P = S (x) e^{u_j - r_i} -> LDS; column sums -> den_part
+            // P = S (x) e^{u_j - r_i} -> LDS (bf16); column sums -> den_part
 #pragma unroll
             for (int x = 0; x < MYT; ++x) {
                 if (tok[x]) {
                     const int i = 16 * tit[x] + l16;
                     const float ri = G[LP + i];
-                    float p[4];
+                    float pv[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int j = 16 * tjt[x] + 4 * g4 + r;
-                        p[r] = (j <= i) ? St[x][r] * exp_e(G[j] - ri) : 0.0f;
+                        pv[r] = (j <= i) ? St[x][r] * exp_e(G[j] - ri) : 0.0f;
                     }
-                    const bf16x4 pb = {(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3]};
+                    const bf16x4 pb = {(bf16)pv[0], (bf16)pv[1], (bf16)pv[2], (bf16)pv[3]};
                     *reinterpret_cast<bf16x4 *>(&Ps[sw_off<PG>(i, 16 * tjt[x] + 4 * g4)]) = pb;
-                    float cs = (p[0] + p[1]) + (p[2] + p[3]);
+                    float cs = (pv[0] + pv[1]) + (pv[2] + pv[3]);
                     cs += __shfl_xor(cs, 16, 64);
                     cs += __shfl_xor(cs, 32, 64);
                     if (g4 == 0) den_part[(wave + NW * x) * 16 + l16] = cs;
                 }
             }
-            // q.n' for this wavefront's token tile: row 0 of Qn (lanes g4 == 0, r == 0)
-            if (wave < NT && g4 == 0) qn[16 * wave + l16] = Qn[0];
+            // hand the partner the partial sums of the tiles it finishes
 #pragma unroll
-            for (int it = 0; it < NT; ++it) {
-                const float si = G[2 * LP + 16 * it + l16];
+            for (int f = 0; f < NF; ++f) {
+                const int it = fin_it(hf ^ 1, f);
+                if (it >= 0) {
 #pragma unroll
-                for (int bt = 0; bt < NBT; ++bt) Ot[bt][it] *= si;
+                    for (int bt = 0; bt < NBT; ++bt) Xch[wave ^ 4][f * NBT + bt][lane] = pick(Ot[bt], it);
+                }
             }
         } else {
-            if (more && wave == 0) gate_prep(m_next, gt[buf ^ 1]);
+            if (more && wave == GW) gate_prep(m_next, gt[(c + 1) & 1]);
         }
-        __syncthreads();  // (C) P, den_part, qn visible; every wavefront is done with Q
+        __builtin_amdgcn_s_waitcnt(0);  // V of this chunk (copied at the end of the last one) has landed
+        __syncthreads();                // (C)
         if (more && !STATE_ONLY) copy_q(c + 1);
 
-        // V^T fragments (token index along k) by transpose reads of the row-major V tile
-        // lane (l16, g4): rows j = 32 js + 8 g4 + e (+4), columns b0 + 4 (l16 & 3)
-        const int te = l16 >> 2, tq = l16 & 3;
         if (!STATE_ONLY) {
-            // ---- O^T += V^T P^T, then h
+            // finish this wavefront's token tiles: partner's partial, inter scale,
+            // V^T P^T, normaliser, output gate
 #pragma unroll
-            for (int js = 0; js < NJS; ++js) {
-                bf16x8 av[NBT];
+            for (int f = 0; f < NF; ++f) {
+                const int it = fin_it(hf, f);
+                if (it < 0) continue;
+                const int i = 16 * it + l16;
+                const float si = G[2 * LP + i] * sigma;
+                f32x4 acc[NBT];
 #pragma unroll
-                for (int bt = 0; bt < NBT; ++bt) {
-                    const int b0 = wcol0 + 16 * bt + 4 * tq;
-                    const int j0 = 32 * js + 8 * g4 + te;
-                    av[bt] = cat8(tr_read(&V[sw_off<VG>(j0, b0)]), tr_read(&V[sw_off<VG>(j0 + 4, b0)]));
-                }
+                for (int bt = 0; bt < NBT; ++bt) acc[bt] = (pick(Ot[bt], it) + Xch[wave][f * NBT + bt][lane]) * si;
 #pragma unroll
-                for (int it = 0; it < NT; ++it) {
+                for (int js = 0; js < NJS; ++js) {
                     if (32 * js <= 16 * it + 15) {
-                        const int i = 16 * it + l16;
                         const bf16x8 bp = *reinterpret_cast<const bf16x8 *>(&Ps[sw_off<PG>(i, 32 * js + 8 * g4)]);
 #pragma unroll
-                        for (int bt = 0; bt < NBT; ++bt) Ot[bt][it] = mfma(av[bt], bp, Ot[bt][it]);
+                        for (int bt = 0; bt < NBT; ++bt) {
+                            const int c0 = wc0 + 16 * bt + 4 * tq;
+                            const bf16 *v0 = Vs + 32 * js * BV;
+                            const bf16x8 av = cat8(tr_read(v0 + sw_off<VG>(trow0, c0) ),
+                                                   tr_read(v0 + sw_off<VG>(trow1, c0)));
+                            acc[bt] = mfma(av, bp, acc[bt]);
+                        }
                     }
                 }
-            }
-#pragma unroll
-            for (int it = 0; it < NT; ++it) {
-                const int i = 16 * it + l16;
                 const int t = tc + i;
                 float den = G[2 * LP + i] * qn[i];
 #pragma unroll
@@ -448,15 +534,15 @@ __global__ __launch_bounds__(256, 1) void mlstm_bf16_kernel(FwdArgs a) {
                 const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), G[3 * LP + i]));
 #pragma unroll
                 for (int bt = 0; bt < NBT; ++bt) {
-                    const int b = col0 + wcol0 + 16 * bt + 4 * g4;
+                    const int b = col0 + wc0 + 16 * bt + 4 * g4;
                     if (t < t_end && b < dv) {
-                        const uint2 o4 = orw[it][bt];
+                        const uint2 o4 = orw[f][bt];
                         float y[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const uint32_t wd = e < 2 ? o4.x : o4.y;
                             const float ox = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
-                            y[e] = Ot[bt][it][e] * inv * __builtin_amdgcn_rcpf(1.0f + exp_e(-ox));
+                            y[e] = acc[bt][e] * inv * __builtin_amdgcn_rcpf(1.0f + exp_e(-ox));
                         }
                         const bf16x4 hv = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
                         *reinterpret_cast<bf16x4 *>(hg + (size_t)t * dv + b) = hv;
@@ -465,66 +551,79 @@ __global__ __launch_bounds__(256, 1) void mlstm_bf16_kernel(FwdArgs a) {
             }
         }
 
-        // ---- C' <- e^{m - r_last} C' + K^T (w (x) V);  n' <- e^{m - r_last} n' + K^T w
+        // ---- C'/sigma += K^T ((w/sigma') (x) V),  n'/sigma likewise  (sigma' = sigma * decay)
+        sigma *= s_last;
+        if (sigma < kRenorm) {  // uniform: fold sigma back into the held state
 #pragma unroll
-        for (int at = 0; at < NAT; ++at)
+            for (int at = 0; at < NAH; ++at)
 #pragma unroll
-            for (int bt = 0; bt < NBT; ++bt) Cr[at][bt] *= s_last;
+                for (int bt = 0; bt < NBT; ++bt) Cr[at][bt] *= sigma;
 #pragma unroll
-        for (int x = 0; x < NA_W; ++x) Nr[x] *= s_last;
+            for (int x = 0; x < NNW; ++x) Nr[x] *= sigma;
+            sigma = 1.0f;
+        }
+        const float rsig = 1.0f / sigma;
 #pragma unroll
         for (int js = 0; js < NJS; ++js) {
             float w8[8];
             {
                 const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&G[4 * LP + 32 * js + 8 * g4]);
                 const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&G[4 * LP + 32 * js + 8 * g4 + 4]);
-                w8[0] = w0[0]; w8[1] = w0[1]; w8[2] = w0[2]; w8[3] = w0[3];
-                w8[4] = w1[0]; w8[5] = w1[1]; w8[6] = w1[2]; w8[7] = w1[3];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    w8[e] = w0[e] * rsig;
+                    w8[e + 4] = w1[e] * rsig;
+                }
             }
             bf16x8 bw[NBT];
+            const bf16 *v0 = Vs + 32 * js * BV;
 #pragma unroll
             for (int bt = 0; bt < NBT; ++bt) {
-                const int b0 = wcol0 + 16 * bt + 4 * tq;
-                const int j0 = 32 * js + 8 * g4 + te;
-                const bf16x8 vv = cat8(tr_read(&V[sw_off<VG>(j0, b0)]), tr_read(&V[sw_off<VG>(j0 + 4, b0)]));
-                float x[8];
+                const int c0 = wc0 + 16 * bt + 4 * tq;
+                const bf16x8 vv = cat8(tr_read(v0 + sw_off<VG>(trow0, c0)), tr_read(v0 + sw_off<VG>(trow1, c0)));
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = (float)vv[e] * w8[e];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bw[bt][e] = (bf16)x[e];
+                for (int e = 0; e < 8; ++e) bw[bt][e] = (bf16)((float)vv[e] * w8[e]);
             }
-            // w as a 16-column operand with only column 0 non-zero (for n')
+            // w (hi, lo) as a 16-column operand with only column 0 non-zero (for n');
+            // the table holds w unscaled, the n' tiles are held divided by sigma too
             bf16x8 bnh, bnl;
             {
-                const float z = l16 == 0 ? 1.0f : 0.0f;
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = w8[e] * z;
-                split8(x, bnh, bnl);
+                const bf16 *W2 = reinterpret_cast<const bf16 *>(&G[5 * LP]);
+                const bf16 *ph = l16 == 0 ? W2 + 32 * js + 8 * g4 : reinterpret_cast<const bf16 *>(&zero16);
+                const bf16 *pl = l16 == 0 ? W2 + LP + 32 * js + 8 * g4 : reinterpret_cast<const bf16 *>(&zero16);
+                bnh = *reinterpret_cast<const bf16x8 *>(ph);
+                bnl = *reinterpret_cast<const bf16x8 *>(pl);
             }
+            const bf16 *k0 = K + 32 * js * DKP;
 #pragma unroll
-            for (int at = 0; at < NAT; ++at) {
+            for (int at = 0; at < NAH; ++at) {
                 if ((at & 3) == 0) __builtin_amdgcn_sched_barrier(0);
-                const int a0 = 16 * at + 4 * tq;
-                const int j0 = 32 * js + 8 * g4 + te;
-                const bf16x8 ak = cat8(tr_read(&K[sw_off<QG>(j0, a0)]), tr_read(&K[sw_off<QG>(j0 + 4, a0)]));
+                const int c0 = arow0 + 16 * at + 4 * tq;
+                const bf16x8 ak = cat8(tr_read(k0 + sw_off<QG>(trow0, c0)), tr_read(k0 + sw_off<QG>(trow1, c0)));
 #pragma unroll
                 for (int bt = 0; bt < NBT; ++bt) Cr[at][bt] = mfma(ak, bw[bt], Cr[at][bt]);
-                if (at / NA_W == wave) {
-                    Nr[at % NA_W] = mfma(ak, bnh, Nr[at % NA_W]);
-                    Nr[at % NA_W] = mfma(ak, bnl, Nr[at % NA_W]);
+#pragma unroll
+                for (int x = 0; x < NNW; ++x) {
+                    if (at == p + 4 * x) {
+                        f32x4 t0 = mfma(ak, bnh, f32x4{0.f, 0.f, 0.f, 0.f});
+                        t0 = mfma(ak, bnl, t0);
+                        Nr[x] += t0 * rsig;
+                    }
                 }
             }
         }
-        // publish n' (column 0 of the n' tiles) for the next chunk's q.n'
+        // publish n' (true scale) for the next chunk's q.n'
         if (l16 == 0) {
 #pragma unroll
-            for (int x = 0; x < NA_W; ++x)
-                *reinterpret_cast<f32x4 *>(&nsh[16 * (wave * NA_W + x) + 4 * g4]) = Nr[x];
+            for (int x = 0; x < NNW; ++x) {
+                const int tl = p + 4 * x;
+                if (tl < NAH) *reinterpret_cast<f32x4 *>(&nsh[arow0 + 16 * tl + 4 * g4]) = Nr[x] * sigma;
+            }
         }
         m_prev = m_next;
-        __builtin_amdgcn_s_waitcnt(0);  // this chunk's copies of the next chunk have landed
+        __builtin_amdgcn_s_waitcnt(0);  // next chunk's K and Q have landed
         __syncthreads();                // (D)
+        if (more) copy_v(c + 1);
     }
 
     // ---- state out
@@ -542,14 +641,14 @@ __global__ __launch_bounds__(256, 1) void mlstm_bf16_kernel(FwdArgs a) {
     }
     if (Cdst) {
 #pragma unroll
-        for (int at = 0; at < NAT; ++at)
+        for (int at = 0; at < NAH; ++at)
 #pragma unroll
             for (int bt = 0; bt < NBT; ++bt) {
-                const int b = col0 + wcol0 + 16 * bt + l16;
+                const int b = col0 + wc0 + 16 * bt + l16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * at + 4 * g4 + r;
-                    if (row < dk && b < dv) Cdst[(size_t)row * dv + b] = Cr[at][bt][r];
+                    const int row = arow0 + 16 * at + 4 * g4 + r;
+                    if (row < dk && b < dv) Cdst[(size_t)row * dv + b] = Cr[at][bt][r] * sigma;
                 }
             }
         if (tile == 0) {
