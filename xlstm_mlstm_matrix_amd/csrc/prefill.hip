@@ -9,7 +9,7 @@ int prefill_dkp(int dk) { return dk <= 32 ? 32 : dk <= 64 ? 64 : dk <= 128 ? 128
 
 int prefill_bv(int io_bf16, int dk, int dv, int chunk) {
     (void)dk; (void)chunk;
-    if (io_bf16) return dv >= 128 ? 128 : 64;
+    if (io_bf16) return (dv % 128 == 0 || (dv > 128 && dv % 64 != 0)) ? 128 : 64;
     return 64;
 }
 
@@ -88,18 +88,21 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(FwdArgs a, const float
 
 }  // namespace
 
-bool bf16_fast_path(int chunk, int dkp);
+bool bf16_fast_path(int chunk, int dk, int dv);
 
 bool prefill_supported(int io_bf16, int dk, int dv, int chunk) {
     const int dkp = prefill_dkp(dk);
     const int bv = prefill_bv(io_bf16, dk, dv, chunk);
-    if (io_bf16 && bf16_fast_path(chunk, dkp)) return true;
+    if (io_bf16 && bf16_fast_path(chunk, dk, dv)) return true;
     if (io_bf16) return bv == 128 ? shape_fits<bf16, 128>(chunk, dkp) : shape_fits<bf16, 64>(chunk, dkp);
     return shape_fits<float, 64>(chunk, dkp);
 }
 
-// bf16 kernel with LDS copies and transpose reads: chunk <= 64, padded d_qk >= 64
-bool bf16_fast_path(int chunk, int dkp) { return chunk <= 64 && dkp >= 64; }
+// bf16 kernel with LDS copies and transpose reads: chunk <= 64, d_qk in
+// {64, 128, 256} (no padding) and d_v a multiple of the column tile
+bool bf16_fast_path(int chunk, int dk, int dv) {
+    return chunk <= 64 && (dk == 64 || dk == 128 || dk == 256) && dv % 64 == 0;
+}
 
 template <int L, int DKP, int BV, bool SO>
 hipError_t run_bf16(const FwdArgs &a, hipStream_t s) {
@@ -124,7 +127,7 @@ hipError_t bf16_by_shape(const FwdArgs &a, int chunk, int dkp, hipStream_t s) {
 hipError_t launch_fused(const FwdArgs &a, int io_bf16, int chunk, int state_only, hipStream_t s) {
     const int dkp = prefill_dkp(a.dk);
     const int bv = prefill_bv(io_bf16, a.dk, a.dv, chunk);
-    if (io_bf16 && bf16_fast_path(chunk, dkp)) {
+    if (io_bf16 && bf16_fast_path(chunk, a.dk, a.dv)) {
         if (bv == 128)
             return state_only ? bf16_by_shape<128, true>(a, chunk, dkp, s)
                               : bf16_by_shape<128, false>(a, chunk, dkp, s);

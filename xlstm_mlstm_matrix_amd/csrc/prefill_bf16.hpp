@@ -18,9 +18,10 @@
 //    halves (split-K) and the partial sums are exchanged through LDS; each
 //    wavefront of the pair then finishes half of the chunk's token tiles;
 //  * Q, K, V are staged with global->LDS copies (16 B per lane) into
-//    row-major tiles whose 16-byte granules are XOR-swizzled per row; K is
-//    double buffered (next chunk's K lands during the whole chunk), V and Q
-//    are reloaded as soon as the current chunk is done with them;
+//    row-major tiles whose 16-byte granules are XOR-swizzled per row; each
+//    copy is issued after the last read of the buffer it refills within the
+//    chunk (K is double buffered), so it lands while the rest of the chunk
+//    and the start of the next one compute;
 //  * K^T and V^T fragments (token index along the MFMA k) come from the LDS
 //    transpose read (ds_read_b64_tr_b16) of the row-major tiles;
 //  * the read-out splits C' into a bf16 high part and a bf16 remainder (two
@@ -31,7 +32,10 @@
 //  * gate quantities of the next chunk are computed by one wavefront with
 //    DPP scans into a double-buffered table; q.n' is a small VALU dot
 //    product spread over all threads; n' is updated with MFMAs;
-//  * two workgroup barriers per chunk.
+//  * two workgroup barriers per chunk, ordering LDS only, so copies stay in
+//    flight across them.
+// This schedule needs d_qk in {64, 128, 256} and d_v a multiple of BV; other
+// shapes use the general kernel of prefill_kernel.hpp.
 #pragma once
 
 #include "prefill_kernel.hpp"
@@ -126,6 +130,31 @@ __device__ __forceinline__ float wave_scan_max(float x) {
     return x;
 }
 
+// Workgroup barrier for LDS data: this wavefront's LDS writes are complete
+// (lgkmcnt 0) and at most VM of its vector-memory operations are still
+// outstanding (they complete in issue order), so every global->LDS copy
+// issued before the last VM of them has landed for all wavefronts after the
+// barrier.  Copies issued later stay in flight across it.  The signal fences
+// keep the compiler from moving LDS accesses across the barrier.
+template <int VM>
+__device__ __forceinline__ void block_sync() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 0xf) | (0x7 << 4) | (0x0 << 8) | ((VM >> 4) << 14));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until at most VM of this wavefront's vector-memory operations are
+// outstanding (no LDS wait).  Placed before the use of a plain load's result
+// whose exact position in the issue order is known, so that the compiler does
+// not add a full drain of the global->LDS copies issued after it.
+template <int VM>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 0xf) | (0x7 << 4) | (0xf << 8) | ((VM >> 4) << 14));
+}
+
 template <int L, int DKP, int BV, bool STATE_ONLY>
 __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
     using Cfg = Bf16Cfg<L, DKP, BV>;
@@ -136,7 +165,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
     constexpr float kRenorm = 8.6736174e-19f;  // 2^-60: renormalise the lazy state scale below this
 
     __shared__ __attribute__((aligned(16))) bf16 Qs[LP * DKP];
-    __shared__ __attribute__((aligned(16))) bf16 Ks[2][LP * DKP];
+    __shared__ __attribute__((aligned(16))) bf16 Ks[2][LP * DKP];  // K of even / odd chunks
     __shared__ __attribute__((aligned(16))) bf16 Vs[LP * BV];
     __shared__ __attribute__((aligned(16))) bf16 Ps[L * LP];
     __shared__ __attribute__((aligned(16))) f32x4 Xch[NW][NF * NBT][64];
@@ -146,7 +175,6 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
     __shared__ float den_part[NCT * 16];
     __shared__ float qn[L];
     __shared__ __attribute__((aligned(16))) float nsh[DKP];
-    __shared__ __attribute__((aligned(16))) uint4 zero16;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -164,25 +192,24 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
     const int seg = rest % gseg;
     const int bh = rest / gseg;
 
-    const int dk = a.dk, dv = a.dv, T = a.T;
+    const int dk = a.dk, dv = a.dv, T = a.T;  // here dk == DKP and dv is a multiple of BV
     const int t_begin = seg * a.seg_len;
     const int t_end = min(t_begin + a.seg_len, T);
     const int nchunks = (t_end - t_begin + L - 1) / L;
     const int col0 = tile * BV;
     const int wc0 = p * WC;  // first column of this wavefront pair (tile-local)
-    const int bv_here = min(BV, dv - col0);
 
-    const bf16 *qg = static_cast<const bf16 *>(a.q) + (size_t)bh * T * dk;
-    const bf16 *kg = static_cast<const bf16 *>(a.k) + (size_t)bh * T * dk;
+    const bf16 *qg = static_cast<const bf16 *>(a.q) + (size_t)bh * T * DKP;
+    const bf16 *kg = static_cast<const bf16 *>(a.k) + (size_t)bh * T * DKP;
     const bf16 *vg = static_cast<const bf16 *>(a.v) + (size_t)bh * T * dv + col0;
-    const bf16 *og = static_cast<const bf16 *>(a.o) + (size_t)bh * T * dv;
-    bf16 *hg = static_cast<bf16 *>(a.h) + (size_t)bh * T * dv;
+    const bf16 *og = static_cast<const bf16 *>(a.o) + (size_t)bh * T * dv + col0;
+    bf16 *hg = static_cast<bf16 *>(a.h) + (size_t)bh * T * dv + col0;
     const float *igg = a.ig + (size_t)bh * T;
     const float *fgg = a.fg + (size_t)bh * T;
 
-    // ---- zero every tile once: padding rows/columns and P's upper tiles stay zero
+    // ---- zero every tile once: padding rows and P's upper tiles stay zero
     {
-        uint4 z = make_uint4(0, 0, 0, 0);
+        const uint4 z = make_uint4(0, 0, 0, 0);
         uint4 *q4 = reinterpret_cast<uint4 *>(Qs);
         for (int e = tid; e < LP * DKP / 8; e += NTH) q4[e] = z;
         uint4 *k4 = reinterpret_cast<uint4 *>(&Ks[0][0]);
@@ -192,10 +219,9 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
         uint4 *p4 = reinterpret_cast<uint4 *>(Ps);
         for (int e = tid; e < L * LP / 8; e += NTH) p4[e] = z;
         for (int e = tid; e < 2 * GTF; e += NTH) (&gt[0][0])[e] = 0.0f;
-        if (tid == 0) zero16 = z;
     }
 
-    // ---- initial state (C' in this wavefront's half of d_qk, its pair's columns)
+    // ---- initial state (C' rows of this wavefront's d_qk half, its pair's columns)
     const size_t rec = seg_state_floats(dk, dv);
     const float *Cs = nullptr, *ns = nullptr;
     float m_prev = 0.0f;
@@ -212,70 +238,94 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
         m_prev = a.m0[bh];
     }
     const int arow0 = hf * (DKP / 2);  // first d_qk row of this wavefront's half
+    const int bcol = col0 + wc0 + l16; // state column of this lane (tile bt adds 16 bt)
     f32x4 Cr[NAH][NBT];
 #pragma unroll
     for (int at = 0; at < NAH; ++at)
 #pragma unroll
-        for (int bt = 0; bt < NBT; ++bt) {
-            const int b = col0 + wc0 + 16 * bt + l16;
+        for (int bt = 0; bt < NBT; ++bt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = arow0 + 16 * at + 4 * g4 + r;
-                Cr[at][bt][r] = (Cs && row < dk && b < dv) ? Cs[(size_t)row * dv + b] : 0.0f;
+            for (int r = 0; r < 4; ++r)
+                Cr[at][bt][r] = Cs ? Cs[(size_t)(arow0 + 16 * at + 4 * g4 + r) * dv + bcol + 16 * bt] : 0.0f;
+    // n' lives in LDS (true scale); 16-row tiles p + 4x of each half are
+    // updated by the wavefront (p, hf) with an MFMA whose column 0 is K^T w
+    for (int e = tid; e < DKP; e += NTH) nsh[e] = ns ? ns[e] : 0.0f;
+    float sigma = 1.0f;  // C' is held divided by sigma
+
+    // ---- global -> LDS copies, fully unrolled.  Physical granule g of a tile
+    // is (row, gl) with gl = (g % gpr) ^ swz(row); each lane of a copy
+    // instruction fetches the granule that belongs at its LDS slot.  Rows past
+    // the segment end are clamped to its last row (finite data; their gates
+    // zero them out).
+    // Instruction k of a wavefront fills granules [(k NW + wave) 64, +64), i.e.
+    // rows row0 + k RPI with RPI = NW 64 / GPR a multiple of 8, so the swizzle
+    // of a lane is the same for every k: the per-lane part of the address is
+    // one byte offset (voff), the rest is uniform.
+    // (recomputed at every copy from an opaque copy of the lane index, so the
+    // compiler does not keep it live across the chunk loop)
+    auto lane_voff = [&](auto gpr_c, int ld) -> int {
+        constexpr int GPR = decltype(gpr_c)::value;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int pgr = wave * 64 + ln;
+        const int row = pgr / GPR;
+        const int gl = (pgr % GPR) ^ swz8(row);
+        return row * ld * 2 + gl * 16;
+    };
+    auto copy_tile = [&](bf16 *dst, const bf16 *src, int ld, auto gpr_c, int tc) {
+        constexpr int GPR = decltype(gpr_c)::value;
+        const int voff = lane_voff(gpr_c, ld);
+        constexpr int TOTAL = L * GPR;                    // granules
+        constexpr int NI = (TOTAL + NW * 64 - 1) / (NW * 64);
+        constexpr int RPI = NW * 64 / GPR;
+        static_assert(RPI % 8 == 0, "rows per copy instruction keep the swizzle");
+        if (tc + L <= t_end) {  // whole chunk inside the segment
+#pragma unroll
+            for (int k = 0; k < NI; ++k) {
+                const int blk = (k * NW + wave) * 64;
+                if (TOTAL % (NW * 64) == 0 || blk < TOTAL) {
+                    const char *base = reinterpret_cast<const char *>(src + (size_t)(tc + k * RPI) * ld);
+                    __builtin_amdgcn_global_load_lds((const void *)(base + voff), (lds_void *)(dst + blk * 8),
+                                                     16, 0, 0);
+                }
+            }
+        } else {  // last chunk of the segment: rows past its end read its last row
+            // (same instruction count as above, so waits on later copies stay exact)
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+#pragma unroll
+            for (int k = 0; k < NI; ++k) {
+                const int blk = (k * NW + wave) * 64;
+                if (TOTAL % (NW * 64) == 0 || blk < TOTAL) {
+                    const int pgr = blk + ln;
+                    const int row = pgr / GPR;
+                    const int gl = (pgr % GPR) ^ swz8(row);
+                    const int t = min(tc + row, t_end - 1);
+                    __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)t * ld + gl * 8),
+                                                     (lds_void *)(dst + blk * 8), 16, 0, 0);
+                }
             }
         }
-    // n' tiles kept by this wavefront: tiles arow0/16 + p + 4x (column 0 of an MFMA tile)
-    f32x4 Nr[NNW];
-#pragma unroll
-    for (int x = 0; x < NNW; ++x) {
-        const int tl = p + 4 * x;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = arow0 + 16 * tl + 4 * g4 + r;
-            Nr[x][r] = (ns && tl < NAH && l16 == 0 && row < dk) ? ns[row] : 0.0f;
-        }
-    }
-    for (int e = tid; e < DKP; e += NTH) nsh[e] = (ns && e < dk) ? ns[e] : 0.0f;
-    float sigma = 1.0f;  // C' (and n' tiles) are held divided by sigma
-
-    // ---- global -> LDS copies.  Physical granule g of a tile is (row, gl)
-    // with gl = (g % gpr) ^ swz(row); each lane of a copy instruction fetches
-    // the granule that belongs at its LDS slot.
-    auto copy_tile = [&](bf16 *dst, const bf16 *src, int ld, int gpr_log2, int valid_g, int rows, int tc) {
-        const int total = rows << gpr_log2;
-        const int gpr = 1 << gpr_log2;
-        for (int blk = wave * 64; blk < total; blk += NW * 64) {
-            const int pgr = blk + lane;
-            const int row = pgr >> gpr_log2;
-            const int gl = (pgr & (gpr - 1)) ^ swz8(row);
-            const int t = min(tc + row, t_end - 1);
-            if (gl < valid_g)
-                __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)t * ld + gl * 8),
-                                                 (lds_void *)(dst + blk * 8), 16, 0, 0);
-        }
     };
-    constexpr int QGL = QG == 8 ? 3 : QG == 16 ? 4 : 5;
-    constexpr int VGL = VG == 8 ? 3 : 4;
-    static_assert((1 << QGL) == QG && (1 << VGL) == VG, "power-of-two tiles");
-    const int dk_g = dk >> 3, bv_g = bv_here >> 3;
-    auto copy_q = [&](int c) { copy_tile(Qs, qg, dk, QGL, dk_g, L, t_begin + c * L); };
-    auto copy_k = [&](int c) { copy_tile(Ks[c & 1], kg, dk, QGL, dk_g, L, t_begin + c * L); };
-    auto copy_v = [&](int c) { copy_tile(Vs, vg, dv, VGL, bv_g, L, t_begin + c * L); };
+    using QGc = std::integral_constant<int, QG>;
+    using VGc = std::integral_constant<int, VG>;
 
-    // ---- gates (wavefront NW-1; one token per lane)
+    // ---- gates (wavefront GW; one token per lane)
     constexpr int GW = NW - 1;
+    // raw loads here; lanes past the segment are masked in gate_prep, so the
+    // loads stay in flight until then
     float gf = 0.0f, gi = -INFINITY;
+    bool gok = false;
     auto load_gates = [&](int c) {
         const int t = t_begin + c * L + lane;
-        const bool ok = lane < L && t < t_end;
+        gok = lane < L && t < t_end;
         const int tc = min(t, t_end - 1);
-        const float f = fgg[tc], i = igg[tc];
-        gf = ok ? f : 0.0f;
-        gi = ok ? i : -INFINITY;
+        gf = fgg[tc];
+        gi = igg[tc];
     };
     auto gate_prep = [&](float m_before, float *G) {
-        const float b = wave_scan_add(gf);
-        const float u = gi - b;
+        const float b = wave_scan_add(gok ? gf : 0.0f);
+        const float u = (gok ? gi : -INFINITY) - b;
         const float pm = wave_scan_max(u);
         const float r = fmaxf(m_before, pm);
         const float r_last = __shfl(r, L - 1, 64);
@@ -312,24 +362,28 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
         tit[x] = it;
         tjt[x] = t - it * (it + 1) / 2;
     }
-    // token tiles this wavefront finishes (balanced causal work between the pair)
-    // (NT = 4: tiles {0, 3} and {1, 2}; NT = 2: one each; NT = 1: the first half only)
-    auto fin_it = [&](int h, int f) -> int {
-        if (NT == 4) return h == 0 ? (f == 0 ? 0 : 3) : (f == 0 ? 1 : 2);
-        if (NT == 2) return h;
-        return h == 0 ? 0 : -1;
-    };
-    // register tile it of an array indexed by a wave-uniform runtime value
-    auto pick = [&](const f32x4(&arr)[NT], int it) -> f32x4 {
-        f32x4 r = arr[0];
-#pragma unroll
-        for (int k = 1; k < NT; ++k)
-            if (it == k) r = arr[k];
-        return r;
-    };
+    // token tiles of the read-out in slot order: this wavefront's own tiles
+    // first (it finishes them), then the partner's (it hands their partial
+    // sums over).  NT = 4: tiles {0, 3} and {1, 2} (balanced causal work).
+    const int nown = (NT == 1 && hf == 1) ? 0 : NF;
+    int slot_it[NT];
+    if constexpr (NT == 4) {
+        slot_it[0] = hf;
+        slot_it[1] = 3 - hf;
+        slot_it[2] = 1 - hf;
+        slot_it[3] = 2 + hf;
+    } else if constexpr (NT == 2) {
+        slot_it[0] = hf;
+        slot_it[1] = 1 - hf;
+    } else {
+        slot_it[0] = 0;
+    }
+    // own slot f needs the k-step js of V^T P^T (P is zero above the diagonal):
+    // with NT = 4 the first own tile is 0 or 1 (one k-step), the second 2 or 3
+    auto need_js = [](int f, int js) constexpr { return js == 0 || (NT == 4 && f == 1); };
 
     // ---- per-lane LDS offsets (loop invariant)
-    const int s16 = swz8(l16);                 // swizzle of rows 16 t + l16
+    const int s16 = swz8(l16);  // swizzle of rows 16 t + l16
     // Q / K fragment for k-step ks: rows 16 t + l16, columns 32 ks + 4 g4 (+16)
     int qkoff[2][2];
 #pragma unroll
@@ -337,53 +391,59 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
             qkoff[par][hh] = l16 * DKP + (((((par << 2) | ((g4 >> 1) + 2 * hh)) ^ s16)) << 3) + 4 * (g4 & 1);
+    auto qk_frag = [&](const bf16 *tilebase, int ks) -> bf16x8 {  // tilebase: row 16 t of the tile
+        const bf16 *b = tilebase + ((ks >> 1) << 6);
+        return cat8(ld4(b + qkoff[ks & 1][0]), ld4(b + qkoff[ks & 1][1]));
+    };
     // transpose reads: rows 32 js + 8 g4 + te (+4), columns c0 + 4 tq
-    const int trow0 = (8 * g4 + te), trow1 = trow0 + 4;
+    const int trow0 = 8 * g4 + te, trow1 = trow0 + 4;
+    auto tr_frag = [&](const bf16 *rowblock, auto gpr_c, int c0) -> bf16x8 {
+        constexpr int GPR = decltype(gpr_c)::value;
+        return cat8(tr_read(rowblock + sw_off<GPR>(trow0, c0)), tr_read(rowblock + sw_off<GPR>(trow1, c0)));
+    };
 
     float g_total = 0.0f;
     if (nchunks > 0) {
-        __syncthreads();  // zeroing done before the copies land
-        if (!STATE_ONLY) copy_q(0);
-        copy_k(0);
-        copy_v(0);
+        block_sync<0>();  // zeroing done before the copies land
+        if (!STATE_ONLY) copy_tile(Qs, qg, DKP, QGc{}, t_begin);
+        copy_tile(Ks[0], kg, DKP, QGc{}, t_begin);
+        copy_tile(Vs, vg, dv, VGc{}, t_begin);
         if (wave == GW) {
             load_gates(0);
+            vm_wait<0>();
             gate_prep(m_prev, gt[0]);
         }
-        __builtin_amdgcn_s_waitcnt(0);
     }
-    __syncthreads();
+    block_sync<0>();
 
+    // Pipeline of the copies (each fills a buffer no wavefront reads until a
+    // later barrier):
+    //   after the S tiles of chunk c   K(c+1) -> the other K buffer (read
+    //                                  last in chunk c-1)
+    //   after barrier C                Q(c+1) (every wavefront is done with Q(c))
+    //   after barrier D                V(c+1) (first read after barrier C of c+1)
+    // Barrier C waits for V(c), barrier D for Q(c+1) and K(c+1).
+    constexpr int NIK = (L * QG) / (NW * 64);          // K (and Q) copy instructions per wavefront
+    constexpr bool EXACT = (L * QG) % (NW * 64) == 0 && NT >= 2;
+    constexpr int NORW = NF * NBT;                      // output-gate loads after the K copy
+    constexpr int VM_C = EXACT ? NIK + NORW : 0;        // outstanding allowed at barrier C
+    constexpr int VM_D = EXACT ? NF * NBT : 0;          // ... at barrier D (this chunk's h stores)
     for (int c = 0; c < nchunks; ++c) {
+        const bf16 *K = Ks[c & 1];
+        bf16 *Knext = Ks[(c + 1) & 1];
         const float *G = gt[c & 1];
+        float *Gnext = gt[(c + 1) & 1];
         const int tc = t_begin + c * L;
         const float m_next = G[6 * LP + 0], s_last = G[6 * LP + 1];
         g_total += G[6 * LP + 2];
         const bool more = c + 1 < nchunks;
-        const bf16 *K = Ks[c & 1];
 
-        // output-gate inputs of the token tiles this wavefront finishes
-        uint2 orw[NF][NBT];
-        if (!STATE_ONLY) {
-#pragma unroll
-            for (int f = 0; f < NF; ++f) {
-                const int it = fin_it(hf, f);
-#pragma unroll
-                for (int bt = 0; bt < NBT; ++bt) {
-                    const int t = min(tc + 16 * max(it, 0) + l16, t_end - 1);
-                    const int b = min(col0 + wc0 + 16 * bt + 4 * g4, dv - 4);
-                    orw[f][bt] = *reinterpret_cast<const uint2 *>(og + (size_t)t * dv + b);
-                }
-            }
-        }
-        if (more) {
-            if (wave == GW) load_gates(c + 1);
-            copy_k(c + 1);
-        }
+        uint2 orw[NF][NBT];  // output-gate inputs of this wavefront's own tiles
+        if (more && wave == GW) load_gates(c + 1);
 
         f32x4 Ot[NBT][NT];
         if (!STATE_ONLY) {
-            // q.n' for every token (VALU, all threads): n' of the previous state
+            // q.n' for every token (VALU, all threads), n' of the previous state
             {
                 constexpr int PARTS = NTH / L;
                 constexpr int SPAN = DKP / PARTS;  // >= 2
@@ -414,37 +474,8 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
                 if (part == 0) qn[i] = acc;
             }
 
-            // O^T partial over this half of d_qk: C'^T Q^T (C' split hi + lo)
-#pragma unroll
-            for (int bt = 0; bt < NBT; ++bt)
-#pragma unroll
-                for (int it = 0; it < NT; ++it) Ot[bt][it] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < NKH; ++kk) {
-                __builtin_amdgcn_sched_barrier(0);  // bound the live fragments to one k-step
-                const int ks = hf * NKH + kk;  // global k-step (wave-uniform)
-                bf16x8 ach[NBT], acl[NBT];
-#pragma unroll
-                for (int bt = 0; bt < NBT; ++bt) {
-                    const float x[8] = {Cr[2 * kk][bt][0], Cr[2 * kk][bt][1], Cr[2 * kk][bt][2],
-                                        Cr[2 * kk][bt][3], Cr[2 * kk + 1][bt][0], Cr[2 * kk + 1][bt][1],
-                                        Cr[2 * kk + 1][bt][2], Cr[2 * kk + 1][bt][3]};
-                    split8(x, ach[bt], acl[bt]);
-                }
-                const int kb = (ks >> 1) << 6;  // granule block of 8 (64 elements)
-                const int par = ks & 1;
-#pragma unroll
-                for (int it = 0; it < NT; ++it) {
-                    const bf16 *q0 = Qs + 16 * it * DKP + kb;
-                    const bf16x8 bq = cat8(ld4(q0 + qkoff[par][0]), ld4(q0 + qkoff[par][1]));
-#pragma unroll
-                    for (int bt = 0; bt < NBT; ++bt) {
-                        Ot[bt][it] = mfma(ach[bt], bq, Ot[bt][it]);
-                        Ot[bt][it] = mfma(acl[bt], bq, Ot[bt][it]);
-                    }
-                }
-            }
-            // causal S tiles over all of d_qk
+            __builtin_amdgcn_sched_barrier(0);
+            // causal S tiles over all of d_qk (next k-step's fragments fetched ahead)
             f32x4 St[MYT];
 #pragma unroll
             for (int x = 0; x < MYT; ++x) {
@@ -452,18 +483,30 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
                 if (tok[x]) {
                     const bf16 *q0 = Qs + 16 * tit[x] * DKP;
                     const bf16 *k0 = K + 16 * tjt[x] * DKP;
+                    bf16x8 fq = qk_frag(q0, 0), fk = qk_frag(k0, 0);
 #pragma unroll
                     for (int ks = 0; ks < 2 * NKH; ++ks) {
-                        if ((ks & 3) == 0) __builtin_amdgcn_sched_barrier(0);
-                        const int kb = (ks >> 1) << 6, par = ks & 1;
-                        const bf16x8 bq = cat8(ld4(q0 + kb + qkoff[par][0]), ld4(q0 + kb + qkoff[par][1]));
-                        const bf16x8 ak = cat8(ld4(k0 + kb + qkoff[par][0]), ld4(k0 + kb + qkoff[par][1]));
-                        St[x] = mfma(ak, bq, St[x]);
+                        bf16x8 nq, nk;
+                        if (ks + 1 < 2 * NKH) {
+                            nq = qk_frag(q0, ks + 1);
+                            nk = qk_frag(k0, ks + 1);
+                        }
+                        St[x] = mfma(fk, fq, St[x]);
+                        if (ks + 1 < 2 * NKH) {
+                            fq = nq;
+                            fk = nk;
+                        }
                     }
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            // K(c) is not read again until the state update: fetch K(c+1)
+            if (more) copy_tile(Knext, kg, DKP, QGc{}, tc + L);
             // next chunk's gate table (one wavefront)
-            if (more && wave == GW) gate_prep(m_next, gt[(c + 1) & 1]);
+            if (more && wave == GW) {
+                vm_wait<EXACT ? NIK : 0>();  // gate loads were issued before the K copy
+                gate_prep(m_next, Gnext);
+            }
 
             // P = S (x) e^{u_j - r_i} -> LDS (bf16); column sums -> den_part
 #pragma unroll
@@ -485,57 +528,113 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
                     if (g4 == 0) den_part[(wave + NW * x) * 16 + l16] = cs;
                 }
             }
-            // hand the partner the partial sums of the tiles it finishes
+            __builtin_amdgcn_sched_barrier(0);
+            // O^T partial over this half of d_qk: C'^T Q^T, C' split into hi + lo.
+            // Q fragments of the next k-step are fetched before this one's MFMAs.
 #pragma unroll
-            for (int f = 0; f < NF; ++f) {
-                const int it = fin_it(hf ^ 1, f);
-                if (it >= 0) {
+            for (int bt = 0; bt < NBT; ++bt)
 #pragma unroll
-                    for (int bt = 0; bt < NBT; ++bt) Xch[wave ^ 4][f * NBT + bt][lane] = pick(Ot[bt], it);
+                for (int s = 0; s < NT; ++s) Ot[bt][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const bf16 *qrow[NT];
+#pragma unroll
+            for (int s = 0; s < NT; ++s) qrow[s] = Qs + 16 * slot_it[s] * DKP;
+            bf16x8 bq = qk_frag(qrow[0], hf * NKH);
+#pragma unroll
+            for (int kk = 0; kk < NKH; ++kk) {
+                bf16x8 ach[NBT], acl[NBT];
+#pragma unroll
+                for (int bt = 0; bt < NBT; ++bt) {
+                    const float x[8] = {Cr[2 * kk][bt][0], Cr[2 * kk][bt][1], Cr[2 * kk][bt][2],
+                                        Cr[2 * kk][bt][3], Cr[2 * kk + 1][bt][0], Cr[2 * kk + 1][bt][1],
+                                        Cr[2 * kk + 1][bt][2], Cr[2 * kk + 1][bt][3]};
+                    split8(x, ach[bt], acl[bt]);
+                }
+#pragma unroll
+                for (int s = 0; s < NT; ++s) {
+                    bf16x8 bqn;
+                    const bool nxt = s + 1 < NT || kk + 1 < NKH;
+                    if (nxt) bqn = qk_frag(qrow[(s + 1) % NT], hf * NKH + kk + (s + 1) / NT);
+#pragma unroll
+                    for (int bt = 0; bt < NBT; ++bt) {
+                        Ot[bt][s] = mfma(ach[bt], bq, Ot[bt][s]);
+                        Ot[bt][s] = mfma(acl[bt], bq, Ot[bt][s]);
+                    }
+                    if (nxt) bq = bqn;
                 }
             }
+            // hand the partner the partial sums of the tiles it finishes
+#pragma unroll
+            for (int s = 0; s < NT; ++s) {
+                if (s >= nown) {
+#pragma unroll
+                    for (int bt = 0; bt < NBT; ++bt) Xch[wave ^ 4][(s - nown) * NBT + bt][lane] = Ot[bt][s];
+                }
+            }
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+#pragma unroll
+                for (int bt = 0; bt < NBT; ++bt) {
+                    const int t = min(tc + 16 * slot_it[f] + l16, t_end - 1);
+                    orw[f][bt] = *reinterpret_cast<const uint2 *>(og + (size_t)t * dv + wc0 + 16 * bt + 4 * g4);
+                }
         } else {
-            if (more && wave == GW) gate_prep(m_next, gt[(c + 1) & 1]);
+            if (more) copy_tile(Knext, kg, DKP, QGc{}, tc + L);
+            if (more && wave == GW) {
+                vm_wait<EXACT ? NIK : 0>();  // gate loads were issued before the K copy
+                gate_prep(m_next, Gnext);
+            }
         }
-        __builtin_amdgcn_s_waitcnt(0);  // V of this chunk (copied at the end of the last one) has landed
-        __syncthreads();                // (C)
-        if (more && !STATE_ONLY) copy_q(c + 1);
+        // (C) V(c) landed; P, den_part, qn, Xch visible; Q(c) free.  The last
+        // chunk issued no K copy, so only the output-gate loads may stay.
+        if (more)
+            block_sync<STATE_ONLY ? 0 : VM_C>();
+        else
+            block_sync<(STATE_ONLY || !EXACT) ? 0 : NORW>();
+        if (more && !STATE_ONLY) copy_tile(Qs, qg, DKP, QGc{}, tc + L);
+        // output-gate loads (issued before barrier C) complete; Q(c+1) stays in flight
+        if (!STATE_ONLY) {
+            if (more)
+                vm_wait<EXACT ? NIK : 0>();
+            else
+                vm_wait<0>();
+        }
 
         if (!STATE_ONLY) {
-            // finish this wavefront's token tiles: partner's partial, inter scale,
-            // V^T P^T, normaliser, output gate
+            // finish this wavefront's own token tiles: partner's partial,
+            // inter-chunk scale, V^T P^T, normaliser, output gate
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
-                const int it = fin_it(hf, f);
-                if (it < 0) continue;
+                __builtin_amdgcn_sched_barrier(0);
+                if (f >= nown) continue;
+                const int it = slot_it[f];
                 const int i = 16 * it + l16;
                 const float si = G[2 * LP + i] * sigma;
                 f32x4 acc[NBT];
 #pragma unroll
-                for (int bt = 0; bt < NBT; ++bt) acc[bt] = (pick(Ot[bt], it) + Xch[wave][f * NBT + bt][lane]) * si;
+                for (int bt = 0; bt < NBT; ++bt) acc[bt] = (Ot[bt][f] + Xch[wave][f * NBT + bt][lane]) * si;
+                // O^T += V^T P^T (fragments loaded next to their use: low register pressure;
+                // the other wavefront on the SIMD covers the LDS latency)
 #pragma unroll
                 for (int js = 0; js < NJS; ++js) {
-                    if (32 * js <= 16 * it + 15) {
+                    if (need_js(f, js)) {
                         const bf16x8 bp = *reinterpret_cast<const bf16x8 *>(&Ps[sw_off<PG>(i, 32 * js + 8 * g4)]);
 #pragma unroll
-                        for (int bt = 0; bt < NBT; ++bt) {
-                            const int c0 = wc0 + 16 * bt + 4 * tq;
-                            const bf16 *v0 = Vs + 32 * js * BV;
-                            const bf16x8 av = cat8(tr_read(v0 + sw_off<VG>(trow0, c0) ),
-                                                   tr_read(v0 + sw_off<VG>(trow1, c0)));
-                            acc[bt] = mfma(av, bp, acc[bt]);
-                        }
+                        for (int bt = 0; bt < NBT; ++bt)
+                            acc[bt] = mfma(tr_frag(Vs + 32 * js * BV, VGc{}, wc0 + 16 * bt + 4 * tq), bp, acc[bt]);
                     }
                 }
-                const int t = tc + i;
                 float den = G[2 * LP + i] * qn[i];
+                // column tiles jt <= it contribute; every index below stays inside den_part
 #pragma unroll
-                for (int jt = 0; jt <= it; ++jt) den += den_part[(it * (it + 1) / 2 + jt) * 16 + l16];
+                for (int jt = 0; jt < NT; ++jt) {
+                    const float dp = den_part[(it * (it + 1) / 2 + jt) * 16 + l16];
+                    den += jt <= it ? dp : 0.0f;
+                }
                 const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), G[3 * LP + i]));
+                const int t = tc + i;
+                if (t < t_end) {
 #pragma unroll
-                for (int bt = 0; bt < NBT; ++bt) {
-                    const int b = col0 + wc0 + 16 * bt + 4 * g4;
-                    if (t < t_end && b < dv) {
+                    for (int bt = 0; bt < NBT; ++bt) {
                         const uint2 o4 = orw[f][bt];
                         float y[4];
 #pragma unroll
@@ -545,12 +644,13 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
                             y[e] = acc[bt][e] * inv * __builtin_amdgcn_rcpf(1.0f + exp_e(-ox));
                         }
                         const bf16x4 hv = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
-                        *reinterpret_cast<bf16x4 *>(hg + (size_t)t * dv + b) = hv;
+                        *reinterpret_cast<bf16x4 *>(hg + (size_t)t * dv + wc0 + 16 * bt + 4 * g4) = hv;
                     }
                 }
             }
         }
 
+        __builtin_amdgcn_sched_barrier(0);
         // ---- C'/sigma += K^T ((w/sigma') (x) V),  n'/sigma likewise  (sigma' = sigma * decay)
         sigma *= s_last;
         if (sigma < kRenorm) {  // uniform: fold sigma back into the held state
@@ -558,13 +658,20 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
             for (int at = 0; at < NAH; ++at)
 #pragma unroll
                 for (int bt = 0; bt < NBT; ++bt) Cr[at][bt] *= sigma;
-#pragma unroll
-            for (int x = 0; x < NNW; ++x) Nr[x] *= sigma;
             sigma = 1.0f;
         }
-        const float rsig = 1.0f / sigma;
+        const float rsig = __builtin_amdgcn_rcpf(sigma);
+        f32x4 nacc[NNW];  // K^T w for this wavefront's n' tiles (column 0)
+#pragma unroll
+        for (int x = 0; x < NNW; ++x) nacc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int js = 0; js < NJS; ++js) {
+            const bf16 *k0 = K + 32 * js * DKP;
+            // K^T fragments in groups of 4 d_qk tiles, the next group fetched ahead
+            constexpr int GRP = 2;  // NAH is even
+            bf16x8 ak[GRP];
+#pragma unroll
+            for (int u = 0; u < GRP; ++u) ak[u] = tr_frag(k0, QGc{}, arow0 + 16 * u + 4 * tq);
             float w8[8];
             {
                 const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&G[4 * LP + 32 * js + 8 * g4]);
@@ -576,54 +683,66 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
                 }
             }
             bf16x8 bw[NBT];
-            const bf16 *v0 = Vs + 32 * js * BV;
 #pragma unroll
             for (int bt = 0; bt < NBT; ++bt) {
-                const int c0 = wc0 + 16 * bt + 4 * tq;
-                const bf16x8 vv = cat8(tr_read(v0 + sw_off<VG>(trow0, c0)), tr_read(v0 + sw_off<VG>(trow1, c0)));
+                const bf16x8 vv = tr_frag(Vs + 32 * js * BV, VGc{}, wc0 + 16 * bt + 4 * tq);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) bw[bt][e] = (bf16)((float)vv[e] * w8[e]);
             }
-            // w (hi, lo) as a 16-column operand with only column 0 non-zero (for n');
-            // the table holds w unscaled, the n' tiles are held divided by sigma too
+            // w (hi, lo) as a 16-column operand with only column 0 non-zero (for n')
             bf16x8 bnh, bnl;
             {
                 const bf16 *W2 = reinterpret_cast<const bf16 *>(&G[5 * LP]);
-                const bf16 *ph = l16 == 0 ? W2 + 32 * js + 8 * g4 : reinterpret_cast<const bf16 *>(&zero16);
-                const bf16 *pl = l16 == 0 ? W2 + LP + 32 * js + 8 * g4 : reinterpret_cast<const bf16 *>(&zero16);
-                bnh = *reinterpret_cast<const bf16x8 *>(ph);
-                bnl = *reinterpret_cast<const bf16x8 *>(pl);
+                const uint4 wh = *reinterpret_cast<const uint4 *>(W2 + 32 * js + 8 * g4);
+                const uint4 wl = *reinterpret_cast<const uint4 *>(W2 + LP + 32 * js + 8 * g4);
+                const bool c0 = l16 == 0;
+                const uint4 zh = {c0 ? wh.x : 0u, c0 ? wh.y : 0u, c0 ? wh.z : 0u, c0 ? wh.w : 0u};
+                const uint4 zl = {c0 ? wl.x : 0u, c0 ? wl.y : 0u, c0 ? wl.z : 0u, c0 ? wl.w : 0u};
+                bnh = *reinterpret_cast<const bf16x8 *>(&zh);
+                bnl = *reinterpret_cast<const bf16x8 *>(&zl);
             }
-            const bf16 *k0 = K + 32 * js * DKP;
 #pragma unroll
-            for (int at = 0; at < NAH; ++at) {
-                if ((at & 3) == 0) __builtin_amdgcn_sched_barrier(0);
-                const int c0 = arow0 + 16 * at + 4 * tq;
-                const bf16x8 ak = cat8(tr_read(k0 + sw_off<QG>(trow0, c0)), tr_read(k0 + sw_off<QG>(trow1, c0)));
+            for (int g0 = 0; g0 < NAH; g0 += GRP) {
+                __builtin_amdgcn_sched_barrier(0);
+                bf16x8 akn[GRP];
+                if (g0 + GRP < NAH) {
 #pragma unroll
-                for (int bt = 0; bt < NBT; ++bt) Cr[at][bt] = mfma(ak, bw[bt], Cr[at][bt]);
+                    for (int u = 0; u < GRP; ++u) akn[u] = tr_frag(k0, QGc{}, arow0 + 16 * (g0 + GRP + u) + 4 * tq);
+                }
 #pragma unroll
-                for (int x = 0; x < NNW; ++x) {
-                    if (at == p + 4 * x) {
-                        f32x4 t0 = mfma(ak, bnh, f32x4{0.f, 0.f, 0.f, 0.f});
-                        t0 = mfma(ak, bnl, t0);
-                        Nr[x] += t0 * rsig;
+                for (int u = 0; u < GRP; ++u) {
+                    const int at = g0 + u;
+#pragma unroll
+                    for (int bt = 0; bt < NBT; ++bt) Cr[at][bt] = mfma(ak[u], bw[bt], Cr[at][bt]);
+#pragma unroll
+                    for (int x = 0; x < NNW; ++x) {
+                        if (at == p + 4 * x) {
+                            nacc[x] = mfma(ak[u], bnh, nacc[x]);
+                            nacc[x] = mfma(ak[u], bnl, nacc[x]);
+                        }
                     }
+                }
+                if (g0 + GRP < NAH) {
+#pragma unroll
+                    for (int u = 0; u < GRP; ++u) ak[u] = akn[u];
                 }
             }
         }
-        // publish n' (true scale) for the next chunk's q.n'
+        __builtin_amdgcn_sched_barrier(0);
+        // n' <- decay n' + K^T w (this wavefront's tiles; read again after barrier D)
         if (l16 == 0) {
 #pragma unroll
             for (int x = 0; x < NNW; ++x) {
                 const int tl = p + 4 * x;
-                if (tl < NAH) *reinterpret_cast<f32x4 *>(&nsh[arow0 + 16 * tl + 4 * g4]) = Nr[x] * sigma;
+                if (tl < NAH) {
+                    f32x4 *np = reinterpret_cast<f32x4 *>(&nsh[arow0 + 16 * tl + 4 * g4]);
+                    *np = *np * s_last + nacc[x];
+                }
             }
         }
         m_prev = m_next;
-        __builtin_amdgcn_s_waitcnt(0);  // next chunk's K and Q have landed
-        __syncthreads();                // (D)
-        if (more) copy_v(c + 1);
+        block_sync<STATE_ONLY ? 0 : VM_D>();  // (D) Q(c+1), K(c+1) landed; n' visible; V(c) free
+        if (more) copy_tile(Vs, vg, dv, VGc{}, tc + L);
     }
 
     // ---- state out
@@ -643,14 +762,10 @@ __global__ __launch_bounds__(512, 1) void mlstm_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int at = 0; at < NAH; ++at)
 #pragma unroll
-            for (int bt = 0; bt < NBT; ++bt) {
-                const int b = col0 + wc0 + 16 * bt + l16;
+            for (int bt = 0; bt < NBT; ++bt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = arow0 + 16 * at + 4 * g4 + r;
-                    if (row < dk && b < dv) Cdst[(size_t)row * dv + b] = Cr[at][bt][r] * sigma;
-                }
-            }
+                for (int r = 0; r < 4; ++r)
+                    Cdst[(size_t)(arow0 + 16 * at + 4 * g4 + r) * dv + bcol + 16 * bt] = Cr[at][bt][r] * sigma;
         if (tile == 0) {
             for (int e = tid; e < dk; e += NTH) ndst[e] = nsh[e];
             if (tid == 0) mdst[0] = m_prev;
