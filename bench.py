@@ -32,8 +32,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["xlstm_mlstm_matrix_amd/csrc/prefill_kernel.hpp", "xlstm_mlstm_matrix_amd/csrc/prefill.hip",
-                  "xlstm_mlstm_matrix_amd/csrc/step.hip"]
+METRIC = "mLSTM prefill tokens/s + %MFMA peak; decode step state GB/s + %HBM peak"
+CSRC = os.path.join("xlstm_mlstm_matrix_amd", "csrc")
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(os.path.join(ROOT, CSRC))
+                        if f.endswith((".hip", ".hpp", ".cpp")))
+CPU_THREADS_MAX = 16  # host cores that go with one GPU
 
 
 def log(msg):
@@ -128,8 +131,10 @@ def bench_prefill(torch, I, binding, name, steps, warmup, variant="auto"):
     return w, ms, flops, nbytes, (g, h, C, n, m)
 
 
-def bench_decode(torch, I, binding, warmup_passes=1):
+def bench_decode(torch, I, binding, warmup_passes=1, nsteps=None):
     w = I.workload("decode_bf16")
+    if nsteps:
+        w = I.workload("decode_bf16", T=nsteps)
     t0 = time.time()
     C0, n0, m0 = (x.cuda() for x in I.gen_decode_state(w, threads=16))
     steps = {}
@@ -167,7 +172,7 @@ def cpu_baseline(I, pairs_sample):
     import oracle
     w = I.workload("prefill_7b_bf16")
     d = I.gen_prefill(w, pairs=pairs_sample, threads=16)
-    cores = len(os.sched_getaffinity(0))
+    cores = min(len(os.sched_getaffinity(0)), CPU_THREADS_MAX)
     threads = min(cores, len(pairs_sample))
     orc = oracle.load()
     t0 = time.time()
@@ -192,7 +197,11 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-pairs", type=int, default=16)
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the 7B prefill line (profiling runs of the other workloads)")
+    ap.add_argument("--decode-steps", type=int, default=0,
+                    help="decode steps per pass (default: the workload's 1024)")
+    ap.add_argument("--cpu-pairs", type=int, default=64)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -216,13 +225,20 @@ def main():
         log("copy probe: 3 x 1 GiB device copies done")
         del src, dst
 
-    w, ms, flops, nbytes, _keep = bench_prefill(torch, I, binding, "prefill_7b_bf16", args.steps, args.warmup)
-    del _keep
-    torch.cuda.empty_cache()
+    rec = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1}
+    if args.no_prefill:
+        w = I.workload("prefill_7b_bf16")
+        ms = flops = nbytes = float("nan")
+    else:
+        w, ms, flops, nbytes, _keep = bench_prefill(torch, I, binding, "prefill_7b_bf16", args.steps,
+                                                    args.warmup)
+        del _keep
+        torch.cuda.empty_cache()
     tflops = flops / ms / 1e9
     gbs = nbytes / ms / 1e6
+    kc, nseg = binding.schedule(w.B, w.H, w.T, w.d_qk, w.d_v, w.chunk, binding.BF16)
     rec = {
-        "metric": "mLSTM prefill tokens/s (7B-layer-shaped, chunkwise, bf16 I/O, fp32 state)",
+        "metric": METRIC,
         "value": w.B * w.T / ms * 1e3,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -236,10 +252,11 @@ def main():
         "data": "synthetic (seeded, distributions of the workload spec)",
         "config": {"workload": "prefill B=8 H=8 T=4096 d_qk=256 d_v=512 chunk=64 bf16 I/O fp32 state",
                    "global_batch": w.B, "seq_len": w.T, "heads": w.H, "d_qk": w.d_qk, "d_v": w.d_v,
-                   "chunk": w.chunk, "parallelism": "single GPU"},
+                   "chunk": w.chunk, "kernel_chunk": kc, "segments": nseg,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": traffic_record("prefill_7b"),
-                     "kernel": "mlstm_chunk_kernel (fused chunkwise forward)",
+                     "kernel": "mlstm_bf16_kernel<64,256,128> (fused chunkwise forward, one launch per step)",
                      "mfma": {"achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                               "frac": tflops / PEAK_BF16_TFLOPS},
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes},
@@ -251,8 +268,11 @@ def main():
                                                   max(3, args.steps // 4), 1)
             del _keep
             torch.cuda.empty_cache()
+            kcl, nsl = binding.schedule(wl.B, wl.H, wl.T, wl.d_qk, wl.d_v, wl.chunk, binding.BF16)
             rec["long_context"] = {
-                "workload": "prefill B=1 H=8 T=65536 d_qk=256 d_v=512 chunk=128 bf16 I/O (segmented schedule)",
+                "workload": "prefill B=1 H=8 T=65536 d_qk=256 d_v=512 chunk=128 bf16 I/O fp32 state, "
+                            "final state returned",
+                "kernel_chunk": kcl, "segments": nsl,
                 "ms_per_step": msl, "tokens_per_s": wl.B * wl.T / msl * 1e3,
                 "mfma_frac": fl / msl / 1e9 / PEAK_BF16_TFLOPS, "hbm_frac": bl / msl / 1e6 / PEAK_HBM_GBS}
         except Exception as e:  # reported, not hidden
@@ -260,7 +280,7 @@ def main():
             log(f"long context: {e}")
 
     if not args.no_decode:
-        wd, msd, sb, tb = bench_decode(torch, I, binding)
+        wd, msd, sb, tb = bench_decode(torch, I, binding, nsteps=args.decode_steps or None)
         rec["decode"] = {
             "workload": "decode B=256 H=8 d_qk=256 d_v=512, 1024 in-place mlstm_step calls, bf16 I/O fp32 state",
             "ms_per_step": msd, "tokens_per_s": wd.B / msd * 1e3,
@@ -272,6 +292,7 @@ def main():
     if not args.no_cpu:
         Pn = max(1, args.cpu_pairs)
         sample = [(p // 8, p % 8) for p in range(0, 64, max(1, 64 // Pn))][:Pn]
+        log(f"cpu oracle: {len(sample)} pairs")
         rec["cpu_baseline"] = cpu_baseline(I, sample)
     print(json.dumps(rec), flush=True)
 

@@ -33,6 +33,13 @@
  *    returns MLSTM_ERR_HIP.  No exception crosses the ABI.
  *  - Supported shapes: 1 <= d_qk <= 256 and 1 <= d_v <= 512, both multiples
  *    of 16; chunk in {16, 32, 64, 128}; any T >= 1; B, H >= 1.
+ *  - chunk is the longest token block the caller allows between two state
+ *    passes.  The chunkwise form computes the same recurrence for every
+ *    block length, so where the tiles of the requested chunk do not fit in a
+ *    compute unit's 160 KB of LDS for this d_qk, d_v and dtype, the kernels
+ *    use the longest of chunk/2, chunk/4, ... (>= 16) that does (for example
+ *    64 for bfloat16 with d_qk = 256, d_v = 512 and chunk = 128);
+ *    mlstm_fwd_chunkwise_schedule reports the length used.
  */
 #ifndef MLSTM_H
 #define MLSTM_H
@@ -75,6 +82,17 @@ const char *mlstm_status_string(mlstm_status_t s);
 const char *mlstm_version(void);
 
 /*
+ * Schedule of a chunkwise call, host-only (touches no device): the chunk
+ * length the kernels use (*kernel_chunk, <= chunk) and the number of
+ * segments each sequence is split into (*segments; 1 unless the variant is
+ * the segment scan).  Same validation and errors as mlstm_fwd_chunkwise's
+ * shape checks; NULL outputs -> MLSTM_ERR_NULL.
+ */
+mlstm_status_t mlstm_fwd_chunkwise_schedule(int B, int H, int T, int d_qk, int d_v, int chunk,
+                                            mlstm_dtype_t io, mlstm_variant_t variant,
+                                            int *kernel_chunk, int *segments);
+
+/*
  * Bytes of device workspace mlstm_fwd_chunkwise needs for this shape with
  * MLSTM_VARIANT_AUTO (written to *bytes; 0 means none).  Host-only: touches
  * no device.  The segment-scan variant keeps one float32 state per segment
@@ -104,7 +122,8 @@ mlstm_status_t mlstm_fwd_chunkwise_workspace_size_variant(int B, int H, int T, i
  *  C_T, n_T, m_T  same shapes as C0, n0, m0: final stabilized state, or all
  *            three NULL when not wanted.  C_T may be exactly C0 (same pointer;
  *            likewise n_T/n0, m_T/m0): the state is then updated in place.
- *  chunk     chunk length L of the chunkwise form (16, 32, 64 or 128).
+ *  chunk     longest chunk L of the chunkwise form (16, 32, 64 or 128; see
+ *            the conventions above for the length the kernels use).
  *  workspace device buffer of at least the queried size (may be NULL when
  *            the query gives 0); its contents on entry are irrelevant.
  *

@@ -37,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s+(mlstm_\w+)", out))
@@ -78,6 +78,36 @@ def test_workspace_query(lib):
     assert ws(1, 1, 64, 64, 64, 64, 7)[0] == UNSUP          # dtype
     assert ws(1, 1, 64, 64, 64, 64, B.F32, variant=9)[0] == UNSUP
     assert B.lib().mlstm_fwd_chunkwise_workspace_size(1, 1, 64, 64, 64, 64, 0, None) == NULL
+
+
+def sched(*args, variant=0):
+    kc, ns = ctypes.c_int(-1), ctypes.c_int(-1)
+    s = B.lib().mlstm_fwd_chunkwise_schedule(*args, variant, ctypes.byref(kc), ctypes.byref(ns))
+    return s, kc.value, ns.value
+
+
+def test_schedule_query(lib):
+    # 7B-layer prefill: one workgroup per (pair, value tile) already fills the chip
+    assert sched(8, 8, 4096, 256, 512, 64, B.BF16) == (OK, 64, 1)
+    # long context, few pairs: segmented; chunk 128 tiles of d_qk 256 exceed LDS
+    s, kc, ns = sched(1, 8, 65536, 256, 512, 128, B.BF16)
+    assert (s, kc) == (OK, 64) and ns >= 2
+    assert sched(1, 8, 65536, 256, 512, 128, B.BF16, variant=1) == (OK, 64, 1)
+    assert sched(1, 1, 64, 16, 16, 16, B.F32, variant=1) == (OK, 16, 1)
+    assert sched(1, 1, 64, 24, 16, 16, B.F32)[0] == UNSUP
+    assert B.lib().mlstm_fwd_chunkwise_schedule(1, 1, 64, 16, 16, 16, 0, 0, None, None) == NULL
+
+
+@pytest.mark.parametrize("io", [0, 1])
+def test_every_documented_shape_is_supported(lib, io):
+    """d_qk, d_v multiples of 16 up to 256 / 512 and every chunk: a schedule
+    exists, with a kernel chunk that is a power of two in [16, chunk]."""
+    for dk in range(16, 257, 16):
+        for dv in (16, 48, 64, 80, 128, 176, 256, 320, 512):
+            for chunk in (16, 32, 64, 128):
+                s, kc, ns = sched(2, 2, 300, dk, dv, chunk, io)
+                assert s == OK, (dk, dv, chunk)
+                assert 16 <= kc <= chunk and kc & (kc - 1) == 0 and ns >= 1, (dk, dv, chunk, kc)
 
 
 class Fake:

@@ -173,3 +173,35 @@ def test_7b_full_size_sampled(variant):
     ref = PT.run_oracle(sub)
     flat = lambda t: t.reshape(w.B * w.H, *t.shape[2:])[idx]
     PT.compare_fwd((flat(h), flat(C), flat(n), flat(m)), ref, "bf16", f"7b full, sampled pairs {sample}")
+
+
+@pytest.fixture(scope="module")
+def long_context():
+    """Long-context workload (B=1 H=8 T=65536 d_qk=256 d_v=512, bf16) and its
+    oracle result over every pair."""
+    w = I.workload("prefill_long_bf16")
+    print("[case] long context: inputs + oracle (8 pairs x 65536 tokens)", flush=True)
+    d = I.gen_prefill(w)
+    ref = PT.run_oracle(d, threads=8)
+    return w, d, ref
+
+
+@pytest.mark.parametrize("variant", ["auto", "fused"])
+def test_long_context_full_size(long_context, variant):
+    """The long-context workload at full size, requested with chunk 128 (the
+    kernels run 64-token chunks for d_qk 256), in the launch configuration
+    the benchmark times (auto: segment scan) and as one fused pass: h of
+    every token and the final (C, n, m) of every pair against the oracle."""
+    w, d, ref = long_context
+    kc, nseg = binding.schedule(w.B, w.H, w.T, w.d_qk, w.d_v, w.chunk, binding.BF16, variant)
+    print(f"[case] long context variant={variant} kernel chunk={kc} segments={nseg}", flush=True)
+    assert kc == 64 and (nseg > 1) == (variant == "auto")
+    g = PT.cuda(d)
+    shp = lambda t: t.reshape(w.B, w.H, *t.shape[1:])
+    h, (C, n, m) = binding.fwd_chunkwise(*[shp(g[k]) for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")],
+                                         chunk=w.chunk, variant=variant)
+    torch.cuda.synchronize()
+    flat = lambda t: t.reshape(w.B * w.H, *t.shape[2:])
+    PT.compare_fwd((flat(h), flat(C), flat(n), flat(m)), ref, "bf16", f"long context {variant}")
+    m_ref = PT.m_closed_form(d["i_pre"].double().numpy(), d["f_pre"].double().numpy())
+    assert np.max(np.abs(PT.to_np(m).reshape(-1) - m_ref)) <= PT.TOL_M["bf16"]

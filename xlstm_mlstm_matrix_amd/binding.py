@@ -28,6 +28,7 @@ SIGNATURES = {
     "mlstm_version": (ctypes.c_char_p, []),
     "mlstm_fwd_chunkwise_workspace_size": (_i, [_i] * 7 + [ctypes.POINTER(_sz)]),
     "mlstm_fwd_chunkwise_workspace_size_variant": (_i, [_i] * 8 + [ctypes.POINTER(_sz)]),
+    "mlstm_fwd_chunkwise_schedule": (_i, [_i] * 8 + [ctypes.POINTER(_i)] * 2),
     "mlstm_fwd_chunkwise": (_i, [_vp] * 13 + [_i] * 7 + [_vp, _sz, _vp]),
     "mlstm_fwd_chunkwise_variant": (_i, [_vp] * 13 + [_i] * 8 + [_vp, _sz, _vp]),
     "mlstm_step": (_i, [_vp] * 13 + [_i] * 5 + [_vp]),
@@ -107,6 +108,14 @@ def workspace_size(B, H, T, d_qk, d_v, chunk, io: int, variant: str = "auto") ->
     _check(lib().mlstm_fwd_chunkwise_workspace_size_variant(
         B, H, T, d_qk, d_v, chunk, io, VARIANTS[variant], ctypes.byref(n)))
     return n.value
+
+
+def schedule(B, H, T, d_qk, d_v, chunk, io: int, variant: str = "auto"):
+    """(kernel chunk length, segments per sequence) of a chunkwise call."""
+    kc, ns = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().mlstm_fwd_chunkwise_schedule(B, H, T, d_qk, d_v, chunk, io, VARIANTS[variant],
+                                              ctypes.byref(kc), ctypes.byref(ns)))
+    return kc.value, ns.value
 
 
 def fwd_chunkwise(q, k, v, i_pre, f_pre, o_pre, C0=None, n0=None, m0=None, *, chunk: int = 64,

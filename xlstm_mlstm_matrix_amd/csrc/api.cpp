@@ -51,6 +51,7 @@ bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
 // Schedule of one chunkwise call.
 struct Plan {
     int variant;     // MLSTM_VARIANT_FUSED or MLSTM_VARIANT_SEGSCAN
+    int kchunk;      // tokens per chunk in the kernels (<= the requested chunk)
     int ntile;       // value-column tiles per sequence
     int nseg;        // segments per sequence
     int seg_len;     // tokens per segment (multiple of chunk)
@@ -68,7 +69,12 @@ mlstm_status_t make_plan(int B, int H, int T, int dk, int dv, int chunk, mlstm_d
         variant != MLSTM_VARIANT_SEGSCAN)
         return MLSTM_ERR_UNSUPPORTED;
     const int bf = io == MLSTM_BF16;
-    if (!prefill_supported(bf, dk, dv, chunk)) return MLSTM_ERR_UNSUPPORTED;
+    // the chunkwise form is exact for any chunk length: where the requested
+    // chunk's tiles do not fit in LDS, a shorter power of two is used
+    const int kc = prefill_kernel_chunk(bf, dk, dv, chunk);
+    if (kc == 0) return MLSTM_ERR_UNSUPPORTED;
+    p->kchunk = kc;
+    chunk = kc;
     size_t BH, el;
     if (!mul_ok((size_t)B, (size_t)H, &BH) || BH > (size_t)INT32_MAX / 4) return MLSTM_ERR_SHAPE;
     if (!mul_ok(BH * (size_t)T, (size_t)(dk > dv ? dk : dv), &el) || el > SIZE_MAX / 8)
@@ -125,6 +131,18 @@ mlstm_status_t mlstm_fwd_chunkwise_workspace_size_variant(int B, int H, int T, i
     mlstm_status_t st = make_plan(B, H, T, d_qk, d_v, chunk, io, variant, &p);
     if (st != MLSTM_OK) return st;
     *bytes = p.bytes();
+    return MLSTM_OK;
+}
+
+mlstm_status_t mlstm_fwd_chunkwise_schedule(int B, int H, int T, int d_qk, int d_v, int chunk,
+                                            mlstm_dtype_t io, mlstm_variant_t variant,
+                                            int *kernel_chunk, int *segments) {
+    if (!kernel_chunk || !segments) return MLSTM_ERR_NULL;
+    Plan p;
+    mlstm_status_t st = make_plan(B, H, T, d_qk, d_v, chunk, io, variant, &p);
+    if (st != MLSTM_OK) return st;
+    *kernel_chunk = p.kchunk;
+    *segments = p.nseg;
     return MLSTM_OK;
 }
 
@@ -200,17 +218,17 @@ mlstm_status_t mlstm_fwd_chunkwise_variant(const void *q, const void *k, const v
             a.n0 = ncopy;
             a.m0 = mcopy;
         }
-        if (e == hipSuccess) e = launch_fused(a, bf, chunk, 0, s);
+        if (e == hipSuccess) e = launch_fused(a, bf, p.kchunk, 0, s);
     } else {
         float *seg = ws + p.ws_state;
         const size_t rec = seg_state_floats(d_qk, d_v);
         a.seg_out = seg;                                  // local states, segments 0..nseg-2
-        e = launch_fused(a, bf, chunk, 1, s);
+        e = launch_fused(a, bf, p.kchunk, 1, s);
         if (e == hipSuccess) e = launch_seg_combine(a, seg, s);  // reads C0/n0/m0
         if (e == hipSuccess) {
             a.seg_in = seg + BH * (size_t)(p.nseg - 1) * rec;  // incoming state per segment
             a.seg_out = nullptr;
-            e = launch_fused(a, bf, chunk, 0, s);
+            e = launch_fused(a, bf, p.kchunk, 0, s);
         }
     }
     return e == hipSuccess ? MLSTM_OK : MLSTM_ERR_HIP;

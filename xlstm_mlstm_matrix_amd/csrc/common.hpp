@@ -72,5 +72,8 @@ hipError_t launch_seg_combine(const FwdArgs &a, float *ws, hipStream_t s);
 int prefill_dkp(int dk);                 // d_qk padded to the kernel's compile-time width
 int prefill_bv(int io_bf16, int dk, int dv, int chunk);  // value columns per workgroup
 bool prefill_supported(int io_bf16, int dk, int dv, int chunk);  // tiles fit in LDS
+// chunk the kernels run with when the caller allows up to `chunk` tokens per
+// chunk: the largest of chunk, chunk/2, ..., 16 whose tiles fit (0: none)
+int prefill_kernel_chunk(int io_bf16, int dk, int dv, int chunk);
 
 }  // namespace mlstm

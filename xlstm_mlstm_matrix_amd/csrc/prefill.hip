@@ -98,6 +98,12 @@ bool prefill_supported(int io_bf16, int dk, int dv, int chunk) {
     return shape_fits<float, 64>(chunk, dkp);
 }
 
+int prefill_kernel_chunk(int io_bf16, int dk, int dv, int chunk) {
+    for (int c = chunk; c >= 16; c /= 2)
+        if (prefill_supported(io_bf16, dk, dv, c)) return c;
+    return 0;
+}
+
 // bf16 kernel with LDS copies and transpose reads: chunk <= 64, d_qk in
 // {64, 128, 256} (no padding) and d_v a multiple of the column tile
 bool bf16_fast_path(int chunk, int dk, int dv) {
