@@ -1,0 +1,560 @@
+// prefill_ws.hpp -- chunkwise mLSTM forward for bf16 I/O on gfx950 with the
+// wavefronts of a workgroup split by role.
+//
+// Mathematics as in prefill_kernel.hpp (the chunkwise form of the xLSTM
+// note's mLSTM recurrence, "mLSTM (matrix LSTM)" section, with the
+// stabilizer of its "sLSTM" section): per chunk of L = 64 tokens, with
+// b = in-chunk cumsum of f~, u_j = i~_j - b_j, r_i = max(m, max_{j<=i} u_j),
+//   h_i = sigmoid(o~_i) (sum_j P_ij v_j + e^{m-r_i} C'^T q_i)
+//                       / max(|sum_j P_ij + e^{m-r_i} n'.q_i|, e^{-(b_i+r_i)}),
+//   P_ij = (q_i.k_j) e^{u_j - r_i} (j <= i),
+//   C' <- e^{m-r_L} C' + sum_j e^{u_j-r_L} k_j v_j^T, n' likewise, m <- b_L + r_L.
+//
+// Schedule.  One workgroup owns one (pair, segment, block of 128 value
+// columns) and walks its chunks in order.  Its 8 wavefronts sit two per SIMD,
+// one of each role, so the matrix cores of a SIMD run one role's MFMAs while
+// its vector ALU runs the other role's elementwise work:
+//  * state wavefronts (0..3): wavefront s holds all d_qk rows of C' for value
+//    columns [32 s, 32 s + 32) in registers (MFMA accumulator layout, float32,
+//    for the whole sequence).  Per chunk they compute the inter-chunk
+//    read-out C'^T Q^T (C' split into a bf16 high part and remainder, two
+//    MFMAs) and hand it to the intra wavefronts through LDS, then update
+//    C' and n' with MFMAs.  They issue every global->LDS copy of the Q, K, V
+//    tiles;
+//  * intra wavefronts (4..7): wavefront 4 + t owns token tile t (16 tokens)
+//    for all 128 columns: its causal S tiles (MFMA), q.n' (MFMA with n' as a
+//    broadcast operand), P in registers (the S accumulator layout is, up to
+//    a permutation of the MFMA k index that the V^T fragment follows too, the
+//    B operand of V^T P^T), V^T P^T, the normaliser, the output gate and the
+//    bf16 h stores.  They issue only plain loads (o~, gates) and stores.
+// Two phases per chunk, separated by workgroup barriers:
+//   phase 1: state: copies V(c), K(c+1); read-out of chunk c -> LDS
+//            intra: S, q.n', P of chunk c; one of them prepares the gate
+//                   table of chunk c+1
+//   phase 2: state: copy Q(c+1); C', n' update with chunk c
+//            intra: V^T P^T on top of the read-out, h of chunk c
+// Only the state wavefronts wait for their copies at the barriers, so the
+// compiler never has to wait for copies and plain loads together.
+#pragma once
+
+#include "prefill_bf16.hpp"
+
+namespace mlstm {
+
+template <int DKP_>
+struct WsCfg {
+    static constexpr int L = 64, DKP = DKP_, BV = 128;
+    static constexpr int NW = 8, NTH = 512, NSW = 4;  // wavefronts; state wavefronts
+    static constexpr int NT = L / 16;                 // token tiles (one per intra wavefront)
+    static constexpr int NAT = DKP / 16;              // 16-row tiles of C'
+    static constexpr int NKS = DKP / 32;              // MFMA k-steps over d_qk
+    static constexpr int NCT = BV / 16;               // 16-column tiles of the value block
+    static constexpr int QG = DKP / 8, VG = BV / 8;   // 16-byte granules per row
+    static constexpr int GTF = 6 * L + 8;             // gate table floats (as Bf16Cfg)
+    static constexpr size_t LDS_BYTES = 2 * (3 * (size_t)L * DKP + (size_t)L * BV) +
+                                        16 * (size_t)NT * NCT * 64 + 4 * (2 * (size_t)GTF + DKP) +
+                                        2 * 2 * (size_t)DKP;
+    static_assert(NT == NW - NSW, "one token tile per intra wavefront");
+    static_assert(NAT % 4 == 0, "n' tiles spread over the state wavefronts");
+    static_assert(QG >= 8, "swizzle needs 8 granules per row");
+};
+
+// Workgroup barrier; state wavefronts first wait for all their copies, the
+// intra wavefronts only for their LDS accesses.
+__device__ __forceinline__ void role_sync(bool is_state) {
+    if (is_state)
+        __builtin_amdgcn_s_waitcnt((0x0) | (0x7 << 4) | (0x0 << 8) | (0x0 << 14));  // vmcnt 0, lgkmcnt 0
+    else
+        __builtin_amdgcn_s_waitcnt((0xf) | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));  // lgkmcnt 0
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int DKP>
+__global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
+    using Cfg = WsCfg<DKP>;
+    constexpr int L = Cfg::L, LP = L, BV = Cfg::BV, NSW = Cfg::NSW, NT = Cfg::NT;
+    constexpr int NAT = Cfg::NAT, NKS = Cfg::NKS, NCT = Cfg::NCT, QG = Cfg::QG, VG = Cfg::VG;
+    constexpr int GTF = Cfg::GTF;
+    constexpr float kRenorm = 8.6736174e-19f;  // 2^-60: renormalise the lazy state scale below this
+
+    __shared__ __attribute__((aligned(16))) bf16 Qs[L * DKP];
+    __shared__ __attribute__((aligned(16))) bf16 Ks[2][L * DKP];  // K of even / odd chunks
+    __shared__ __attribute__((aligned(16))) bf16 Vs[L * BV];
+    __shared__ __attribute__((aligned(16))) f32x4 Xch[NT][NCT][64];  // scaled read-out, accumulator layout
+    // gate tables (double buffered): u, r, s, floor, w [L] floats, w as bf16
+    // high/low pairs [L], then scalars (m after, decay, sum f~)
+    __shared__ __attribute__((aligned(16))) float gt[2][GTF];
+    __shared__ __attribute__((aligned(16))) float nsh[DKP];     // n' (true scale)
+    __shared__ __attribute__((aligned(16))) bf16 nhl[2][DKP];   // n' as bf16 high part, remainder
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool is_state = wave < NSW;
+    const int s = wave & 3;  // state: column group; intra: token tile
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int te = l16 >> 2, tq = l16 & 3;  // transpose-read source row / column quad
+
+    const int nwg = gridDim.x;
+    int logical = blockIdx.x;
+    if ((nwg & 7) == 0) logical = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int tile = logical % a.ntile;
+    const int rest = logical / a.ntile;
+    const int seg = rest % a.nseg;
+    const int bh = rest / a.nseg;
+
+    const int dk = a.dk, dv = a.dv, T = a.T;  // here dk == DKP and dv is a multiple of BV
+    const int t_begin = seg * a.seg_len;
+    const int t_end = min(t_begin + a.seg_len, T);
+    const int nchunks = (t_end - t_begin + L - 1) / L;
+    const int col0 = tile * BV;
+
+    const bf16 *qg = static_cast<const bf16 *>(a.q) + (size_t)bh * T * DKP;
+    const bf16 *kg = static_cast<const bf16 *>(a.k) + (size_t)bh * T * DKP;
+    const bf16 *vg = static_cast<const bf16 *>(a.v) + (size_t)bh * T * dv + col0;
+    const bf16 *og = static_cast<const bf16 *>(a.o) + (size_t)bh * T * dv + col0;
+    bf16 *hg = static_cast<bf16 *>(a.h) + (size_t)bh * T * dv + col0;
+    const float *igg = a.ig + (size_t)bh * T;
+    const float *fgg = a.fg + (size_t)bh * T;
+
+    for (int e = tid; e < 2 * GTF; e += Cfg::NTH) (&gt[0][0])[e] = 0.0f;
+
+    // ---- initial state
+    const size_t rec = seg_state_floats(dk, dv);
+    const float *Cs = nullptr, *ns = nullptr;
+    float m_prev = 0.0f;
+    if (a.seg_in) {
+        const float *r = a.seg_in + ((size_t)bh * a.nseg + seg) * rec;
+        Cs = r;
+        ns = r + (size_t)dk * dv;
+        m_prev = r[(size_t)dk * dv + dk];
+    } else if (a.C0) {
+        Cs = a.C0 + (size_t)bh * dk * dv;
+        ns = a.n0 + (size_t)bh * dk;
+        m_prev = a.m0[bh];
+    }
+    const int scol = col0 + 32 * s + l16;  // state column of this lane (tile bt adds 16 bt)
+    f32x4 Cr[NAT][2];
+#pragma unroll
+    for (int at = 0; at < NAT; ++at)
+#pragma unroll
+        for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Cr[at][bt][r] = (is_state && Cs) ? Cs[(size_t)(16 * at + 4 * g4 + r) * dv + scol + 16 * bt] : 0.0f;
+    for (int e = tid; e < DKP; e += Cfg::NTH) {
+        const float x = ns ? ns[e] : 0.0f;
+        nsh[e] = x;
+        const bf16 hi = (bf16)x;
+        nhl[0][e] = hi;
+        nhl[1][e] = (bf16)(x - (float)hi);
+    }
+    float sigma = 1.0f;  // C' is held divided by sigma (state wavefronts)
+
+    // ---- global -> LDS copies by the state wavefronts.  Physical granule g of
+    // a tile is (row, gl) with gl = (g % gpr) ^ swz(row); instruction k of
+    // wavefront s fills granules [(k NSW + s) 64, +64), rows k RPI + const with
+    // RPI a multiple of 8, so each lane's swizzle is the same for every k.
+    // Rows past the segment end are clamped to its last row (finite data;
+    // their gates zero them out).
+    auto copy_tile = [&](bf16 *dst, const bf16 *src, int ld, auto gpr_c, int tc) {
+        constexpr int GPR = decltype(gpr_c)::value;
+        constexpr int TOTAL = L * GPR;
+        constexpr int NI = TOTAL / (NSW * 64);
+        constexpr int RPI = NSW * 64 / GPR;
+        static_assert(TOTAL % (NSW * 64) == 0 && RPI % 8 == 0, "copy shape");
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int pgr = s * 64 + ln;
+        const int row = pgr / GPR;
+        const int gl = (pgr % GPR) ^ swz8(row);
+        if (tc + L <= t_end) {
+            const int voff = row * ld * 2 + gl * 16;
+#pragma unroll
+            for (int k = 0; k < NI; ++k) {
+                const char *base = reinterpret_cast<const char *>(src + (size_t)(tc + k * RPI) * ld);
+                __builtin_amdgcn_global_load_lds((const void *)(base + voff),
+                                                 (lds_void *)(dst + (k * NSW + s) * 64 * 8), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NI; ++k) {
+                const int t = min(tc + k * RPI + row, t_end - 1);
+                __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)t * ld + gl * 8),
+                                                 (lds_void *)(dst + (k * NSW + s) * 64 * 8), 16, 0, 0);
+            }
+        }
+    };
+    using QGc = std::integral_constant<int, QG>;
+    using VGc = std::integral_constant<int, VG>;
+
+    // ---- gates (first intra wavefront; one token per lane)
+    constexpr int GW = NSW;
+    float gf = 0.0f, gi = -INFINITY;
+    bool gok = false;
+    auto load_gates = [&](int c) {
+        const int t = t_begin + c * L + lane;
+        gok = lane < L && t < t_end;
+        const int tcl = min(t, t_end - 1);
+        gf = fgg[tcl];
+        gi = igg[tcl];
+    };
+    auto gate_prep = [&](float m_before, float *G) {
+        const float b = wave_scan_add(gok ? gf : 0.0f);
+        const float u = (gok ? gi : -INFINITY) - b;
+        const float pm = wave_scan_max(u);
+        const float r = fmaxf(m_before, pm);
+        const float r_last = __shfl(r, L - 1, 64);
+        const float b_last = __shfl(b, L - 1, 64);
+        const float w = exp_e(u - r_last);
+        G[lane] = u;
+        G[LP + lane] = r;
+        G[2 * LP + lane] = exp_e(m_before - r);
+        G[3 * LP + lane] = exp_e(-(b + r));
+        G[4 * LP + lane] = w;
+        const bf16 whi = (bf16)w;
+        const bf16 wlo = (bf16)(w - (float)whi);
+        bf16 *W2 = reinterpret_cast<bf16 *>(&G[5 * LP]);
+        W2[lane] = whi;
+        W2[LP + lane] = wlo;
+        if (lane == 0) {
+            G[6 * LP + 0] = b_last + r_last;           // stabilizer after the chunk
+            G[6 * LP + 1] = exp_e(m_before - r_last);  // decay of the carried state
+            G[6 * LP + 2] = b_last;                    // sum of the chunk's log forget gates
+        }
+    };
+
+    // ---- per-lane LDS offsets
+    const int s16 = swz8(l16);
+    // Q / K fragment for k-step ks of rows 16 t + l16: columns 32 ks + 4 g4 (+16)
+    int qkoff[2][2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            qkoff[par][hh] = l16 * DKP + (((((par << 2) | ((g4 >> 1) + 2 * hh)) ^ s16)) << 3) + 4 * (g4 & 1);
+    auto qk_frag = [&](const bf16 *tilebase, int ks) -> bf16x8 {  // tilebase: row 16 t of the tile
+        const bf16 *b = tilebase + ((ks >> 1) << 6);
+        return cat8(ld4(b + qkoff[ks & 1][0]), ld4(b + qkoff[ks & 1][1]));
+    };
+    // Transpose reads of a 16-column block cb = 4 hi + lo of a swizzled tile:
+    // the swizzle touches the low three granule bits only, so the per-lane part
+    // of the offset depends on (row, lo) and hi adds 64 elements (8 granules).
+    auto tr_off = [&](auto gpr_c, int row, int lo) -> int {
+        constexpr int GPR = decltype(gpr_c)::value;
+        return row * GPR * 8 + (((2 * lo + (tq >> 1)) ^ swz8(row)) << 3) + 4 * (tq & 1);
+    };
+    // k index in the S accumulator order (V^T of V^T P^T): rows 32 js + 4 g4 + te (+16)
+    const int prow0 = 4 * g4 + te, prow1 = prow0 + 16;
+
+    if (nchunks > 0) block_sync<0>();  // gate tables zeroed, n' written
+
+    // Each role runs its own chunk loop; both execute the same sequence of
+    // barriers (one after the prologue, two per chunk).
+    if (is_state) {
+        // ========================= state wavefronts =========================
+        if (nchunks > 0) {
+            copy_tile(Qs, qg, DKP, QGc{}, t_begin);
+            copy_tile(Ks[0], kg, DKP, QGc{}, t_begin);
+        }
+        role_sync(true);
+        for (int c = 0; c < nchunks; ++c) {
+            const float *G = gt[c & 1];
+            const int tc = t_begin + c * L;
+            const float m_next = G[6 * LP + 0], s_last = G[6 * LP + 1];
+            const bool more = c + 1 < nchunks;
+
+            // ---- phase 1: copies V(c), K(c+1); read-out O^T = C'^T Q^T
+            copy_tile(Vs, vg, dv, VGc{}, tc);
+            if (more) copy_tile(Ks[(c + 1) & 1], kg, DKP, QGc{}, tc + L);
+            {
+                f32x4 Ot[2][NT];
+#pragma unroll
+                for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) Ot[bt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                bf16x8 bq = qk_frag(Qs, 0);
+#pragma unroll
+                for (int kk = 0; kk < NKS; ++kk) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    bf16x8 ach[2], acl[2];
+#pragma unroll
+                    for (int bt = 0; bt < 2; ++bt) {
+                        const float x[8] = {Cr[2 * kk][bt][0],     Cr[2 * kk][bt][1],     Cr[2 * kk][bt][2],
+                                            Cr[2 * kk][bt][3],     Cr[2 * kk + 1][bt][0], Cr[2 * kk + 1][bt][1],
+                                            Cr[2 * kk + 1][bt][2], Cr[2 * kk + 1][bt][3]};
+                        split8(x, ach[bt], acl[bt]);
+                    }
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        bf16x8 bqn;
+                        const bool nxt = t + 1 < NT || kk + 1 < NKS;
+                        if (nxt) bqn = qk_frag(Qs + 16 * ((t + 1) % NT) * DKP, kk + (t + 1) / NT);
+#pragma unroll
+                        for (int bt = 0; bt < 2; ++bt) Ot[bt][t] = mfma(ach[bt], bq, Ot[bt][t]);
+#pragma unroll
+                        for (int bt = 0; bt < 2; ++bt) Ot[bt][t] = mfma(acl[bt], bq, Ot[bt][t]);
+                        if (nxt) bq = bqn;
+                    }
+                }
+                // scale by e^{m - r_i} and the held state's sigma, hand over
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const float si = G[2 * LP + 16 * t + l16] * sigma;
+#pragma unroll
+                    for (int bt = 0; bt < 2; ++bt) Xch[t][2 * s + bt][lane] = Ot[bt][t] * si;
+                }
+            }
+            role_sync(true);  // (X) read-out in LDS; V(c), K(c+1) landed; Q(c) free
+
+            // ---- phase 2: copy Q(c+1); C'/sigma' += K^T ((w/sigma') (x) V),
+            // sigma' = sigma * decay; n' likewise (true scale)
+            if (more) copy_tile(Qs, qg, DKP, QGc{}, tc + L);
+            sigma *= s_last;
+            if (sigma < kRenorm) {  // uniform: fold sigma back into the held state
+#pragma unroll
+                for (int at = 0; at < NAT; ++at)
+#pragma unroll
+                    for (int bt = 0; bt < 2; ++bt) Cr[at][bt] *= sigma;
+                sigma = 1.0f;
+            }
+            const float rsig = __builtin_amdgcn_rcpf(sigma);
+            const bf16 *K = Ks[c & 1];
+            // K^T fragment offsets by (row tile & 3, read), recomputed here from
+            // an opaque copy of the lane index so they are not held across the loop
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int lte = (ln & 15) >> 2, ltq = ln & 3, lg4 = ln >> 4;
+            auto tr_off2 = [&](auto gpr_c, int row, int lo) -> int {
+                constexpr int GPR = decltype(gpr_c)::value;
+                return row * GPR * 8 + (((2 * lo + (ltq >> 1)) ^ swz8(row)) << 3) + 4 * (ltq & 1);
+            };
+            const int krow0 = 8 * lg4 + lte, krow1 = krow0 + 4;
+            int kto[4][2];
+#pragma unroll
+            for (int lo = 0; lo < 4; ++lo) {
+                kto[lo][0] = tr_off2(QGc{}, krow0, lo);
+                kto[lo][1] = tr_off2(QGc{}, krow1, lo);
+            }
+            auto kt_frag = [&](const bf16 *rowblock, int at) -> bf16x8 {
+                const bf16 *b = rowblock + 64 * (at >> 2);
+                return cat8(tr_read(b + kto[at & 3][0]), tr_read(b + kto[at & 3][1]));
+            };
+            f32x4 nacc[NAT / 4];
+#pragma unroll
+            for (int x = 0; x < NAT / 4; ++x) nacc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int js = 0; js < L / 32; ++js) {
+                const bf16 *k0 = K + 32 * js * DKP;
+                float w8[8];
+                {
+                    const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&G[4 * LP + 32 * js + 8 * g4]);
+                    const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&G[4 * LP + 32 * js + 8 * g4 + 4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        w8[e] = w0[e] * rsig;
+                        w8[e + 4] = w1[e] * rsig;
+                    }
+                }
+                bf16x8 bw[2];
+#pragma unroll
+                for (int bt = 0; bt < 2; ++bt) {
+                    const int cb = 2 * s + bt;
+                    const bf16 *vb = Vs + 32 * js * BV + 64 * (cb >> 2);
+                    const bf16x8 vv = cat8(tr_read(vb + tr_off2(VGc{}, krow0, cb & 3)),
+                                           tr_read(vb + tr_off2(VGc{}, krow1, cb & 3)));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bw[bt][e] = (bf16)((float)vv[e] * w8[e]);
+                }
+                // w (hi, lo) in every column of the operand: every lane gets K^T w
+                const bf16 *W2 = reinterpret_cast<const bf16 *>(&G[5 * LP]);
+                const bf16x8 bnh = *reinterpret_cast<const bf16x8 *>(W2 + 32 * js + 8 * g4);
+                const bf16x8 bnl = *reinterpret_cast<const bf16x8 *>(W2 + LP + 32 * js + 8 * g4);
+                constexpr int GRP = 2;
+                bf16x8 ak[GRP];
+#pragma unroll
+                for (int u = 0; u < GRP; ++u) ak[u] = kt_frag(k0, u);
+#pragma unroll
+                for (int g0 = 0; g0 < NAT; g0 += GRP) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    bf16x8 akn[GRP];
+                    if (g0 + GRP < NAT) {
+#pragma unroll
+                        for (int u = 0; u < GRP; ++u) akn[u] = kt_frag(k0, g0 + GRP + u);
+                    }
+#pragma unroll
+                    for (int u = 0; u < GRP; ++u) {
+                        const int at = g0 + u;
+#pragma unroll
+                        for (int bt = 0; bt < 2; ++bt) Cr[at][bt] = mfma(ak[u], bw[bt], Cr[at][bt]);
+                        if ((at & 3) == s) {
+                            nacc[at >> 2] = mfma(ak[u], bnh, nacc[at >> 2]);
+                            nacc[at >> 2] = mfma(ak[u], bnl, nacc[at >> 2]);
+                        }
+                    }
+                    if (g0 + GRP < NAT) {
+#pragma unroll
+                        for (int u = 0; u < GRP; ++u) ak[u] = akn[u];
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // n' <- decay n' + K^T w for row tiles s + 4x (read after barrier Y)
+            if (l16 == 0) {
+#pragma unroll
+                for (int x = 0; x < NAT / 4; ++x) {
+                    const int r0 = 16 * (s + 4 * x) + 4 * g4;
+                    f32x4 *np = reinterpret_cast<f32x4 *>(&nsh[r0]);
+                    const f32x4 nn = *np * s_last + nacc[x];
+                    *np = nn;
+                    bf16x4 hi, lo;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        hi[r] = (bf16)nn[r];
+                        lo[r] = (bf16)(nn[r] - (float)hi[r]);
+                    }
+                    *reinterpret_cast<bf16x4 *>(&nhl[0][r0]) = hi;
+                    *reinterpret_cast<bf16x4 *>(&nhl[1][r0]) = lo;
+                }
+            }
+            m_prev = m_next;
+            role_sync(true);  // (Y) Q(c+1), K(c+1) landed; n' visible; V(c), Xch free
+        }
+
+        // ---- state out (n' and m from wavefront 0 of column block 0)
+        if (a.CT && seg == a.nseg - 1) {
+            float *Cdst = a.CT + (size_t)bh * dk * dv;
+#pragma unroll
+            for (int at = 0; at < NAT; ++at)
+#pragma unroll
+                for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Cdst[(size_t)(16 * at + 4 * g4 + r) * dv + scol + 16 * bt] = Cr[at][bt][r] * sigma;
+            if (tile == 0 && wave == 0) {
+                float *ndst = a.nT + (size_t)bh * dk;
+                for (int e = lane; e < dk; e += 64) ndst[e] = nsh[e];
+                if (lane == 0) a.mT[bh] = m_prev;
+            }
+        }
+    } else {
+        // ========================= intra wavefronts =========================
+        if (nchunks > 0 && wave == GW) {
+            load_gates(0);
+            gate_prep(m_prev, gt[0]);
+        }
+        role_sync(false);
+        const int it = s;                // token tile of this wavefront
+        const int irow = 16 * it + l16;  // token of this lane within the chunk (accumulator column)
+        for (int c = 0; c < nchunks; ++c) {
+            const float *G = gt[c & 1];
+            float *Gnext = gt[(c + 1) & 1];
+            const int tc = t_begin + c * L;
+            const float m_next = G[6 * LP + 0];
+            const bool more = c + 1 < nchunks;
+
+            // ---- phase 1: S, q.n', P of this token tile; next gate table
+            uint2 orw[NCT];  // output-gate inputs (used in phase 2)
+            {
+                const int t = min(tc + irow, t_end - 1);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+                    orw[ct] = *reinterpret_cast<const uint2 *>(og + (size_t)t * dv + 16 * ct + 4 * g4);
+            }
+            if (more && wave == GW) load_gates(c + 1);
+            // S^T tiles (jt, it) for jt <= it and q.n', k-step outermost so
+            // each Q fragment serves all of them
+            f32x4 St[NT];
+#pragma unroll
+            for (int jt = 0; jt < NT; ++jt) St[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 qd = {0.f, 0.f, 0.f, 0.f};
+            const bf16 *qrow = Qs + 16 * it * DKP;
+            const bf16 *K = Ks[c & 1];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const bf16x8 fq = qk_frag(qrow, ks);
+                // n' in the same k order, identical in every row of the operand
+                const int nc = 32 * ks + 4 * g4;
+                const bf16x8 nh = cat8(ld4(&nhl[0][nc]), ld4(&nhl[0][nc + 16]));
+                const bf16x8 nl = cat8(ld4(&nhl[1][nc]), ld4(&nhl[1][nc + 16]));
+#pragma unroll
+                for (int jt = 0; jt < NT; ++jt) {
+                    if (jt <= it) St[jt] = mfma(qk_frag(K + 16 * jt * DKP, ks), fq, St[jt]);
+                }
+                qd = mfma(nh, fq, qd);
+                qd = mfma(nl, fq, qd);
+            }
+            const float qn = qd[0];
+            // P = S (x) e^{u_j - r_i} (j <= i), bf16, in the k order of the V^T fragments
+            bf16x4 Pb[NT];
+            float rowsum = 0.0f;
+            const float ri = G[LP + irow];
+#pragma unroll
+            for (int jt = 0; jt < NT; ++jt) {
+                if (jt <= it) {
+                    const f32x4 u4 = *reinterpret_cast<const f32x4 *>(&G[16 * jt + 4 * g4]);
+                    float pv[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 16 * jt + 4 * g4 + r;
+                        pv[r] = (j <= irow) ? St[jt][r] * exp_e(u4[r] - ri) : 0.0f;
+                    }
+                    rowsum += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+                    Pb[jt] = bf16x4{(bf16)pv[0], (bf16)pv[1], (bf16)pv[2], (bf16)pv[3]};
+                } else {
+                    Pb[jt] = bf16x4{(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+                }
+            }
+            rowsum += __shfl_xor(rowsum, 16, 64);
+            rowsum += __shfl_xor(rowsum, 32, 64);
+            if (more && wave == GW) gate_prep(m_next, Gnext);
+            role_sync(false);  // (X)
+
+            // ---- phase 2: O^T of this token tile = scaled read-out + V^T P^T; h
+            int vpo[4][2];  // V^T fragment offsets by (column tile & 3, read)
+#pragma unroll
+            for (int lo = 0; lo < 4; ++lo) {
+                vpo[lo][0] = tr_off(VGc{}, prow0, lo);
+                vpo[lo][1] = tr_off(VGc{}, prow1, lo);
+            }
+            f32x4 acc[NCT];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) acc[ct] = Xch[it][ct][lane];
+#pragma unroll
+            for (int js = 0; js < L / 32; ++js) {
+                if (2 * js <= it) {
+                    const bf16x8 bp = cat8(Pb[2 * js], Pb[2 * js + 1]);
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        const bf16 *vb = Vs + 32 * js * BV + 64 * (ct >> 2);
+                        const bf16x8 av = cat8(tr_read(vb + vpo[ct & 3][0]), tr_read(vb + vpo[ct & 3][1]));
+                        acc[ct] = mfma(av, bp, acc[ct]);
+                    }
+                }
+            }
+            const float den = G[2 * LP + irow] * qn + rowsum;
+            const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), G[3 * LP + irow]));
+            const int t = tc + irow;
+            if (t < t_end) {
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const uint2 o4 = orw[ct];
+                    float y[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t wd = e < 2 ? o4.x : o4.y;
+                        const float ox = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
+                        y[e] = acc[ct][e] * inv * __builtin_amdgcn_rcpf(1.0f + exp_e(-ox));
+                    }
+                    const bf16x4 hv = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
+                    *reinterpret_cast<bf16x4 *>(hg + (size_t)t * dv + 16 * ct + 4 * g4) = hv;
+                }
+            }
+            role_sync(false);  // (Y)
+        }
+    }
+}
+
+}  // namespace mlstm
