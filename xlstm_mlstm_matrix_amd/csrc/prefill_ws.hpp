@@ -18,23 +18,25 @@
 //    columns [32 s, 32 s + 32) in registers (MFMA accumulator layout, float32,
 //    for the whole sequence).  Per chunk they compute the inter-chunk
 //    read-out C'^T Q^T (C' split into a bf16 high part and remainder, two
-//    MFMAs) and hand it to the intra wavefronts through LDS, then update
-//    C' and n' with MFMAs.  They issue every global->LDS copy of the Q, K, V
-//    tiles;
+//    MFMAs) and q.n' (MFMA with n' as a broadcast operand, token tile s) and
+//    hand them to the intra wavefronts through LDS, then update C' and n'
+//    with MFMAs.  They issue no memory instructions (a wavefront whose
+//    vector-memory queue is full stalls at issue);
 //  * intra wavefronts (4..7): wavefront 4 + t owns token tile t (16 tokens)
-//    for all 128 columns: its causal S tiles (MFMA), q.n' (MFMA with n' as a
-//    broadcast operand), P in registers (the S accumulator layout is, up to
-//    a permutation of the MFMA k index that the V^T fragment follows too, the
-//    B operand of V^T P^T), V^T P^T, the normaliser, the output gate and the
-//    bf16 h stores.  They issue only plain loads (o~, gates) and stores.
+//    for all 128 columns: its causal S tiles (MFMA), P in registers (the S
+//    accumulator layout is, up to a permutation of the MFMA k index that the
+//    V^T fragment follows too, the B operand of V^T P^T), V^T P^T, the
+//    normaliser, the output gate and the bf16 h stores.  They copy the Q, K
+//    and V tiles.
 // Two phases per chunk, separated by workgroup barriers:
-//   phase 1: state: copies V(c), K(c+1); read-out of chunk c -> LDS
-//            intra: S, q.n', P of chunk c; one of them prepares the gate
-//                   table of chunk c+1
-//   phase 2: state: copy Q(c+1); C', n' update with chunk c
-//            intra: V^T P^T on top of the read-out, h of chunk c
-// Only the state wavefronts wait for their copies at the barriers, so the
-// compiler never has to wait for copies and plain loads together.
+//   phase 1: state: read-out and q.n' of chunk c -> LDS
+//            intra: copy V(c), load o~, gates; S, P of chunk c; one of them
+//                   prepares the gate table of chunk c+1; copy K(c+1)
+//   phase 2: state: C', n' update with chunk c
+//            intra: copy Q(c+1); V^T P^T on top of the read-out, h of chunk c
+// No wavefront has a copy in flight when it uses a plain load (the compiler
+// counts loads and copies together and would wait for both); the barriers
+// wait for the copies with exact counts.
 #pragma once
 
 #include "prefill_bf16.hpp"
@@ -59,13 +61,23 @@ struct WsCfg {
     static_assert(QG >= 8, "swizzle needs 8 granules per row");
 };
 
-// Workgroup barrier; state wavefronts first wait for all their copies, the
-// intra wavefronts only for their LDS accesses.
-__device__ __forceinline__ void role_sync(bool is_state) {
-    if (is_state)
-        __builtin_amdgcn_s_waitcnt((0x0) | (0x7 << 4) | (0x0 << 8) | (0x0 << 14));  // vmcnt 0, lgkmcnt 0
-    else
-        __builtin_amdgcn_s_waitcnt((0xf) | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));  // lgkmcnt 0
+// Row swizzle of the 16-byte granules of the Q and K tiles (rows with 16 or
+// more granules): a bijection of row mod 16, so the 16 rows an MFMA fragment
+// read touches at one logical granule land in 16 different granules; the
+// transpose reads of K (4 consecutive rows, and the same rows + 8) stay
+// spread as well.
+__device__ __forceinline__ int swz16(int r) {
+    const int f = (r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
+    return (f << 1) | ((r >> 3) & 1);
+}
+
+// Workgroup barrier after this wavefront's LDS accesses have completed and at
+// most VM of its vector-memory operations are outstanding (they complete in
+// issue order).  State wavefronts issue none and pass VM = 63 (no wait).
+template <int VM>
+__device__ __forceinline__ void role_sync() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 0xf) | (0x7 << 4) | (0x0 << 8) | ((VM >> 4) << 14));
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -88,6 +100,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) float gt[2][GTF];
     __shared__ __attribute__((aligned(16))) float nsh[DKP];     // n' (true scale)
     __shared__ __attribute__((aligned(16))) bf16 nhl[2][DKP];   // n' as bf16 high part, remainder
+    __shared__ float qn_sh[L];                                  // q.n' of the chunk's tokens
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -153,40 +166,39 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     }
     float sigma = 1.0f;  // C' is held divided by sigma (state wavefronts)
 
-    // ---- global -> LDS copies by the state wavefronts.  Physical granule g of
-    // a tile is (row, gl) with gl = (g % gpr) ^ swz(row); instruction k of
-    // wavefront s fills granules [(k NSW + s) 64, +64), rows k RPI + const with
-    // RPI a multiple of 8, so each lane's swizzle is the same for every k.
-    // Rows past the segment end are clamped to its last row (finite data;
-    // their gates zero them out).
-    auto copy_tile = [&](bf16 *dst, const bf16 *src, int ld, auto gpr_c, int tc) {
+    // Q and K tiles are swizzled with swz16 (swz8 below 16 granules per row),
+    // V tiles with swz8.
+    auto qswz = [](int row) -> int {
+        if constexpr (QG >= 16)
+            return swz16(row);
+        else
+            return swz8(row);
+    };
+    // ---- global -> LDS copies by the intra wavefronts.  Physical granule g
+    // of a tile is (row, p) with p = g % gpr holding logical granule
+    // p ^ swz(row); instruction k of wavefront s fills granules
+    // [(k NSW + s) 64, +64), rows k RPI + const.  Rows past the segment end
+    // are clamped to its last row (finite data; their gates zero them out).
+    // copy_part issues instruction k of a tile copy, copy_tile all of them.
+    auto copy_part = [&](bf16 *dst, const bf16 *src, int ld, auto gpr_c, int tc, int k) {
         constexpr int GPR = decltype(gpr_c)::value;
-        constexpr int TOTAL = L * GPR;
-        constexpr int NI = TOTAL / (NSW * 64);
         constexpr int RPI = NSW * 64 / GPR;
-        static_assert(TOTAL % (NSW * 64) == 0 && RPI % 8 == 0, "copy shape");
+        static_assert((L * GPR) % (NSW * 64) == 0 && RPI % 8 == 0, "copy shape");
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int pgr = s * 64 + ln;
-        const int row = pgr / GPR;
-        const int gl = (pgr % GPR) ^ swz8(row);
-        if (tc + L <= t_end) {
-            const int voff = row * ld * 2 + gl * 16;
-#pragma unroll
-            for (int k = 0; k < NI; ++k) {
-                const char *base = reinterpret_cast<const char *>(src + (size_t)(tc + k * RPI) * ld);
-                __builtin_amdgcn_global_load_lds((const void *)(base + voff),
-                                                 (lds_void *)(dst + (k * NSW + s) * 64 * 8), 16, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < NI; ++k) {
-                const int t = min(tc + k * RPI + row, t_end - 1);
-                __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)t * ld + gl * 8),
-                                                 (lds_void *)(dst + (k * NSW + s) * 64 * 8), 16, 0, 0);
-            }
-        }
+        const int row = k * RPI + pgr / GPR;
+        const int gl = (pgr % GPR) ^ (GPR == QG ? qswz(row) : swz8(row));
+        const int t = min(tc + row, t_end - 1);
+        __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)t * ld + gl * 8),
+                                         (lds_void *)(dst + (k * NSW + s) * 64 * 8), 16, 0, 0);
     };
+    auto copy_tile = [&](bf16 *dst, const bf16 *src, int ld, auto gpr_c, int tc) {
+        constexpr int NI = L * decltype(gpr_c)::value / (NSW * 64);
+#pragma unroll
+        for (int k = 0; k < NI; ++k) copy_part(dst, src, ld, gpr_c, tc, k);
+    };
+    static_assert(L * QG / (NSW * 64) == NKS, "one K or Q copy instruction per d_qk k-step");
     using QGc = std::integral_constant<int, QG>;
     using VGc = std::integral_constant<int, VG>;
 
@@ -227,17 +239,21 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     };
 
     // ---- per-lane LDS offsets
-    const int s16 = swz8(l16);
-    // Q / K fragment for k-step ks of rows 16 t + l16: columns 32 ks + 4 g4 (+16)
-    int qkoff[2][2];
+    // Q / K fragment for k-step ks of rows 16 t + l16: columns 32 ks + 4 g4
+    // (+16), i.e. logical granule 4 ks + (g4 >> 1) (+2); the swizzle touches
+    // the low four granule bits, so the per-lane part depends on ks & 3 and
+    // ks >> 2 adds 16 granules (128 elements)
+    constexpr int NQO = NKS < 4 ? NKS : 4;
+    const int s16 = qswz(l16);
+    int qkoff[NQO][2];
 #pragma unroll
-    for (int par = 0; par < 2; ++par)
+    for (int par = 0; par < NQO; ++par)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-            qkoff[par][hh] = l16 * DKP + (((((par << 2) | ((g4 >> 1) + 2 * hh)) ^ s16)) << 3) + 4 * (g4 & 1);
+            qkoff[par][hh] = l16 * DKP + (((4 * par + (g4 >> 1) + 2 * hh) ^ s16) << 3) + 4 * (g4 & 1);
     auto qk_frag = [&](const bf16 *tilebase, int ks) -> bf16x8 {  // tilebase: row 16 t of the tile
-        const bf16 *b = tilebase + ((ks >> 1) << 6);
-        return cat8(ld4(b + qkoff[ks & 1][0]), ld4(b + qkoff[ks & 1][1]));
+        const bf16 *b = tilebase + ((ks >> 2) << 7);
+        return cat8(ld4(b + qkoff[ks & 3][0]), ld4(b + qkoff[ks & 3][1]));
     };
     // Transpose reads of a 16-column block cb = 4 hi + lo of a swizzled tile:
     // the swizzle touches the low three granule bits only, so the per-lane part
@@ -255,27 +271,25 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     // barriers (one after the prologue, two per chunk).
     if (is_state) {
         // ========================= state wavefronts =========================
-        if (nchunks > 0) {
-            copy_tile(Qs, qg, DKP, QGc{}, t_begin);
-            copy_tile(Ks[0], kg, DKP, QGc{}, t_begin);
-        }
-        role_sync(true);
+        role_sync<63>();
         for (int c = 0; c < nchunks; ++c) {
             const float *G = gt[c & 1];
-            const int tc = t_begin + c * L;
             const float m_next = G[6 * LP + 0], s_last = G[6 * LP + 1];
-            const bool more = c + 1 < nchunks;
 
-            // ---- phase 1: copies V(c), K(c+1); read-out O^T = C'^T Q^T
-            copy_tile(Vs, vg, dv, VGc{}, tc);
-            if (more) copy_tile(Ks[(c + 1) & 1], kg, DKP, QGc{}, tc + L);
+            // ---- phase 1: read-out O^T = C'^T Q^T and q.n'
             {
                 f32x4 Ot[2][NT];
 #pragma unroll
                 for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
                     for (int t = 0; t < NT; ++t) Ot[bt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                bf16x8 bq = qk_frag(Qs, 0);
+                // the Q fragments of a k-step stay in registers for the high
+                // and the low pass; the low pass refills each for the next
+                // k-step
+                bf16x8 qf[NT];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) qf[t] = qk_frag(Qs + 16 * t * DKP, 0);
+                f32x4 qd = {0.f, 0.f, 0.f, 0.f};  // q.n' of token tile s (every row)
 #pragma unroll
                 for (int kk = 0; kk < NKS; ++kk) {
                     __builtin_amdgcn_sched_barrier(0);
@@ -288,15 +302,27 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                         split8(x, ach[bt], acl[bt]);
                     }
 #pragma unroll
+                    for (int t = 0; t < NT; ++t)
+#pragma unroll
+                        for (int bt = 0; bt < 2; ++bt) Ot[bt][t] = mfma(ach[bt], qf[t], Ot[bt][t]);
+                    {
+                        // n' in the k order of the Q fragments, identical in every row
+                        const int nc = 32 * kk + 4 * g4;
+                        const bf16x8 nh = cat8(ld4(&nhl[0][nc]), ld4(&nhl[0][nc + 16]));
+                        const bf16x8 nl = cat8(ld4(&nhl[1][nc]), ld4(&nhl[1][nc + 16]));
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) {
+                            if (t == s) {
+                                qd = mfma(nh, qf[t], qd);
+                                qd = mfma(nl, qf[t], qd);
+                            }
+                        }
+                    }
+#pragma unroll
                     for (int t = 0; t < NT; ++t) {
-                        bf16x8 bqn;
-                        const bool nxt = t + 1 < NT || kk + 1 < NKS;
-                        if (nxt) bqn = qk_frag(Qs + 16 * ((t + 1) % NT) * DKP, kk + (t + 1) / NT);
 #pragma unroll
-                        for (int bt = 0; bt < 2; ++bt) Ot[bt][t] = mfma(ach[bt], bq, Ot[bt][t]);
-#pragma unroll
-                        for (int bt = 0; bt < 2; ++bt) Ot[bt][t] = mfma(acl[bt], bq, Ot[bt][t]);
-                        if (nxt) bq = bqn;
+                        for (int bt = 0; bt < 2; ++bt) Ot[bt][t] = mfma(acl[bt], qf[t], Ot[bt][t]);
+                        if (kk + 1 < NKS) qf[t] = qk_frag(Qs + 16 * t * DKP, kk + 1);
                     }
                 }
                 // scale by e^{m - r_i} and the held state's sigma, hand over
@@ -306,12 +332,12 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
 #pragma unroll
                     for (int bt = 0; bt < 2; ++bt) Xch[t][2 * s + bt][lane] = Ot[bt][t] * si;
                 }
+                if (g4 == 0) qn_sh[16 * s + l16] = qd[0];
             }
-            role_sync(true);  // (X) read-out in LDS; V(c), K(c+1) landed; Q(c) free
+            role_sync<63>();  // (X) read-out, q.n' in LDS; V(c) landed; Q(c) free
 
-            // ---- phase 2: copy Q(c+1); C'/sigma' += K^T ((w/sigma') (x) V),
-            // sigma' = sigma * decay; n' likewise (true scale)
-            if (more) copy_tile(Qs, qg, DKP, QGc{}, tc + L);
+            // ---- phase 2: C'/sigma' += K^T ((w/sigma') (x) V), sigma' =
+            // sigma * decay; n' likewise (true scale)
             sigma *= s_last;
             if (sigma < kRenorm) {  // uniform: fold sigma back into the held state
 #pragma unroll
@@ -332,15 +358,12 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                 return row * GPR * 8 + (((2 * lo + (ltq >> 1)) ^ swz8(row)) << 3) + 4 * (ltq & 1);
             };
             const int krow0 = 8 * lg4 + lte, krow1 = krow0 + 4;
-            int kto[4][2];
-#pragma unroll
-            for (int lo = 0; lo < 4; ++lo) {
-                kto[lo][0] = tr_off2(QGc{}, krow0, lo);
-                kto[lo][1] = tr_off2(QGc{}, krow1, lo);
-            }
+            // K^T row tile at: logical granule 2 at + (tq >> 1) of rows krow0 / krow1
+            const int kb0 = krow0 * QG * 8 + 4 * (ltq & 1), kb1 = krow1 * QG * 8 + 4 * (ltq & 1);
+            const int kx0 = qswz(krow0) ^ (ltq >> 1), kx1 = qswz(krow1) ^ (ltq >> 1);
             auto kt_frag = [&](const bf16 *rowblock, int at) -> bf16x8 {
-                const bf16 *b = rowblock + 64 * (at >> 2);
-                return cat8(tr_read(b + kto[at & 3][0]), tr_read(b + kto[at & 3][1]));
+                return cat8(tr_read(rowblock + kb0 + (((2 * at) ^ kx0) << 3)),
+                            tr_read(rowblock + kb1 + (((2 * at) ^ kx1) << 3)));
             };
             f32x4 nacc[NAT / 4];
 #pragma unroll
@@ -372,31 +395,21 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                 const bf16 *W2 = reinterpret_cast<const bf16 *>(&G[5 * LP]);
                 const bf16x8 bnh = *reinterpret_cast<const bf16x8 *>(W2 + 32 * js + 8 * g4);
                 const bf16x8 bnl = *reinterpret_cast<const bf16x8 *>(W2 + LP + 32 * js + 8 * g4);
-                constexpr int GRP = 2;
-                bf16x8 ak[GRP];
+                // K^T fragments fetched two row tiles ahead (ring of three)
+                constexpr int AHEAD = 2;
+                bf16x8 ak[AHEAD + 1];
 #pragma unroll
-                for (int u = 0; u < GRP; ++u) ak[u] = kt_frag(k0, u);
+                for (int u = 0; u < AHEAD; ++u) ak[u] = kt_frag(k0, u);
 #pragma unroll
-                for (int g0 = 0; g0 < NAT; g0 += GRP) {
+                for (int at = 0; at < NAT; ++at) {
                     __builtin_amdgcn_sched_barrier(0);
-                    bf16x8 akn[GRP];
-                    if (g0 + GRP < NAT) {
+                    if (at + AHEAD < NAT) ak[(at + AHEAD) % (AHEAD + 1)] = kt_frag(k0, at + AHEAD);
+                    const bf16x8 &a0 = ak[at % (AHEAD + 1)];
 #pragma unroll
-                        for (int u = 0; u < GRP; ++u) akn[u] = kt_frag(k0, g0 + GRP + u);
-                    }
-#pragma unroll
-                    for (int u = 0; u < GRP; ++u) {
-                        const int at = g0 + u;
-#pragma unroll
-                        for (int bt = 0; bt < 2; ++bt) Cr[at][bt] = mfma(ak[u], bw[bt], Cr[at][bt]);
-                        if ((at & 3) == s) {
-                            nacc[at >> 2] = mfma(ak[u], bnh, nacc[at >> 2]);
-                            nacc[at >> 2] = mfma(ak[u], bnl, nacc[at >> 2]);
-                        }
-                    }
-                    if (g0 + GRP < NAT) {
-#pragma unroll
-                        for (int u = 0; u < GRP; ++u) ak[u] = akn[u];
+                    for (int bt = 0; bt < 2; ++bt) Cr[at][bt] = mfma(a0, bw[bt], Cr[at][bt]);
+                    if ((at & 3) == s) {
+                        nacc[at >> 2] = mfma(a0, bnh, nacc[at >> 2]);
+                        nacc[at >> 2] = mfma(a0, bnl, nacc[at >> 2]);
                     }
                 }
             }
@@ -420,7 +433,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                 }
             }
             m_prev = m_next;
-            role_sync(true);  // (Y) Q(c+1), K(c+1) landed; n' visible; V(c), Xch free
+            role_sync<63>();  // (Y) Q(c+1), K(c+1) landed; n' visible; V(c), Xch, q.n' free
         }
 
         // ---- state out (n' and m from wavefront 0 of column block 0)
@@ -441,11 +454,15 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
         }
     } else {
         // ========================= intra wavefronts =========================
-        if (nchunks > 0 && wave == GW) {
-            load_gates(0);
-            gate_prep(m_prev, gt[0]);
+        if (nchunks > 0) {
+            copy_tile(Qs, qg, DKP, QGc{}, t_begin);
+            copy_tile(Ks[0], kg, DKP, QGc{}, t_begin);
+            if (wave == GW) {
+                load_gates(0);
+                gate_prep(m_prev, gt[0]);
+            }
         }
-        role_sync(false);
+        role_sync<0>();
         const int it = s;                // token tile of this wavefront
         const int irow = 16 * it + l16;  // token of this lane within the chunk (accumulator column)
         for (int c = 0; c < nchunks; ++c) {
@@ -455,8 +472,10 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             const float m_next = G[6 * LP + 0];
             const bool more = c + 1 < nchunks;
 
-            // ---- phase 1: S, q.n', P of this token tile; next gate table
-            uint2 orw[NCT];  // output-gate inputs (used in phase 2)
+            // ---- phase 1: copy V(c); S, P of this token tile; next gate
+            // table; copy K(c+1)
+            copy_tile(Vs, vg, dv, VGc{}, tc);
+            uint2 orw[NCT];  // output-gate inputs
             {
                 const int t = min(tc + irow, t_end - 1);
 #pragma unroll
@@ -464,29 +483,31 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                     orw[ct] = *reinterpret_cast<const uint2 *>(og + (size_t)t * dv + 16 * ct + 4 * g4);
             }
             if (more && wave == GW) load_gates(c + 1);
-            // S^T tiles (jt, it) for jt <= it and q.n', k-step outermost so
-            // each Q fragment serves all of them
+            // S^T tiles (jt, it) for jt <= it, k-step outermost so each Q
+            // fragment serves all of them; each K fragment is refilled for the
+            // next k-step right after its MFMA
             f32x4 St[NT];
 #pragma unroll
             for (int jt = 0; jt < NT; ++jt) St[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            f32x4 qd = {0.f, 0.f, 0.f, 0.f};
             const bf16 *qrow = Qs + 16 * it * DKP;
             const bf16 *K = Ks[c & 1];
+            bf16x8 fq = qk_frag(qrow, 0), fk[NT];
+#pragma unroll
+            for (int jt = 0; jt < NT; ++jt)
+                if (jt <= it) fk[jt] = qk_frag(K + 16 * jt * DKP, 0);
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 fq = qk_frag(qrow, ks);
-                // n' in the same k order, identical in every row of the operand
-                const int nc = 32 * ks + 4 * g4;
-                const bf16x8 nh = cat8(ld4(&nhl[0][nc]), ld4(&nhl[0][nc + 16]));
-                const bf16x8 nl = cat8(ld4(&nhl[1][nc]), ld4(&nhl[1][nc + 16]));
+                bf16x8 fqn;
+                if (ks + 1 < NKS) fqn = qk_frag(qrow, ks + 1);
 #pragma unroll
                 for (int jt = 0; jt < NT; ++jt) {
-                    if (jt <= it) St[jt] = mfma(qk_frag(K + 16 * jt * DKP, ks), fq, St[jt]);
+                    if (jt <= it) {
+                        St[jt] = mfma(fk[jt], fq, St[jt]);
+                        if (ks + 1 < NKS) fk[jt] = qk_frag(K + 16 * jt * DKP, ks + 1);
+                    }
                 }
-                qd = mfma(nh, fq, qd);
-                qd = mfma(nl, fq, qd);
+                if (ks + 1 < NKS) fq = fqn;
             }
-            const float qn = qd[0];
             // P = S (x) e^{u_j - r_i} (j <= i), bf16, in the k order of the V^T fragments
             bf16x4 Pb[NT];
             float rowsum = 0.0f;
@@ -510,7 +531,18 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             rowsum += __shfl_xor(rowsum, 16, 64);
             rowsum += __shfl_xor(rowsum, 32, 64);
             if (more && wave == GW) gate_prep(m_next, Gnext);
-            role_sync(false);  // (X)
+            // the output-gate loads (and the V copy before them) complete here,
+            // before the K copy goes out (the opaque use keeps the compiler from
+            // waiting for them later, together with the copies)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) asm volatile("" : "+v"(orw[ct].x), "+v"(orw[ct].y));
+            if (more) copy_tile(Ks[(c + 1) & 1], kg, DKP, QGc{}, tc + L);
+            // (X) V(c) landed (only the K copy may stay in flight)
+            if (more)
+                role_sync<NKS>();
+            else
+                role_sync<0>();
+            if (more) copy_tile(Qs, qg, DKP, QGc{}, tc + L);  // every reader of Q(c) is past X
 
             // ---- phase 2: O^T of this token tile = scaled read-out + V^T P^T; h
             int vpo[4][2];  // V^T fragment offsets by (column tile & 3, read)
@@ -534,25 +566,32 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                     }
                 }
             }
-            const float den = G[2 * LP + irow] * qn + rowsum;
-            const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), G[3 * LP + irow]));
-            const int t = tc + irow;
+            // token index from an opaque copy of the lane (cheaper to recompute
+            // than to keep in a register across the chunk loop)
+            int ln2 = lane;
+            asm volatile("" : "+v"(ln2));
+            const int irow2 = 16 * it + (ln2 & 15);
+            const float den = G[2 * LP + irow2] * qn_sh[irow2] + rowsum;
+            const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), G[3 * LP + irow2]));
+            const int t = tc + irow2;
             if (t < t_end) {
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
-                    const uint2 o4 = orw[ct];
+                    const float ox[4] = {__uint_as_float(orw[ct].x << 16), __uint_as_float(orw[ct].x & 0xffff0000u),
+                                         __uint_as_float(orw[ct].y << 16), __uint_as_float(orw[ct].y & 0xffff0000u)};
                     float y[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t wd = e < 2 ? o4.x : o4.y;
-                        const float ox = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
-                        y[e] = acc[ct][e] * inv * __builtin_amdgcn_rcpf(1.0f + exp_e(-ox));
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        y[e] = acc[ct][e] * inv * __builtin_amdgcn_rcpf(1.0f + exp_e(-ox[e]));
                     const bf16x4 hv = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
                     *reinterpret_cast<bf16x4 *>(hg + (size_t)t * dv + 16 * ct + 4 * g4) = hv;
                 }
             }
-            role_sync(false);  // (Y)
+            // (Y) K(c+1), Q(c+1) landed (only this chunk's h stores may stay in flight)
+            if (more)
+                role_sync<NCT>();
+            else
+                role_sync<0>();
         }
     }
 }
