@@ -12,7 +12,7 @@
 // once in and once out (512 KiB each way per pair at 256x512), against ~5 flops per
 // element.  One workgroup owns one pair, so the in-place update of n and m
 // cannot race with another workgroup.  Threads are laid out as TPR = d_v/4
-// column groups (one float4 of a row each) times RPI = 256/TPR row groups, so
+// column groups (one float4 of a row each) times RPI = NTH/TPR row groups, so
 // a wavefront reads 64 consecutive float4 of one row (1 KiB, fully
 // coalesced); each thread keeps UNROLL rows of loads in flight, and the
 // read-out C'^T q is accumulated in the same pass and reduced over row groups
@@ -23,7 +23,7 @@ namespace mlstm {
 
 namespace {
 
-constexpr int NTH = 256;
+constexpr int NTH = 512;
 constexpr int UNROLL = 8;
 
 // streaming (non-temporal) 16-byte accesses: the memory is touched once per step
