@@ -71,6 +71,13 @@ __device__ __forceinline__ int swz16(int r) {
     return (f << 1) | ((r >> 3) & 1);
 }
 
+// Granules per row of a tile, and whether it is a Q/K tile (swizzled with
+// swz16 from 16 granules per row) or a V tile (swz8).
+template <int G, bool QK>
+struct TileGranules : std::integral_constant<int, G> {
+    static constexpr bool qk_tile = QK;
+};
+
 // Workgroup barrier after this wavefront's LDS accesses have completed and at
 // most VM of its vector-memory operations are outstanding (they complete in
 // issue order).  State wavefronts issue none and pass VM = 63 (no wait).
@@ -180,15 +187,20 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     // [(k NSW + s) 64, +64), rows k RPI + const.  Rows past the segment end
     // are clamped to its last row (finite data; their gates zero them out).
     // copy_part issues instruction k of a tile copy, copy_tile all of them.
+    // gpr_c: granules per row of the tile; Q and K tiles (QG granules per
+    // row) use qswz, the V tile (VG granules per row) swz8 -- the tile kind
+    // follows the granule count type, QGc or VGc, not its value (they are
+    // equal for d_qk 128)
     auto copy_part = [&](bf16 *dst, const bf16 *src, int ld, auto gpr_c, int tc, int k) {
         constexpr int GPR = decltype(gpr_c)::value;
+        constexpr bool QK_TILE = decltype(gpr_c)::qk_tile;
         constexpr int RPI = NSW * 64 / GPR;
         static_assert((L * GPR) % (NSW * 64) == 0 && RPI % 8 == 0, "copy shape");
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int pgr = s * 64 + ln;
         const int row = k * RPI + pgr / GPR;
-        const int gl = (pgr % GPR) ^ (GPR == QG ? qswz(row) : swz8(row));
+        const int gl = (pgr % GPR) ^ (QK_TILE ? qswz(row) : swz8(row));
         const int t = min(tc + row, t_end - 1);
         __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)t * ld + gl * 8),
                                          (lds_void *)(dst + (k * NSW + s) * 64 * 8), 16, 0, 0);
@@ -199,8 +211,8 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
         for (int k = 0; k < NI; ++k) copy_part(dst, src, ld, gpr_c, tc, k);
     };
     static_assert(L * QG / (NSW * 64) == NKS, "one K or Q copy instruction per d_qk k-step");
-    using QGc = std::integral_constant<int, QG>;
-    using VGc = std::integral_constant<int, VG>;
+    using QGc = TileGranules<QG, true>;
+    using VGc = TileGranules<VG, false>;
 
     // ---- gates (first intra wavefront; one token per lane)
     constexpr int GW = NSW;
