@@ -246,7 +246,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": traffic_record("prefill_7b"),
-                     "kernel": "mlstm_bf16_kernel<64,256,128> (fused chunkwise forward, one launch per step)",
+                     "kernel": "mlstm_ws_kernel<256> (role-split chunkwise forward, one launch per step)",
                      "mfma": {"achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                               "frac": tflops / PEAK_BF16_TFLOPS},
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes},
