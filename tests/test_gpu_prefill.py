@@ -71,6 +71,45 @@ def test_chunk64_value_blocks(dk, dv, with_state):
                    f"chunk 64 dk={dk} dv={dv} state={with_state}")
 
 
+@pytest.mark.parametrize("dk", [64, 128, 256])
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_readout_keeps_state_precision(dk, chunk):
+    """The inter-chunk read-out C'^T q must keep the float32 state's precision
+    beyond bf16.  Every row of C0 is a common vector plus a per-row offset
+    2^-9 times smaller, and q_t = e_a - e_b picks the difference of two rows,
+    so h is the difference of the two offsets: a read-out that rounds C' to
+    bf16 alone (8 significant bits) loses it whole, the high part plus the
+    rounded remainder keeps it to well inside the tolerance.  k = 0 keeps the
+    intra-chunk part and the update at zero; i~ = -30 keeps the stabilizer at
+    m, so the read-out is all that h holds."""
+    P, T, dv = 2, 150, 128
+    rng = np.random.default_rng(77 + dk + chunk)
+    q = np.zeros((P, T, dk))
+    for p in range(P):
+        for t in range(T):
+            a, b = rng.choice(dk, size=2, replace=False)
+            q[p, t, a], q[p, t, b] = 1.0, -1.0
+    common = rng.normal(0.0, 1.0, (P, 1, dv))
+    C0 = common + rng.normal(0.0, 2.0 ** -9, (P, dk, dv))
+    d = {
+        "q": torch.from_numpy(q).to(torch.bfloat16),
+        "k": torch.zeros((P, T, dk), dtype=torch.bfloat16),
+        "v": torch.from_numpy(rng.normal(0.0, 1.0, (P, T, dv))).to(torch.bfloat16),
+        "i_pre": torch.full((P, T), -30.0, dtype=torch.float32),
+        "f_pre": torch.from_numpy(-np.log1p(np.exp(-rng.normal(5.0, 1.0, (P, T))))).float(),
+        "o_pre": torch.from_numpy(rng.normal(0.0, 1.0, (P, T, dv))).to(torch.bfloat16),
+        "C0": torch.from_numpy(C0).float(),
+        "n0": torch.from_numpy(rng.normal(0.0, 1.0, (P, dk))).float(),
+        "m0": torch.zeros((P,), dtype=torch.float32),
+    }
+    gpu = PT.run_gpu_fwd(d, chunk, variant="fused")
+    ref = PT.run_oracle(d)
+    eh = PT.compare_fwd(gpu, ref, "bf16", f"read-out precision dk={dk} chunk={chunk}")[0]
+    # bf16 alone would be off by more than 50% on every token (emulated on
+    # the CPU); the high part plus the remainder stays under 0.6%
+    assert eh <= 2e-2
+
+
 def test_segscan_equals_oracle():
     """The segmented schedule (local states, scan, seeded pass) on bf16."""
     w, d = case("prefill_7b_bf16", pairs=[(0, 1), (4, 4)], T=1000)

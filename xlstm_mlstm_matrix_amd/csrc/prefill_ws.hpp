@@ -61,14 +61,60 @@ struct WsCfg {
     static_assert(QG >= 8, "swizzle needs 8 granules per row");
 };
 
-// Row swizzle of the 16-byte granules of the Q and K tiles (rows with 16 or
-// more granules): a bijection of row mod 16, so the 16 rows an MFMA fragment
-// read touches at one logical granule land in 16 different granules; the
-// transpose reads of K (4 consecutive rows, and the same rows + 8) stay
-// spread as well.
-__device__ __forceinline__ int swz16(int r) {
-    const int f = (r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
-    return (f << 1) | ((r >> 3) & 1);
+// Row swizzles of the 16-byte granules of the Q and K tiles.  Two kinds of
+// read must spread over the LDS banks:
+//  * fragment reads: 16 consecutive rows, one whole granule each, at the same
+//    logical granule;
+//  * transpose reads of K: rows 8 g + (0..3), 8-byte halves of four
+//    consecutive logical granules 4 a + (0..3), all at the same half.
+// With 16 or more granules per row (rows a multiple of 256 bytes apart, so a
+// granule's banks depend on its position only) swzt16 swaps the two 2-bit
+// digits of row mod 16: a bijection of row mod 16 (fragment reads), and rows
+// 0..3 of an 8-row group differ in bits 2-3 (the four granules of a transpose
+// read then land in four different aligned groups of four).  With 8 granules
+// per row (128-byte rows: odd rows sit half the banks over) swzt8 reverses
+// the bits of (row / 2) mod 8: a bijection over the 8 rows of each parity,
+// and rows two apart differ in bit 2.
+__device__ __forceinline__ int swzt16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swzt8(int r) {
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+}
+
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Packed bf16 pairs (-1, 0) and (0, -1), the operands that pick one high
+// part out of a pair in split8_pk.  They are built in scalar registers from
+// their bit patterns behind an opaque move: folded into an inline constant of
+// the dot-product instruction, the first of them reads back as a different
+// pair on gfx950 (wrong remainders for every even value).
+struct SplitMasks {
+    bf16x2 neg_lo, neg_hi;
+};
+__device__ __forceinline__ SplitMasks split_masks() {
+    unsigned lo = 0x0000bf80u, hi = 0xbf800000u;
+    asm volatile("" : "+s"(lo), "+s"(hi));
+    return {__builtin_bit_cast(bf16x2, lo), __builtin_bit_cast(bf16x2, hi)};
+}
+
+// Split 8 floats into bf16 high parts (round to nearest even, converted in
+// pairs) and bf16 remainders.  The remainder x - hi is exact in float32; it
+// comes from a bf16 dot product of the packed high parts with (-1, 0) or
+// (0, -1) accumulated onto x, one instruction per value.
+__device__ __forceinline__ void split8_pk(const float *x, const SplitMasks &m, bf16x8 &hi, bf16x8 &lo) {
+    const bf16x2 neg_lo = m.neg_lo, neg_hi = m.neg_hi;
+    bf16x2 h[4], l[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const f32x2 v = {x[2 * p], x[2 * p + 1]};
+        h[p] = __builtin_convertvector(v, bf16x2);
+        const f32x2 r = {__builtin_amdgcn_fdot2_f32_bf16(h[p], neg_lo, v.x, false),
+                         __builtin_amdgcn_fdot2_f32_bf16(h[p], neg_hi, v.y, false)};
+        l[p] = __builtin_convertvector(r, bf16x2);
+    }
+    hi = bf16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+    lo = bf16x8{l[0][0], l[0][1], l[1][0], l[1][1], l[2][0], l[2][1], l[3][0], l[3][1]};
 }
 
 // Granules per row of a tile, and whether it is a Q/K tile (swizzled with
@@ -107,7 +153,6 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) float gt[2][GTF];
     __shared__ __attribute__((aligned(16))) float nsh[DKP];     // n' (true scale)
     __shared__ __attribute__((aligned(16))) bf16 nhl[2][DKP];   // n' as bf16 high part, remainder
-    __shared__ float qn_sh[L];                                  // q.n' of the chunk's tokens
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -156,6 +201,11 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
         m_prev = a.m0[bh];
     }
     const int scol = col0 + 32 * s + l16;  // state column of this lane (tile bt adds 16 bt)
+    // Row i = 4 g4 + r of the 16-row C' tile at holds d_qk index
+    // 32 (at / 2) + 8 g4 + 4 (at % 2) + r: tiles 2 kk and 2 kk + 1 together give
+    // each lane group 8 consecutive d_qk indices, the k slots of one whole Q
+    // granule in the read-out.  The K^T fragments of the update follow it.
+    auto crow = [&](int at, int r) -> int { return 32 * (at >> 1) + 8 * g4 + 4 * (at & 1) + r; };
     f32x4 Cr[NAT][2];
 #pragma unroll
     for (int at = 0; at < NAT; ++at)
@@ -163,7 +213,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
         for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Cr[at][bt][r] = (is_state && Cs) ? Cs[(size_t)(16 * at + 4 * g4 + r) * dv + scol + 16 * bt] : 0.0f;
+                Cr[at][bt][r] = (is_state && Cs) ? Cs[(size_t)crow(at, r) * dv + scol + 16 * bt] : 0.0f;
     for (int e = tid; e < DKP; e += Cfg::NTH) {
         const float x = ns ? ns[e] : 0.0f;
         nsh[e] = x;
@@ -173,13 +223,13 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     }
     float sigma = 1.0f;  // C' is held divided by sigma (state wavefronts)
 
-    // Q and K tiles are swizzled with swz16 (swz8 below 16 granules per row),
-    // V tiles with swz8.
+    // Q and K tiles are swizzled with swzt16 (swzt8 at 8 granules per row), V
+    // tiles with swz8.
     auto qswz = [](int row) -> int {
         if constexpr (QG >= 16)
-            return swz16(row);
+            return swzt16(row);
         else
-            return swz8(row);
+            return swzt8(row);
     };
     // ---- global -> LDS copies by the intra wavefronts.  Physical granule g
     // of a tile is (row, p) with p = g % gpr holding logical granule
@@ -251,21 +301,17 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     };
 
     // ---- per-lane LDS offsets
-    // Q / K fragment for k-step ks of rows 16 t + l16: columns 32 ks + 4 g4
-    // (+16), i.e. logical granule 4 ks + (g4 >> 1) (+2); the swizzle touches
-    // the low four granule bits, so the per-lane part depends on ks & 3 and
+    // Q / K fragment for k-step ks of rows 16 t + l16: columns 32 ks + 8 g4
+    // .. +8, i.e. the whole logical granule 4 ks + g4; the swizzle touches the
+    // low four granule bits, so the per-lane part depends on ks & 3 and
     // ks >> 2 adds 16 granules (128 elements)
     constexpr int NQO = NKS < 4 ? NKS : 4;
     const int s16 = qswz(l16);
-    int qkoff[NQO][2];
+    int qkoff[NQO];
 #pragma unroll
-    for (int par = 0; par < NQO; ++par)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            qkoff[par][hh] = l16 * DKP + (((4 * par + (g4 >> 1) + 2 * hh) ^ s16) << 3) + 4 * (g4 & 1);
+    for (int par = 0; par < NQO; ++par) qkoff[par] = l16 * DKP + (((4 * par + g4) ^ s16) << 3);
     auto qk_frag = [&](const bf16 *tilebase, int ks) -> bf16x8 {  // tilebase: row 16 t of the tile
-        const bf16 *b = tilebase + ((ks >> 2) << 7);
-        return cat8(ld4(b + qkoff[ks & 3][0]), ld4(b + qkoff[ks & 3][1]));
+        return *reinterpret_cast<const bf16x8 *>(tilebase + ((ks >> 2) << 7) + qkoff[ks & 3]);
     };
     // Transpose reads of a 16-column block cb = 4 hi + lo of a swizzled tile:
     // the swizzle touches the low three granule bits only, so the per-lane part
@@ -283,6 +329,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     // barriers (one after the prologue, two per chunk).
     if (is_state) {
         // ========================= state wavefronts =========================
+        const SplitMasks smask = split_masks();
         role_sync<63>();
         for (int c = 0; c < nchunks; ++c) {
             const float *G = gt[c & 1];
@@ -301,7 +348,6 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                 bf16x8 qf[NT];
 #pragma unroll
                 for (int t = 0; t < NT; ++t) qf[t] = qk_frag(Qs + 16 * t * DKP, 0);
-                f32x4 qd = {0.f, 0.f, 0.f, 0.f};  // q.n' of token tile s (every row)
 #pragma unroll
                 for (int kk = 0; kk < NKS; ++kk) {
                     __builtin_amdgcn_sched_barrier(0);
@@ -311,25 +357,12 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                         const float x[8] = {Cr[2 * kk][bt][0],     Cr[2 * kk][bt][1],     Cr[2 * kk][bt][2],
                                             Cr[2 * kk][bt][3],     Cr[2 * kk + 1][bt][0], Cr[2 * kk + 1][bt][1],
                                             Cr[2 * kk + 1][bt][2], Cr[2 * kk + 1][bt][3]};
-                        split8(x, ach[bt], acl[bt]);
+                        split8_pk(x, smask, ach[bt], acl[bt]);
                     }
 #pragma unroll
                     for (int t = 0; t < NT; ++t)
 #pragma unroll
                         for (int bt = 0; bt < 2; ++bt) Ot[bt][t] = mfma(ach[bt], qf[t], Ot[bt][t]);
-                    {
-                        // n' in the k order of the Q fragments, identical in every row
-                        const int nc = 32 * kk + 4 * g4;
-                        const bf16x8 nh = cat8(ld4(&nhl[0][nc]), ld4(&nhl[0][nc + 16]));
-                        const bf16x8 nl = cat8(ld4(&nhl[1][nc]), ld4(&nhl[1][nc + 16]));
-#pragma unroll
-                        for (int t = 0; t < NT; ++t) {
-                            if (t == s) {
-                                qd = mfma(nh, qf[t], qd);
-                                qd = mfma(nl, qf[t], qd);
-                            }
-                        }
-                    }
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -344,9 +377,8 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
 #pragma unroll
                     for (int bt = 0; bt < 2; ++bt) Xch[t][2 * s + bt][lane] = Ot[bt][t] * si;
                 }
-                if (g4 == 0) qn_sh[16 * s + l16] = qd[0];
             }
-            role_sync<63>();  // (X) read-out, q.n' in LDS; V(c) landed; Q(c) free
+            role_sync<63>();  // (X) read-out in LDS; V(c) landed; Q(c) free
 
             // ---- phase 2: C'/sigma' += K^T ((w/sigma') (x) V), sigma' =
             // sigma * decay; n' likewise (true scale)
@@ -370,12 +402,15 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                 return row * GPR * 8 + (((2 * lo + (ltq >> 1)) ^ swz8(row)) << 3) + 4 * (ltq & 1);
             };
             const int krow0 = 8 * lg4 + lte, krow1 = krow0 + 4;
-            // K^T row tile at: logical granule 2 at + (tq >> 1) of rows krow0 / krow1
-            const int kb0 = krow0 * QG * 8 + 4 * (ltq & 1), kb1 = krow1 * QG * 8 + 4 * (ltq & 1);
-            const int kx0 = qswz(krow0) ^ (ltq >> 1), kx1 = qswz(krow1) ^ (ltq >> 1);
+            // K^T row tile at: the lanes of column quad tq supply fragment rows
+            // 4 tq .. 4 tq + 3, here d_qk 32 (at / 2) + 8 tq + 4 (at % 2) + (0..3):
+            // half at % 2 of logical granule 4 (at / 2) + tq of rows krow0 / krow1
+            const int kb0 = krow0 * QG * 8, kb1 = krow1 * QG * 8;
+            const int kx0 = qswz(krow0) ^ ltq, kx1 = qswz(krow1) ^ ltq;
             auto kt_frag = [&](const bf16 *rowblock, int at) -> bf16x8 {
-                return cat8(tr_read(rowblock + kb0 + (((2 * at) ^ kx0) << 3)),
-                            tr_read(rowblock + kb1 + (((2 * at) ^ kx1) << 3)));
+                const int h = 4 * (at & 1), g = 4 * (at >> 1);
+                return cat8(tr_read(rowblock + kb0 + h + ((g ^ kx0) << 3)),
+                            tr_read(rowblock + kb1 + h + ((g ^ kx1) << 3)));
             };
             f32x4 nacc[NAT / 4];
 #pragma unroll
@@ -430,7 +465,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             if (l16 == 0) {
 #pragma unroll
                 for (int x = 0; x < NAT / 4; ++x) {
-                    const int r0 = 16 * (s + 4 * x) + 4 * g4;
+                    const int r0 = crow(s + 4 * x, 0);
                     f32x4 *np = reinterpret_cast<f32x4 *>(&nsh[r0]);
                     const f32x4 nn = *np * s_last + nacc[x];
                     *np = nn;
@@ -457,7 +492,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                 for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        Cdst[(size_t)(16 * at + 4 * g4 + r) * dv + scol + 16 * bt] = Cr[at][bt][r] * sigma;
+                        Cdst[(size_t)crow(at, r) * dv + scol + 16 * bt] = Cr[at][bt][r] * sigma;
             if (tile == 0 && wave == 0) {
                 float *ndst = a.nT + (size_t)bh * dk;
                 for (int e = lane; e < dk; e += 64) ndst[e] = nsh[e];
@@ -498,7 +533,9 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             // S^T tiles (jt, it) for jt <= it, k-step outermost so each Q
             // fragment serves all of them; each K fragment is refilled for the
             // next k-step right after its MFMA
-            f32x4 St[NT];
+            // q.n' of the tile's tokens rides along: an MFMA with n' (high part
+            // and remainder) in every row of the A operand
+            f32x4 St[NT], qd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int jt = 0; jt < NT; ++jt) St[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
             const bf16 *qrow = Qs + 16 * it * DKP;
@@ -511,6 +548,8 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             for (int ks = 0; ks < NKS; ++ks) {
                 bf16x8 fqn;
                 if (ks + 1 < NKS) fqn = qk_frag(qrow, ks + 1);
+                const bf16x8 nh = *reinterpret_cast<const bf16x8 *>(&nhl[0][32 * ks + 8 * g4]);
+                const bf16x8 nl = *reinterpret_cast<const bf16x8 *>(&nhl[1][32 * ks + 8 * g4]);
 #pragma unroll
                 for (int jt = 0; jt < NT; ++jt) {
                     if (jt <= it) {
@@ -518,8 +557,11 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                         if (ks + 1 < NKS) fk[jt] = qk_frag(K + 16 * jt * DKP, ks + 1);
                     }
                 }
+                qd = mfma(nh, fq, qd);
+                qd = mfma(nl, fq, qd);
                 if (ks + 1 < NKS) fq = fqn;
             }
+            const float qn = qd[0];  // q.n' of token irow
             // P = S (x) e^{u_j - r_i} (j <= i), bf16, in the k order of the V^T fragments
             bf16x4 Pb[NT];
             float rowsum = 0.0f;
@@ -583,7 +625,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             int ln2 = lane;
             asm volatile("" : "+v"(ln2));
             const int irow2 = 16 * it + (ln2 & 15);
-            const float den = G[2 * LP + irow2] * qn_sh[irow2] + rowsum;
+            const float den = G[2 * LP + irow2] * qn + rowsum;
             const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), G[3 * LP + irow2]));
             const int t = tc + irow2;
             if (t < t_end) {
