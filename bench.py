@@ -12,7 +12,10 @@ roofline, and the float64 oracle timed on the host cores over a bounded
 sample (`cpu_baseline`).
 
 Kernel times come from HIP events recorded on the stream the library
-launches on (torch's current stream).  Rooflines use algorithmic work:
+launches on (torch's current stream).  The default warmup (200 untimed
+steps, about 0.1 s of work) lets the GPU clock settle after the seconds of
+host-side input generation; with 3 warmup steps the first timed steps still
+run at a lower clock (about 25% slower on the 7B-layer prefill).  Rooflines use algorithmic work:
   prefill flops per token-head  (L+1)(d_qk+d_v) + 4 d_qk d_v + 4 d_qk
   prefill bytes per token-head  2(2 d_qk + 2 d_v) + 2 d_v + 8   (bf16 q,k,v,o~ in, h out, f32 gates)
   decode bytes per pair-step    8(d_qk d_v + d_qk + 1) + 2(2 d_qk + 2 d_v) + 8
@@ -181,8 +184,8 @@ def cpu_baseline(I, pairs_sample):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -255,7 +258,7 @@ def main():
     if not args.no_long:
         try:
             wl, msl, fl, bl, _keep = bench_prefill(torch, I, binding, "prefill_long_bf16",
-                                                  max(3, args.steps // 4), 1)
+                                                  max(3, args.steps // 4), max(1, args.warmup // 4))
             del _keep
             torch.cuda.empty_cache()
             kcl, nsl = binding.schedule(wl.B, wl.H, wl.T, wl.d_qk, wl.d_v, wl.chunk, binding.BF16)

@@ -61,12 +61,13 @@ struct WsCfg {
     static_assert(QG >= 8, "swizzle needs 8 granules per row");
 };
 
-// Row swizzles of the 16-byte granules of the Q and K tiles.  Two kinds of
-// read must spread over the LDS banks:
-//  * fragment reads: 16 consecutive rows, one whole granule each, at the same
-//    logical granule;
-//  * transpose reads of K: rows 8 g + (0..3), 8-byte halves of four
-//    consecutive logical granules 4 a + (0..3), all at the same half.
+// Row swizzles of the 16-byte granules of the Q, K and V tiles.  Two kinds
+// of read must spread over the LDS banks:
+//  * fragment reads (Q, K): 16 consecutive rows, one whole granule each, at
+//    the same logical granule;
+//  * transpose reads (K, V): four rows 4 g + (0..3) or 8 g + (0..3), 8-byte
+//    halves of four consecutive logical granules 4 a + (0..3), all at the
+//    same half.
 // With 16 or more granules per row (rows a multiple of 256 bytes apart, so a
 // granule's banks depend on its position only) swzt16 swaps the two 2-bit
 // digits of row mod 16: a bijection of row mod 16 (fragment reads), and rows
@@ -117,12 +118,14 @@ __device__ __forceinline__ void split8_pk(const float *x, const SplitMasks &m, b
     lo = bf16x8{l[0][0], l[0][1], l[1][0], l[1][1], l[2][0], l[2][1], l[3][0], l[3][1]};
 }
 
-// Granules per row of a tile, and whether it is a Q/K tile (swizzled with
-// swz16 from 16 granules per row) or a V tile (swz8).
-template <int G, bool QK>
-struct TileGranules : std::integral_constant<int, G> {
-    static constexpr bool qk_tile = QK;
-};
+// Swizzle of a tile with GPR granules per row (Q, K and V tiles alike).
+template <int GPR>
+__device__ __forceinline__ int tswz(int r) {
+    if constexpr (GPR >= 16)
+        return swzt16(r);
+    else
+        return swzt8(r);
+}
 
 // Workgroup barrier after this wavefront's LDS accesses have completed and at
 // most VM of its vector-memory operations are outstanding (they complete in
@@ -142,6 +145,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     constexpr int L = Cfg::L, LP = L, BV = Cfg::BV, NSW = Cfg::NSW, NT = Cfg::NT;
     constexpr int NAT = Cfg::NAT, NKS = Cfg::NKS, NCT = Cfg::NCT, QG = Cfg::QG, VG = Cfg::VG;
     constexpr int GTF = Cfg::GTF;
+    constexpr int NHS = NCT / 2;  // 16-byte h stores (and output-gate loads) per lane per chunk
     constexpr float kRenorm = 8.6736174e-19f;  // 2^-60: renormalise the lazy state scale below this
 
     __shared__ __attribute__((aligned(16))) bf16 Qs[L * DKP];
@@ -200,7 +204,12 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
         ns = a.n0 + (size_t)bh * dk;
         m_prev = a.m0[bh];
     }
-    const int scol = col0 + 32 * s + l16;  // state column of this lane (tile bt adds 16 bt)
+    // Value columns.  Row i = 4 g + r of a 16-column tile cb (V^T fragments,
+    // read-out and output accumulators) and column i of C' tile bt = cb - 2 s
+    // stand for value column 32 (cb / 2) + 8 g + 4 (cb % 2) + r: tiles 2 m
+    // and 2 m + 1 together give each lane group 8 consecutive columns, so h
+    // and the output gate move 16 bytes per lane.
+    const int scol = col0 + 32 * s + 8 * te + tq;  // state column of this lane (tile bt adds 4 bt)
     // Row i = 4 g4 + r of the 16-row C' tile at holds d_qk index
     // 32 (at / 2) + 8 g4 + 4 (at % 2) + r: tiles 2 kk and 2 kk + 1 together give
     // each lane group 8 consecutive d_qk indices, the k slots of one whole Q
@@ -213,7 +222,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
         for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Cr[at][bt][r] = (is_state && Cs) ? Cs[(size_t)crow(at, r) * dv + scol + 16 * bt] : 0.0f;
+                Cr[at][bt][r] = (is_state && Cs) ? Cs[(size_t)crow(at, r) * dv + scol + 4 * bt] : 0.0f;
     for (int e = tid; e < DKP; e += Cfg::NTH) {
         const float x = ns ? ns[e] : 0.0f;
         nsh[e] = x;
@@ -223,36 +232,25 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     }
     float sigma = 1.0f;  // C' is held divided by sigma (state wavefronts)
 
-    // Q and K tiles are swizzled with swzt16 (swzt8 at 8 granules per row), V
-    // tiles with swz8.
-    auto qswz = [](int row) -> int {
-        if constexpr (QG >= 16)
-            return swzt16(row);
-        else
-            return swzt8(row);
-    };
+    auto qswz = [](int row) -> int { return tswz<QG>(row); };
     // ---- global -> LDS copies by the intra wavefronts.  Physical granule g
     // of a tile is (row, p) with p = g % gpr holding logical granule
     // p ^ swz(row); instruction k of wavefront s fills granules
     // [(k NSW + s) 64, +64), rows k RPI + const.  Rows past the segment end
     // are clamped to its last row (finite data; their gates zero them out).
     // copy_part issues instruction k of a tile copy, copy_tile all of them.
-    // gpr_c: granules per row of the tile; Q and K tiles (QG granules per
-    // row) use qswz, the V tile (VG granules per row) swz8 -- the tile kind
-    // follows the granule count type, QGc or VGc, not its value (they are
-    // equal for d_qk 128)
+    // gpr_c: granules per row of the tile (its swizzle follows from it).
     auto copy_part = [&](bf16 *dst, const bf16 *src, int ld, auto gpr_c, int tc, int k) {
-        constexpr int GPR = decltype(gpr_c)::value;
-        constexpr bool QK_TILE = decltype(gpr_c)::qk_tile;
-        constexpr int RPI = NSW * 64 / GPR;
+        constexpr unsigned GPR = decltype(gpr_c)::value;
+        constexpr unsigned RPI = NSW * 64 / GPR;
         static_assert((L * GPR) % (NSW * 64) == 0 && RPI % 8 == 0, "copy shape");
-        int ln = lane;
+        unsigned ln = lane;
         asm volatile("" : "+v"(ln));
-        const int pgr = s * 64 + ln;
-        const int row = k * RPI + pgr / GPR;
-        const int gl = (pgr % GPR) ^ (QK_TILE ? qswz(row) : swz8(row));
-        const int t = min(tc + row, t_end - 1);
-        __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)t * ld + gl * 8),
+        const unsigned pgr = (unsigned)s * 64u + ln;
+        const unsigned row = k * RPI + pgr / GPR;
+        const unsigned gl = (pgr % GPR) ^ (unsigned)tswz<GPR>((int)row);
+        const unsigned rc = min(row, (unsigned)(t_end - 1 - tc));  // tc < t_end
+        __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)tc * ld + (rc * (unsigned)ld + gl * 8u)),
                                          (lds_void *)(dst + (k * NSW + s) * 64 * 8), 16, 0, 0);
     };
     auto copy_tile = [&](bf16 *dst, const bf16 *src, int ld, auto gpr_c, int tc) {
@@ -261,8 +259,8 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
         for (int k = 0; k < NI; ++k) copy_part(dst, src, ld, gpr_c, tc, k);
     };
     static_assert(L * QG / (NSW * 64) == NKS, "one K or Q copy instruction per d_qk k-step");
-    using QGc = TileGranules<QG, true>;
-    using VGc = TileGranules<VG, false>;
+    using QGc = std::integral_constant<int, QG>;
+    using VGc = std::integral_constant<int, VG>;
 
     // ---- gates (first intra wavefront; one token per lane)
     constexpr int GW = NSW;
@@ -313,12 +311,12 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     auto qk_frag = [&](const bf16 *tilebase, int ks) -> bf16x8 {  // tilebase: row 16 t of the tile
         return *reinterpret_cast<const bf16x8 *>(tilebase + ((ks >> 2) << 7) + qkoff[ks & 3]);
     };
-    // Transpose reads of a 16-column block cb = 4 hi + lo of a swizzled tile:
-    // the swizzle touches the low three granule bits only, so the per-lane part
-    // of the offset depends on (row, lo) and hi adds 64 elements (8 granules).
-    auto tr_off = [&](auto gpr_c, int row, int lo) -> int {
-        constexpr int GPR = decltype(gpr_c)::value;
-        return row * GPR * 8 + (((2 * lo + (tq >> 1)) ^ swz8(row)) << 3) + 4 * (tq & 1);
+    // Transpose read of value-column tile cb of a V tile row: the lanes of
+    // column quad tq supply fragment rows 4 tq .. 4 tq + 3, value columns
+    // 32 (cb / 2) + 8 tq + 4 (cb % 2) + (0..3): half cb % 2 of logical granule
+    // 4 (cb / 2) + tq.  vtr_off gives the offset without the half.
+    auto vtr_off = [](int row, int m, int q) -> int {
+        return row * VG * 8 + (((4 * m + q) ^ tswz<VG>(row)) << 3);
     };
     // k index in the S accumulator order (V^T of V^T P^T): rows 32 js + 4 g4 + te (+16)
     const int prow0 = 4 * g4 + te, prow1 = prow0 + 16;
@@ -397,10 +395,6 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             int ln = lane;
             asm volatile("" : "+v"(ln));
             const int lte = (ln & 15) >> 2, ltq = ln & 3, lg4 = ln >> 4;
-            auto tr_off2 = [&](auto gpr_c, int row, int lo) -> int {
-                constexpr int GPR = decltype(gpr_c)::value;
-                return row * GPR * 8 + (((2 * lo + (ltq >> 1)) ^ swz8(row)) << 3) + 4 * (ltq & 1);
-            };
             const int krow0 = 8 * lg4 + lte, krow1 = krow0 + 4;
             // K^T row tile at: the lanes of column quad tq supply fragment rows
             // 4 tq .. 4 tq + 3, here d_qk 32 (at / 2) + 8 tq + 4 (at % 2) + (0..3):
@@ -429,12 +423,11 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                     }
                 }
                 bf16x8 bw[2];
+                const bf16 *vb = Vs + 32 * js * BV;
+                const int vo0 = vtr_off(krow0, s, ltq), vo1 = vtr_off(krow1, s, ltq);
 #pragma unroll
-                for (int bt = 0; bt < 2; ++bt) {
-                    const int cb = 2 * s + bt;
-                    const bf16 *vb = Vs + 32 * js * BV + 64 * (cb >> 2);
-                    const bf16x8 vv = cat8(tr_read(vb + tr_off2(VGc{}, krow0, cb & 3)),
-                                           tr_read(vb + tr_off2(VGc{}, krow1, cb & 3)));
+                for (int bt = 0; bt < 2; ++bt) {  // value-column tile 2 s + bt
+                    const bf16x8 vv = cat8(tr_read(vb + vo0 + 4 * bt), tr_read(vb + vo1 + 4 * bt));
 #pragma unroll
                     for (int e = 0; e < 8; ++e) bw[bt][e] = (bf16)((float)vv[e] * w8[e]);
                 }
@@ -492,7 +485,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                 for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        Cdst[(size_t)crow(at, r) * dv + scol + 16 * bt] = Cr[at][bt][r] * sigma;
+                        Cdst[(size_t)crow(at, r) * dv + scol + 4 * bt] = Cr[at][bt][r] * sigma;
             if (tile == 0 && wave == 0) {
                 float *ndst = a.nT + (size_t)bh * dk;
                 for (int e = lane; e < dk; e += 64) ndst[e] = nsh[e];
@@ -522,12 +515,12 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             // ---- phase 1: copy V(c); S, P of this token tile; next gate
             // table; copy K(c+1)
             copy_tile(Vs, vg, dv, VGc{}, tc);
-            uint2 orw[NCT];  // output-gate inputs
+            uint4 orw[NHS];  // output-gate inputs: value columns 32 m + 8 g4 .. +8
             {
                 const int t = min(tc + irow, t_end - 1);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    orw[ct] = *reinterpret_cast<const uint2 *>(og + (size_t)t * dv + 16 * ct + 4 * g4);
+                for (int m = 0; m < NHS; ++m)
+                    orw[m] = *reinterpret_cast<const uint4 *>(og + (size_t)t * dv + 32 * m + 8 * g4);
             }
             if (more && wave == GW) load_gates(c + 1);
             // S^T tiles (jt, it) for jt <= it, k-step outermost so each Q
@@ -589,7 +582,8 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             // before the K copy goes out (the opaque use keeps the compiler from
             // waiting for them later, together with the copies)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) asm volatile("" : "+v"(orw[ct].x), "+v"(orw[ct].y));
+            for (int m = 0; m < NHS; ++m)
+                asm volatile("" : "+v"(orw[m].x), "+v"(orw[m].y), "+v"(orw[m].z), "+v"(orw[m].w));
             if (more) copy_tile(Ks[(c + 1) & 1], kg, DKP, QGc{}, tc + L);
             // (X) V(c) landed (only the K copy may stay in flight)
             if (more)
@@ -599,11 +593,11 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             if (more) copy_tile(Qs, qg, DKP, QGc{}, tc + L);  // every reader of Q(c) is past X
 
             // ---- phase 2: O^T of this token tile = scaled read-out + V^T P^T; h
-            int vpo[4][2];  // V^T fragment offsets by (column tile & 3, read)
+            int vpo[NHS][2];  // V^T fragment offsets by (column tile / 2, read)
 #pragma unroll
-            for (int lo = 0; lo < 4; ++lo) {
-                vpo[lo][0] = tr_off(VGc{}, prow0, lo);
-                vpo[lo][1] = tr_off(VGc{}, prow1, lo);
+            for (int m = 0; m < NHS; ++m) {
+                vpo[m][0] = vtr_off(prow0, m, tq);
+                vpo[m][1] = vtr_off(prow1, m, tq);
             }
             f32x4 acc[NCT];
 #pragma unroll
@@ -614,8 +608,8 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                     const bf16x8 bp = cat8(Pb[2 * js], Pb[2 * js + 1]);
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) {
-                        const bf16 *vb = Vs + 32 * js * BV + 64 * (ct >> 2);
-                        const bf16x8 av = cat8(tr_read(vb + vpo[ct & 3][0]), tr_read(vb + vpo[ct & 3][1]));
+                        const bf16 *vb = Vs + 32 * js * BV + 4 * (ct & 1);
+                        const bf16x8 av = cat8(tr_read(vb + vpo[ct >> 1][0]), tr_read(vb + vpo[ct >> 1][1]));
                         acc[ct] = mfma(av, bp, acc[ct]);
                     }
                 }
@@ -630,20 +624,22 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             const int t = tc + irow2;
             if (t < t_end) {
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    const float ox[4] = {__uint_as_float(orw[ct].x << 16), __uint_as_float(orw[ct].x & 0xffff0000u),
-                                         __uint_as_float(orw[ct].y << 16), __uint_as_float(orw[ct].y & 0xffff0000u)};
-                    float y[4];
+                for (int m = 0; m < NHS; ++m) {
+                    const unsigned ow[4] = {orw[m].x, orw[m].y, orw[m].z, orw[m].w};
+                    bf16x8 hv;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        y[e] = acc[ct][e] * inv * __builtin_amdgcn_rcpf(1.0f + exp_e(-ox[e]));
-                    const bf16x4 hv = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
-                    *reinterpret_cast<bf16x4 *>(hg + (size_t)t * dv + 16 * ct + 4 * g4) = hv;
+                    for (int e = 0; e < 8; ++e) {
+                        const unsigned u = ow[e >> 1];
+                        const float ox = __uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16));
+                        const float a = acc[2 * m + (e >> 2)][e & 3];
+                        hv[e] = (bf16)(a * inv * __builtin_amdgcn_rcpf(1.0f + exp_e(-ox)));
+                    }
+                    *reinterpret_cast<bf16x8 *>(hg + (size_t)t * dv + 32 * m + 8 * g4) = hv;
                 }
             }
-            // (Y) K(c+1), Q(c+1) landed (only this chunk's h stores may stay in flight)
+            // (Y) K(c+1), Q(c+1) landed (only this chunk's NHS h stores may stay in flight)
             if (more)
-                role_sync<NCT>();
+                role_sync<NHS>();
             else
                 role_sync<0>();
         }
