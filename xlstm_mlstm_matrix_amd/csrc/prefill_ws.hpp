@@ -253,10 +253,39 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
         __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)tc * ld + (rc * (unsigned)ld + gl * 8u)),
                                          (lds_void *)(dst + (k * NSW + s) * 64 * 8), 16, 0, 0);
     };
-    auto copy_tile = [&](bf16 *dst, const bf16 *src, int ld, auto gpr_c, int tc) {
-        constexpr int NI = L * decltype(gpr_c)::value / (NSW * 64);
+    // Whole chunks: the per-lane part of instruction k's source offset is
+    // off[k % 2] plus a uniform (k - k % 2) RPI rows (the swizzle repeats
+    // every 16 rows, and 2 RPI is a multiple of 16), so a copy is a scalar
+    // base plus a 32-bit lane offset.  copy_offsets fills off[] once.
+    auto copy_offsets = [&](auto gpr_c, int ld, unsigned *off) {
+        constexpr unsigned GPR = decltype(gpr_c)::value;
+        constexpr unsigned RPI = NSW * 64 / GPR;
+        static_assert((2 * RPI) % 16 == 0, "swizzle period");
+        const unsigned pgr = (unsigned)s * 64u + (unsigned)lane;
 #pragma unroll
-        for (int k = 0; k < NI; ++k) copy_part(dst, src, ld, gpr_c, tc, k);
+        for (int k = 0; k < 2; ++k) {
+            const unsigned row = k * RPI + pgr / GPR;
+            off[k] = row * (unsigned)ld + ((pgr % GPR) ^ (unsigned)tswz<GPR>((int)row)) * 8u;
+        }
+    };
+    auto copy_tile = [&](bf16 *dst, const bf16 *src, int ld, auto gpr_c, int tc, const unsigned *off) {
+        constexpr int GPR = decltype(gpr_c)::value;
+        constexpr int NI = L * GPR / (NSW * 64), RPI = NSW * 64 / GPR;
+        if (tc + L <= t_end) {
+            const bf16 *base = src + (size_t)tc * ld;
+#pragma unroll
+            for (int k = 0; k < NI; ++k) {
+                // opaque per use: the compiler would otherwise hoist one 64-bit
+                // address per instruction out of the chunk loop
+                unsigned o = off[k & 1];
+                asm volatile("" : "+v"(o));
+                __builtin_amdgcn_global_load_lds((const void *)(base + (size_t)((k & ~1) * RPI) * ld + o),
+                                                 (lds_void *)(dst + (k * NSW + s) * 64 * 8), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NI; ++k) copy_part(dst, src, ld, gpr_c, tc, k);
+        }
     };
     static_assert(L * QG / (NSW * 64) == NKS, "one K or Q copy instruction per d_qk k-step");
     using QGc = std::integral_constant<int, QG>;
@@ -494,9 +523,12 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
         }
     } else {
         // ========================= intra wavefronts =========================
+        unsigned qko[2], vo[2];  // per-lane copy offsets of Q/K and V tiles
+        copy_offsets(QGc{}, DKP, qko);
+        copy_offsets(VGc{}, dv, vo);
         if (nchunks > 0) {
-            copy_tile(Qs, qg, DKP, QGc{}, t_begin);
-            copy_tile(Ks[0], kg, DKP, QGc{}, t_begin);
+            copy_tile(Qs, qg, DKP, QGc{}, t_begin, qko);
+            copy_tile(Ks[0], kg, DKP, QGc{}, t_begin, qko);
             if (wave == GW) {
                 load_gates(0);
                 gate_prep(m_prev, gt[0]);
@@ -514,7 +546,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
 
             // ---- phase 1: copy V(c); S, P of this token tile; next gate
             // table; copy K(c+1)
-            copy_tile(Vs, vg, dv, VGc{}, tc);
+            copy_tile(Vs, vg, dv, VGc{}, tc, vo);
             uint4 orw[NHS];  // output-gate inputs: value columns 32 m + 8 g4 .. +8
             {
                 const int t = min(tc + irow, t_end - 1);
@@ -584,13 +616,13 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
 #pragma unroll
             for (int m = 0; m < NHS; ++m)
                 asm volatile("" : "+v"(orw[m].x), "+v"(orw[m].y), "+v"(orw[m].z), "+v"(orw[m].w));
-            if (more) copy_tile(Ks[(c + 1) & 1], kg, DKP, QGc{}, tc + L);
+            if (more) copy_tile(Ks[(c + 1) & 1], kg, DKP, QGc{}, tc + L, qko);
             // (X) V(c) landed (only the K copy may stay in flight)
             if (more)
                 role_sync<NKS>();
             else
                 role_sync<0>();
-            if (more) copy_tile(Qs, qg, DKP, QGc{}, tc + L);  // every reader of Q(c) is past X
+            if (more) copy_tile(Qs, qg, DKP, QGc{}, tc + L, qko);  // every reader of Q(c) is past X
 
             // ---- phase 2: O^T of this token tile = scaled read-out + V^T P^T; h
             int vpo[NHS][2];  // V^T fragment offsets by (column tile / 2, read)
