@@ -1,14 +1,19 @@
 """Summaries of rocprofv3 output for the profiles/ folder (host-side text
 processing only; nothing here touches a GPU).
 
-    python -m xlstm_mlstm_matrix_amd.rocprof_summary stats  STATS_CSV TRACE_CSV OUT_MD "COMMAND"
+    python -m xlstm_mlstm_matrix_amd.rocprof_summary stats  STATS_CSV TRACE_CSV OUT_MD "COMMAND" [TAIL]
     python -m xlstm_mlstm_matrix_amd.rocprof_summary traffic NAME KERNEL_REGEX \
         FETCH_CSV WRITE_CSV OUT_DIR "FETCH_COMMAND" "WRITE_COMMAND"
+    python -m xlstm_mlstm_matrix_amd.rocprof_summary sq KERNEL_REGEX COUNTER_CSV OUT_MD "COMMAND"
 
 `stats` turns the kernel statistics of `rocprofv3 --kernel-trace --stats
 -f csv` into a markdown table, followed by the same durations split into runs
 of consecutive dispatches of one kernel (one benchmark line launches a kernel
-many times in a row; the same kernel in another line forms another run).  `traffic` reads two counter-collection CSVs
+many times in a row; the same kernel in another line forms another run),
+with the average of each run's last TAIL dispatches (default 100, the
+benchmark's timed steps; its untimed warmup steps come first).  `sq` turns a
+counter-collection CSV of SQ/GRBM counters into a table of medians per
+dispatch with derived utilisations.  `traffic` reads two counter-collection CSVs
 (`rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE`, KiB per dispatch) of a
 run that also executed the benchmark's 1 GiB streaming probe (`torch.neg`
 over 2^28 float32: 1 GiB read, 1 GiB written).  The probe's counter readings
@@ -84,7 +89,7 @@ def kernel_runs(trace_csv: str, min_len: int = 3):
     return [x for x in runs if len(x[2]) >= min_len]
 
 
-def stats(stats_csv: str, trace_csv: str, out_md: str, command: str) -> None:
+def stats(stats_csv: str, trace_csv: str, out_md: str, command: str, tail: int = 100) -> None:
     with open(stats_csv, newline="") as f:
         rows = list(csv.DictReader(f))
     lines = ["# Kernel trace statistics", "", "Command (repository root, one MI355X):", "",
@@ -96,10 +101,13 @@ def stats(stats_csv: str, trace_csv: str, out_md: str, command: str) -> None:
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
     lines += ["", "Runs of at least 3 consecutive dispatches of one kernel (in launch order):", "",
-              "| Kernel | First dispatch | Calls | Average (us) | Median (us) | Min (us) | Max (us) |",
-              "|---|---:|---:|---:|---:|---:|---:|"]
+              f"| Kernel | First dispatch | Calls | Average (us) | Average of last {tail} (us) | Median (us) "
+              "| Min (us) | Max (us) |",
+              "|---|---:|---:|---:|---:|---:|---:|---:|"]
     for name, first, ds in kernel_runs(trace_csv):
+        last = ds[-tail:]
         lines.append(f"| `{name}` | {first} | {len(ds)} | {statistics.mean(ds) / 1e3:.2f} | "
+                     f"{statistics.mean(last) / 1e3:.2f} | "
                      f"{statistics.median(ds) / 1e3:.2f} | {min(ds) / 1e3:.2f} | {max(ds) / 1e3:.2f} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -143,9 +151,48 @@ def traffic(name: str, kernel_regex: str, fetch_csv: str, write_csv: str, out_di
     return rec
 
 
+SQ_COUNTERS = ["GRBM_GUI_ACTIVE", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+               "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS"]
+N_SIMD, N_XCD = 256 * 4, 8  # MI355X: 256 compute units of 4 SIMDs, in 8 XCDs
+
+
+def sq(kernel_regex: str, counter_csv: str, out_md: str, command: str) -> None:
+    vals = {}
+    with open(counter_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            if re.search(kernel_regex, row["Kernel_Name"]):
+                key = (row["Counter_Name"], int(row["Dispatch_Id"]))
+                vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    per = {}
+    for (name, _), v in vals.items():
+        per.setdefault(name, []).append(v)
+    m = {k: statistics.median(v) for k, v in per.items()}
+    n = len(per.get("GRBM_GUI_ACTIVE", []))
+    lines = [f"# SQ counters of `{kernel_regex}`", "", "Command (repository root, one MI355X):", "",
+             "```", command, "```", "", f"Median over {n} dispatches (each value summed over the whole GPU):", "",
+             "| Counter | Value |", "|---|---:|"]
+    lines += [f"| {k} | {m[k]:.0f} |" for k in SQ_COUNTERS if k in m]
+    if all(k in m for k in SQ_COUNTERS):
+        cyc = m["GRBM_GUI_ACTIVE"] / N_XCD
+        other = m["SQ_INSTS_VALU"] - m["SQ_INSTS_MFMA"]
+        lines += ["", f"Derived ({N_SIMD // 4} compute units x 4 SIMDs, {N_XCD} XCDs):", "",
+                  f"- kernel length: GRBM_GUI_ACTIVE / {N_XCD} = {cyc:.0f} cycles",
+                  f"- MFMA busy per SIMD: SQ_VALU_MFMA_BUSY_CYCLES / {N_SIMD} / kernel cycles = "
+                  f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / N_SIMD / cyc * 100:.1f}%",
+                  f"- MFMA instructions: {m['SQ_INSTS_MFMA']:.0f} "
+                  f"({m['SQ_VALU_MFMA_BUSY_CYCLES'] / m['SQ_INSTS_MFMA']:.1f} busy cycles each)",
+                  f"- non-MFMA VALU instructions: {other:.0f} = {other / m['SQ_INSTS_MFMA']:.1f} per MFMA; at 4 "
+                  f"cycles per wave64 instruction {other * 4 / N_SIMD / cyc * 100:.1f}% of each SIMD's cycles",
+                  f"- LDS instructions: {m['SQ_INSTS_LDS']:.0f}", ""]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main(argv):
-    if len(argv) >= 1 and argv[0] == "stats" and len(argv) == 5:
-        stats(argv[1], argv[2], argv[3], argv[4])
+    if len(argv) >= 1 and argv[0] == "stats" and len(argv) in (5, 6):
+        stats(argv[1], argv[2], argv[3], argv[4], *(int(x) for x in argv[5:]))
+    elif len(argv) >= 1 and argv[0] == "sq" and len(argv) == 5:
+        sq(argv[1], argv[2], argv[3], argv[4])
     elif len(argv) >= 1 and argv[0] == "traffic" and len(argv) == 8:
         rec = traffic(*argv[1:])
         print(json.dumps({k: rec[k] for k in ("bytes_read_per_launch", "bytes_written_per_launch",
