@@ -57,9 +57,12 @@ def test_head_dims(dk, dv):
 
 @pytest.mark.parametrize("dk,dv", [(64, 128), (128, 256), (256, 128), (256, 384)])
 @pytest.mark.parametrize("with_state", [False, True])
-def test_chunk64_value_blocks(dk, dv, with_state):
+@pytest.mark.parametrize("variant", ["fused", "segscan"])
+def test_chunk64_value_blocks(dk, dv, with_state, variant):
     """Chunk 64 with d_v a multiple of 128 (128-column value blocks), each d_qk
-    in {64, 128, 256}, ragged T, from the zero state and from a random one."""
+    in {64, 128, 256}, ragged T, from the zero state and from a random one; one
+    pass, and the segmented schedule (2 segments at T=200: the state-only pass,
+    the combine with the initial state, the seeded output pass)."""
     w, d = case("prefill_7b_bf16", pairs=[(1, 1), (6, 3)], T=200, d_qk=dk, d_v=dv)
     if with_state:
         rng = np.random.default_rng(1000 + dk + dv)
@@ -67,8 +70,8 @@ def test_chunk64_value_blocks(dk, dv, with_state):
         d["C0"] = torch.from_numpy(rng.normal(0.0, 0.05, (P, dk, dv))).float()
         d["n0"] = torch.from_numpy(rng.normal(0.0, 0.05, (P, dk))).float()
         d["m0"] = torch.from_numpy(rng.uniform(-1.0, 1.0, P)).float()
-    PT.compare_fwd(PT.run_gpu_fwd(d, 64, variant="fused"), PT.run_oracle(d), "bf16",
-                   f"chunk 64 dk={dk} dv={dv} state={with_state}")
+    PT.compare_fwd(PT.run_gpu_fwd(d, 64, variant=variant), PT.run_oracle(d), "bf16",
+                   f"chunk 64 dk={dk} dv={dv} state={with_state} {variant}")
 
 
 @pytest.mark.parametrize("dk", [64, 128, 256])

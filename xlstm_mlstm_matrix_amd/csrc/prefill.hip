@@ -131,23 +131,29 @@ hipError_t bf16_by_shape(const FwdArgs &a, int chunk, int dkp, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-// role-split kernel: chunk 64, whole 128-column value blocks, full output pass
-template <int DKP>
+// role-split kernel: chunk 64, whole 128-column value blocks; the output pass
+// or (SO) the segment scan's state-only pass over all segments but the last
+template <int DKP, bool SO>
 hipError_t run_ws(const FwdArgs &a, hipStream_t s) {
     static_assert(WsCfg<DKP>::LDS_BYTES <= kLdsBudget, "LDS budget");
-    dim3 grid((unsigned)(a.BH * a.nseg * a.ntile)), block(WsCfg<DKP>::NTH);
-    hipLaunchKernelGGL((mlstm_ws_kernel<DKP>), grid, block, 0, s, a);
+    const int gseg = SO ? a.nseg - 1 : a.nseg;
+    dim3 grid((unsigned)(a.BH * gseg * a.ntile)), block(WsCfg<DKP>::NTH);
+    hipLaunchKernelGGL((mlstm_ws_kernel<DKP, SO>), grid, block, 0, s, a);
     return hipGetLastError();
+}
+template <bool SO>
+hipError_t ws_by_shape(const FwdArgs &a, int dkp, hipStream_t s) {
+    if (dkp == 256) return run_ws<256, SO>(a, s);
+    if (dkp == 128) return run_ws<128, SO>(a, s);
+    if (dkp == 64) return run_ws<64, SO>(a, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_fused(const FwdArgs &a, int io_bf16, int chunk, int state_only, hipStream_t s) {
     const int dkp = prefill_dkp(a.dk);
     const int bv = prefill_bv(io_bf16, a.dk, a.dv, chunk);
-    if (io_bf16 && !state_only && chunk == 64 && bv == 128 && bf16_fast_path(chunk, a.dk, a.dv)) {
-        if (dkp == 256) return run_ws<256>(a, s);
-        if (dkp == 128) return run_ws<128>(a, s);
-        if (dkp == 64) return run_ws<64>(a, s);
-    }
+    if (io_bf16 && chunk == 64 && bv == 128 && bf16_fast_path(chunk, a.dk, a.dv))
+        return state_only ? ws_by_shape<true>(a, dkp, s) : ws_by_shape<false>(a, dkp, s);
     if (io_bf16 && bf16_fast_path(chunk, a.dk, a.dv)) {
         if (bv == 128)
             return state_only ? bf16_by_shape<128, true>(a, chunk, dkp, s)

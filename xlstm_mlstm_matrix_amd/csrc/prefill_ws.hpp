@@ -139,7 +139,12 @@ __device__ __forceinline__ void role_sync() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int DKP>
+// SO (state only): the segment scan's first pass -- each segment's local
+// state from the zero state, no output.  The state wavefronts run the update
+// alone; the intra wavefronts copy K and V (both double buffered, the second V
+// buffer in the unused exchange area) and prepare the gates, one barrier per
+// chunk.
+template <int DKP, bool SO>
 __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     using Cfg = WsCfg<DKP>;
     constexpr int L = Cfg::L, LP = L, BV = Cfg::BV, NSW = Cfg::NSW, NT = Cfg::NT;
@@ -169,10 +174,11 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     const int nwg = gridDim.x;
     int logical = blockIdx.x;
     if ((nwg & 7) == 0) logical = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int gseg = SO ? a.nseg - 1 : a.nseg;  // segments this launch covers
     const int tile = logical % a.ntile;
     const int rest = logical / a.ntile;
-    const int seg = rest % a.nseg;
-    const int bh = rest / a.nseg;
+    const int seg = rest % gseg;
+    const int bh = rest / gseg;
 
     const int dk = a.dk, dv = a.dv, T = a.T;  // here dk == DKP and dv is a multiple of BV
     const int t_begin = seg * a.seg_len;
@@ -194,7 +200,9 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     const size_t rec = seg_state_floats(dk, dv);
     const float *Cs = nullptr, *ns = nullptr;
     float m_prev = 0.0f;
-    if (a.seg_in) {
+    if (SO) {
+        m_prev = -1e30f;  // no past: the first chunk's stabilizer comes from its own gates
+    } else if (a.seg_in) {
         const float *r = a.seg_in + ((size_t)bh * a.nseg + seg) * rec;
         Cs = r;
         ns = r + (size_t)dk * dv;
@@ -291,6 +299,10 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     using QGc = std::integral_constant<int, QG>;
     using VGc = std::integral_constant<int, VG>;
 
+    // V tile of chunk c (state-only: double buffered, odd chunks in Xch)
+    auto vbuf = [&](int c) -> bf16 * { return (SO && (c & 1)) ? reinterpret_cast<bf16 *>(&Xch[0][0][0]) : Vs; };
+    static_assert(sizeof(Xch) >= sizeof(Vs), "second V buffer");
+
     // ---- gates (first intra wavefront; one token per lane)
     constexpr int GW = NSW;
     float gf = 0.0f, gi = -INFINITY;
@@ -357,8 +369,117 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     if (is_state) {
         // ========================= state wavefronts =========================
         const SplitMasks smask = split_masks();
+        // C'/sigma' += K^T ((w/sigma') (x) V) with sigma' = sigma * decay, n'
+        // likewise (true scale): the update with the chunk whose K and V tiles
+        // and gate table are given
+        auto update = [&](const bf16 *K, const bf16 *Vt, const float *G, float s_last) {
+                // ---- phase 2: C'/sigma' += K^T ((w/sigma') (x) V), sigma' =
+                // sigma * decay; n' likewise (true scale)
+                sigma *= s_last;
+                if (sigma < kRenorm) {  // uniform: fold sigma back into the held state
+    #pragma unroll
+                    for (int at = 0; at < NAT; ++at)
+    #pragma unroll
+                        for (int bt = 0; bt < 2; ++bt) Cr[at][bt] *= sigma;
+                    sigma = 1.0f;
+                }
+                const float rsig = __builtin_amdgcn_rcpf(sigma);
+                // K^T fragment offsets by (row tile & 3, read), recomputed here from
+                // an opaque copy of the lane index so they are not held across the loop
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const int lte = (ln & 15) >> 2, ltq = ln & 3, lg4 = ln >> 4;
+                const int krow0 = 8 * lg4 + lte, krow1 = krow0 + 4;
+                // K^T row tile at: the lanes of column quad tq supply fragment rows
+                // 4 tq .. 4 tq + 3, here d_qk 32 (at / 2) + 8 tq + 4 (at % 2) + (0..3):
+                // half at % 2 of logical granule 4 (at / 2) + tq of rows krow0 / krow1
+                const int kb0 = krow0 * QG * 8, kb1 = krow1 * QG * 8;
+                const int kx0 = qswz(krow0) ^ ltq, kx1 = qswz(krow1) ^ ltq;
+                auto kt_frag = [&](const bf16 *rowblock, int at) -> bf16x8 {
+                    const int h = 4 * (at & 1), g = 4 * (at >> 1);
+                    return cat8(tr_read(rowblock + kb0 + h + ((g ^ kx0) << 3)),
+                                tr_read(rowblock + kb1 + h + ((g ^ kx1) << 3)));
+                };
+                f32x4 nacc[NAT / 4];
+    #pragma unroll
+                for (int x = 0; x < NAT / 4; ++x) nacc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                for (int js = 0; js < L / 32; ++js) {
+                    const bf16 *k0 = K + 32 * js * DKP;
+                    float w8[8];
+                    {
+                        const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&G[4 * LP + 32 * js + 8 * g4]);
+                        const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&G[4 * LP + 32 * js + 8 * g4 + 4]);
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            w8[e] = w0[e] * rsig;
+                            w8[e + 4] = w1[e] * rsig;
+                        }
+                    }
+                    bf16x8 bw[2];
+                    const bf16 *vb = Vt + 32 * js * BV;
+                    const int vo0 = vtr_off(krow0, s, ltq), vo1 = vtr_off(krow1, s, ltq);
+    #pragma unroll
+                    for (int bt = 0; bt < 2; ++bt) {  // value-column tile 2 s + bt
+                        const bf16x8 vv = cat8(tr_read(vb + vo0 + 4 * bt), tr_read(vb + vo1 + 4 * bt));
+    #pragma unroll
+                        for (int e = 0; e < 8; ++e) bw[bt][e] = (bf16)((float)vv[e] * w8[e]);
+                    }
+                    // w (hi, lo) in every column of the operand: every lane gets K^T w
+                    const bf16 *W2 = reinterpret_cast<const bf16 *>(&G[5 * LP]);
+                    const bf16x8 bnh = *reinterpret_cast<const bf16x8 *>(W2 + 32 * js + 8 * g4);
+                    const bf16x8 bnl = *reinterpret_cast<const bf16x8 *>(W2 + LP + 32 * js + 8 * g4);
+                    // K^T fragments fetched two row tiles ahead (ring of three)
+                    constexpr int AHEAD = 2;
+                    bf16x8 ak[AHEAD + 1];
+    #pragma unroll
+                    for (int u = 0; u < AHEAD; ++u) ak[u] = kt_frag(k0, u);
+    #pragma unroll
+                    for (int at = 0; at < NAT; ++at) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (at + AHEAD < NAT) ak[(at + AHEAD) % (AHEAD + 1)] = kt_frag(k0, at + AHEAD);
+                        const bf16x8 &a0 = ak[at % (AHEAD + 1)];
+    #pragma unroll
+                        for (int bt = 0; bt < 2; ++bt) Cr[at][bt] = mfma(a0, bw[bt], Cr[at][bt]);
+                        if ((at & 3) == s) {
+                            nacc[at >> 2] = mfma(a0, bnh, nacc[at >> 2]);
+                            nacc[at >> 2] = mfma(a0, bnl, nacc[at >> 2]);
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // n' <- decay n' + K^T w for row tiles s + 4x (read after barrier Y)
+                if (l16 == 0) {
+    #pragma unroll
+                    for (int x = 0; x < NAT / 4; ++x) {
+                        const int r0 = crow(s + 4 * x, 0);
+                        f32x4 *np = reinterpret_cast<f32x4 *>(&nsh[r0]);
+                        const f32x4 nn = *np * s_last + nacc[x];
+                        *np = nn;
+                        bf16x4 hi, lo;
+    #pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            hi[r] = (bf16)nn[r];
+                            lo[r] = (bf16)(nn[r] - (float)hi[r]);
+                        }
+                        *reinterpret_cast<bf16x4 *>(&nhl[0][r0]) = hi;
+                        *reinterpret_cast<bf16x4 *>(&nhl[1][r0]) = lo;
+                    }
+                }
+        };
         role_sync<63>();
-        for (int c = 0; c < nchunks; ++c) {
+        float g_total = 0.0f;  // sum of the segment's log forget gates (state-only)
+        if constexpr (SO) {
+            for (int c = 0; c < nchunks; ++c) {
+                const float *G = gt[c & 1];
+                const float m_next = G[6 * LP + 0], s_last = G[6 * LP + 1];
+                g_total += G[6 * LP + 2];
+                update(Ks[c & 1], vbuf(c), G, s_last);
+                m_prev = m_next;
+                role_sync<63>();  // K(c+1), V(c+1), gates of c+1 landed; K(c), V(c) free
+            }
+        }
+        for (int c = 0; c < (SO ? 0 : nchunks); ++c) {
             const float *G = gt[c & 1];
             const float m_next = G[6 * LP + 0], s_last = G[6 * LP + 1];
 
@@ -407,107 +528,26 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             }
             role_sync<63>();  // (X) read-out in LDS; V(c) landed; Q(c) free
 
-            // ---- phase 2: C'/sigma' += K^T ((w/sigma') (x) V), sigma' =
-            // sigma * decay; n' likewise (true scale)
-            sigma *= s_last;
-            if (sigma < kRenorm) {  // uniform: fold sigma back into the held state
-#pragma unroll
-                for (int at = 0; at < NAT; ++at)
-#pragma unroll
-                    for (int bt = 0; bt < 2; ++bt) Cr[at][bt] *= sigma;
-                sigma = 1.0f;
-            }
-            const float rsig = __builtin_amdgcn_rcpf(sigma);
-            const bf16 *K = Ks[c & 1];
-            // K^T fragment offsets by (row tile & 3, read), recomputed here from
-            // an opaque copy of the lane index so they are not held across the loop
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            const int lte = (ln & 15) >> 2, ltq = ln & 3, lg4 = ln >> 4;
-            const int krow0 = 8 * lg4 + lte, krow1 = krow0 + 4;
-            // K^T row tile at: the lanes of column quad tq supply fragment rows
-            // 4 tq .. 4 tq + 3, here d_qk 32 (at / 2) + 8 tq + 4 (at % 2) + (0..3):
-            // half at % 2 of logical granule 4 (at / 2) + tq of rows krow0 / krow1
-            const int kb0 = krow0 * QG * 8, kb1 = krow1 * QG * 8;
-            const int kx0 = qswz(krow0) ^ ltq, kx1 = qswz(krow1) ^ ltq;
-            auto kt_frag = [&](const bf16 *rowblock, int at) -> bf16x8 {
-                const int h = 4 * (at & 1), g = 4 * (at >> 1);
-                return cat8(tr_read(rowblock + kb0 + h + ((g ^ kx0) << 3)),
-                            tr_read(rowblock + kb1 + h + ((g ^ kx1) << 3)));
-            };
-            f32x4 nacc[NAT / 4];
-#pragma unroll
-            for (int x = 0; x < NAT / 4; ++x) nacc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int js = 0; js < L / 32; ++js) {
-                const bf16 *k0 = K + 32 * js * DKP;
-                float w8[8];
-                {
-                    const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&G[4 * LP + 32 * js + 8 * g4]);
-                    const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&G[4 * LP + 32 * js + 8 * g4 + 4]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        w8[e] = w0[e] * rsig;
-                        w8[e + 4] = w1[e] * rsig;
-                    }
-                }
-                bf16x8 bw[2];
-                const bf16 *vb = Vs + 32 * js * BV;
-                const int vo0 = vtr_off(krow0, s, ltq), vo1 = vtr_off(krow1, s, ltq);
-#pragma unroll
-                for (int bt = 0; bt < 2; ++bt) {  // value-column tile 2 s + bt
-                    const bf16x8 vv = cat8(tr_read(vb + vo0 + 4 * bt), tr_read(vb + vo1 + 4 * bt));
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) bw[bt][e] = (bf16)((float)vv[e] * w8[e]);
-                }
-                // w (hi, lo) in every column of the operand: every lane gets K^T w
-                const bf16 *W2 = reinterpret_cast<const bf16 *>(&G[5 * LP]);
-                const bf16x8 bnh = *reinterpret_cast<const bf16x8 *>(W2 + 32 * js + 8 * g4);
-                const bf16x8 bnl = *reinterpret_cast<const bf16x8 *>(W2 + LP + 32 * js + 8 * g4);
-                // K^T fragments fetched two row tiles ahead (ring of three)
-                constexpr int AHEAD = 2;
-                bf16x8 ak[AHEAD + 1];
-#pragma unroll
-                for (int u = 0; u < AHEAD; ++u) ak[u] = kt_frag(k0, u);
-#pragma unroll
-                for (int at = 0; at < NAT; ++at) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (at + AHEAD < NAT) ak[(at + AHEAD) % (AHEAD + 1)] = kt_frag(k0, at + AHEAD);
-                    const bf16x8 &a0 = ak[at % (AHEAD + 1)];
-#pragma unroll
-                    for (int bt = 0; bt < 2; ++bt) Cr[at][bt] = mfma(a0, bw[bt], Cr[at][bt]);
-                    if ((at & 3) == s) {
-                        nacc[at >> 2] = mfma(a0, bnh, nacc[at >> 2]);
-                        nacc[at >> 2] = mfma(a0, bnl, nacc[at >> 2]);
-                    }
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // n' <- decay n' + K^T w for row tiles s + 4x (read after barrier Y)
-            if (l16 == 0) {
-#pragma unroll
-                for (int x = 0; x < NAT / 4; ++x) {
-                    const int r0 = crow(s + 4 * x, 0);
-                    f32x4 *np = reinterpret_cast<f32x4 *>(&nsh[r0]);
-                    const f32x4 nn = *np * s_last + nacc[x];
-                    *np = nn;
-                    bf16x4 hi, lo;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        hi[r] = (bf16)nn[r];
-                        lo[r] = (bf16)(nn[r] - (float)hi[r]);
-                    }
-                    *reinterpret_cast<bf16x4 *>(&nhl[0][r0]) = hi;
-                    *reinterpret_cast<bf16x4 *>(&nhl[1][r0]) = lo;
-                }
-            }
+            update(Ks[c & 1], Vs, G, s_last);
             m_prev = m_next;
             role_sync<63>();  // (Y) Q(c+1), K(c+1) landed; n' visible; V(c), Xch, q.n' free
         }
 
-        // ---- state out (n' and m from wavefront 0 of column block 0)
-        if (a.CT && seg == a.nseg - 1) {
-            float *Cdst = a.CT + (size_t)bh * dk * dv;
+        // ---- state out (n' and m from wavefront 0 of column block 0): the
+        // final state, or (state-only) the segment's local state record
+        float *Cdst = nullptr, *ndst = nullptr, *mdst = nullptr;
+        if (SO) {
+            float *r = a.seg_out + ((size_t)bh * (a.nseg - 1) + seg) * rec;
+            Cdst = r;
+            ndst = r + (size_t)dk * dv;
+            mdst = ndst + dk;
+            if (tile == 0 && wave == 0 && lane == 0) mdst[1] = g_total;
+        } else if (a.CT && seg == a.nseg - 1) {
+            Cdst = a.CT + (size_t)bh * dk * dv;
+            ndst = a.nT + (size_t)bh * dk;
+            mdst = a.mT + bh;
+        }
+        if (Cdst) {
 #pragma unroll
             for (int at = 0; at < NAT; ++at)
 #pragma unroll
@@ -516,9 +556,8 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                     for (int r = 0; r < 4; ++r)
                         Cdst[(size_t)crow(at, r) * dv + scol + 4 * bt] = Cr[at][bt][r] * sigma;
             if (tile == 0 && wave == 0) {
-                float *ndst = a.nT + (size_t)bh * dk;
                 for (int e = lane; e < dk; e += 64) ndst[e] = nsh[e];
-                if (lane == 0) a.mT[bh] = m_prev;
+                if (lane == 0) mdst[0] = m_prev;
             }
         }
     } else {
@@ -526,6 +565,28 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
         unsigned qko[2], vo[2];  // per-lane copy offsets of Q/K and V tiles
         copy_offsets(QGc{}, DKP, qko);
         copy_offsets(VGc{}, dv, vo);
+        if constexpr (SO) {
+            if (nchunks > 0) {
+                copy_tile(Ks[0], kg, DKP, QGc{}, t_begin, qko);
+                copy_tile(vbuf(0), vg, dv, VGc{}, t_begin, vo);
+                if (wave == GW) {
+                    load_gates(0);
+                    gate_prep(m_prev, gt[0]);
+                }
+            }
+            role_sync<0>();
+            for (int c = 0; c < nchunks; ++c) {
+                if (c + 1 < nchunks) {
+                    const int tn = t_begin + (c + 1) * L;
+                    if (wave == GW) load_gates(c + 1);
+                    copy_tile(Ks[(c + 1) & 1], kg, DKP, QGc{}, tn, qko);
+                    copy_tile(vbuf(c + 1), vg, dv, VGc{}, tn, vo);
+                    if (wave == GW) gate_prep(gt[c & 1][6 * LP + 0], gt[(c + 1) & 1]);
+                }
+                role_sync<0>();  // K(c+1), V(c+1) landed, gates of c+1 written
+            }
+            return;
+        }
         if (nchunks > 0) {
             copy_tile(Qs, qg, DKP, QGc{}, t_begin, qko);
             copy_tile(Ks[0], kg, DKP, QGc{}, t_begin, qko);
