@@ -1,4 +1,5 @@
-"""Float64 CPU oracle of the mLSTM cell forward pass (test infrastructure).
+"""Float64 CPU oracle of the mLSTM cell forward and backward passes (test
+infrastructure).
 
 Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg may import this package.  It wraps ``mlstm_ref.c`` (the plain sequential
@@ -18,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "mlstm_ref.c")
 LIB = os.path.join(HERE, "libmlstm_ref.so")
 
-__all__ = ["build", "load", "forward", "Oracle", "SRC", "LIB"]
+__all__ = ["build", "load", "forward", "backward", "Oracle", "SRC", "LIB"]
 
 
 def build(src: str = SRC, out: str = LIB, extra_flags=()) -> str:
@@ -42,6 +43,10 @@ class Oracle:
         f.argtypes = [dp] * 13 + [ctypes.c_long] * 4 + [ctypes.c_int]
         f.restype = ctypes.c_int
         self._f = f
+        b = self.lib.mlstm_ref_backward
+        b.argtypes = [dp] * 19 + [ctypes.c_long] * 4 + [ctypes.c_int]
+        b.restype = ctypes.c_int
+        self._b = b
 
     def forward(self, q, k, v, i_pre, f_pre, o_pre, C0=None, n0=None, m0=None,
                 threads: int = 0):
@@ -73,6 +78,32 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"mlstm_ref_forward failed with code {rc}")
         return h, C, n, m
+
+    def backward(self, q, k, v, i_pre, f_pre, o_pre, dh, C0=None, n0=None, m0=None,
+                 threads: int = 0):
+        """Gradients of sum(dh * h) (dh: [P, T, d_v]) with respect to every
+        input and the initial state: returns (dq, dk, dv, di, df, do, dC0,
+        dn0, dm0) as float64 numpy arrays (the initial-state gradients are
+        those of the zero state when none is given)."""
+        q, k, v, i_pre, f_pre, o_pre, dh = (_f64(x) for x in (q, k, v, i_pre, f_pre, o_pre, dh))
+        P, T, dk = q.shape
+        dv = v.shape[2]
+        assert k.shape == (P, T, dk) and v.shape == (P, T, dv) and o_pre.shape == (P, T, dv)
+        assert i_pre.shape == (P, T) and f_pre.shape == (P, T) and dh.shape == (P, T, dv)
+        have = [x is not None for x in (C0, n0, m0)]
+        if any(have) and not all(have):
+            raise ValueError("initial state must be given completely or not at all")
+        if all(have):
+            C0, n0, m0 = _f64(C0), _f64(n0), _f64(m0)
+            assert C0.shape == (P, dk, dv) and n0.shape == (P, dk) and m0.shape == (P,)
+        out = [np.empty((P, T, dk)), np.empty((P, T, dk)), np.empty((P, T, dv)), np.empty((P, T)),
+               np.empty((P, T)), np.empty((P, T, dv)), np.empty((P, dk, dv)), np.empty((P, dk)),
+               np.empty((P,))]
+        rc = self._b(_p(q), _p(k), _p(v), _p(i_pre), _p(f_pre), _p(o_pre), _p(C0), _p(n0), _p(m0), _p(dh),
+                     *(_p(x) for x in out), P, T, dk, dv, int(threads))
+        if rc != 0:
+            raise RuntimeError(f"mlstm_ref_backward failed with code {rc}")
+        return tuple(out)
 
 
 def _f64(x):
@@ -109,3 +140,8 @@ def load() -> Oracle:
 def forward(*args, **kw):
     """``load().forward(...)``."""
     return load().forward(*args, **kw)
+
+
+def backward(*args, **kw):
+    """``load().backward(...)``."""
+    return load().backward(*args, **kw)
