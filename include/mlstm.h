@@ -1,5 +1,6 @@
 /*
- * mlstm.h -- C ABI of the MI355X (gfx950) mLSTM cell forward library.
+ * mlstm.h -- C ABI of the MI355X (gfx950) mLSTM cell library (forward and
+ * backward).
  *
  * The operation is the mLSTM cell of xLSTM: exponential input and forget
  * gates in log space with the stabilizer m_t = max(f~_t + m_{t-1}, i~_t)
@@ -16,9 +17,10 @@
  * which equals the unstabilized formula exactly.  f~ is the log of the forget
  * gate: the library applies exp to it and nothing else (no sigmoid).
  *
- * Two entry points compute it:
+ * Three entry points compute it or its gradients:
  *   mlstm_fwd_chunkwise -- a whole sequence, chunkwise-parallel (prefill);
- *   mlstm_step          -- one token of the recurrence (decode).
+ *   mlstm_step          -- one token of the recurrence (decode);
+ *   mlstm_bwd_chunkwise -- gradients of a whole sequence (training).
  *
  * Conventions shared by every call:
  *  - All tensor pointers are DEVICE pointers (HIP memory on the current
@@ -168,6 +170,48 @@ mlstm_status_t mlstm_step(const void *q, const void *k, const void *v,
                           const float *C_in, const float *n_in, const float *m_in,
                           void *h, float *C_out, float *n_out, float *m_out,
                           int B, int H, int d_qk, int d_v, mlstm_dtype_t io, void *stream);
+
+/*
+ * Gradients of a loss L with respect to every input of mlstm_fwd_chunkwise,
+ * given dL/dh (training).  Reverse mode of the same recurrence: the
+ * read-out C q / max(|n^T q|, 1) does not depend on the stabilizer, so m is
+ * not differentiated, and where |n'^T q| is at the floor e^{-m} the
+ * normalizer gets no gradient (the floor's branch).  The call recomputes the
+ * forward's states (one pass storing the state at every 32-token chunk
+ * start in the workspace) and then runs backwards over the chunks.
+ *
+ *  q, k, v, i_pre, f_pre, o_pre, C0, n0, m0   as for mlstm_fwd_chunkwise
+ *            (the forward's inputs; C0, n0, m0 all NULL for the zero state)
+ *  dh        [B, H, T, d_v]   io dtype   dL/dh
+ *  dq, dk    [B, H, T, d_qk]  float32    dL/dq, dL/dk (written)
+ *  dv, d_o   [B, H, T, d_v]   float32    dL/dv, dL/do~ (written)
+ *  d_i, d_f  [B, H, T]        float32    dL/di~, dL/df~ (written)
+ *  dC0, dn0, dm0  [B, H, d_qk, d_v], [B, H, d_qk], [B, H] float32: dL with
+ *            respect to the initial state (of the zero state when C0, n0,
+ *            m0 are NULL), or all three NULL when not wanted.
+ *  chunk     as for mlstm_fwd_chunkwise (accepted for symmetry: this
+ *            version always works in chunks of 32 tokens, which the
+ *            chunkwise form allows without changing the result).
+ *  workspace device buffer of at least mlstm_bwd_chunkwise_workspace_size
+ *            bytes; contents on entry are irrelevant.
+ *
+ * Gradients are float32 for either io dtype.  This version keeps one
+ * sequence's tiles and carried gradient in one compute unit: 1 <= d_qk,
+ * d_v <= 64 (multiples of 16); larger heads return MLSTM_ERR_UNSUPPORTED.
+ * Errors as for mlstm_fwd_chunkwise; every output must overlap no input, no
+ * other output and no workspace (MLSTM_ERR_ALIAS).
+ */
+mlstm_status_t mlstm_bwd_chunkwise_workspace_size(int B, int H, int T, int d_qk, int d_v,
+                                                  int chunk, mlstm_dtype_t io, size_t *bytes);
+mlstm_status_t mlstm_bwd_chunkwise(const void *q, const void *k, const void *v,
+                                   const float *i_pre, const float *f_pre, const void *o_pre,
+                                   const float *C0, const float *n0, const float *m0,
+                                   const void *dh, float *dq, float *dk, float *dv,
+                                   float *d_i, float *d_f, float *d_o,
+                                   float *dC0, float *dn0, float *dm0,
+                                   int B, int H, int T, int d_qk, int d_v, int chunk,
+                                   mlstm_dtype_t io, void *workspace, size_t workspace_bytes,
+                                   void *stream);
 
 #ifdef __cplusplus
 }

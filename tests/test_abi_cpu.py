@@ -37,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s+(mlstm_\w+)", out))
@@ -215,3 +215,66 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 4, 16)
     with pytest.raises(Exception):
         B.fwd_chunkwise(x, x, x, torch.zeros(1, 1, 4), torch.zeros(1, 1, 4), x)
+
+
+# ---- backward: host-side validation only (every call below returns before any
+# device work; the fake addresses are never dereferenced)
+
+def bws(*args):
+    n = ctypes.c_size_t(12345)
+    s = B.lib().mlstm_bwd_chunkwise_workspace_size(*args, ctypes.byref(n))
+    return s, n.value
+
+
+def test_bwd_workspace_query(lib):
+    s, n = bws(2, 3, 70, 64, 48, 32, B.F32)
+    # the state (C', n', m) at every 32-token chunk start of every pair
+    assert s == OK and n == 6 * 3 * (64 * 48 + 64 + 1) * 4
+    assert bws(2, 3, 70, 128, 64, 32, B.F32)[0] == UNSUP     # d_qk above this version's 64
+    assert bws(2, 3, 70, 64, 80, 32, B.BF16)[0] == UNSUP     # d_v above 64
+    assert bws(2, 3, 70, 24, 64, 32, B.F32)[0] == UNSUP      # not a multiple of 16
+    assert bws(2, 3, 70, 64, 64, 48, B.F32)[0] == UNSUP      # chunk
+    assert bws(2, 3, 0, 64, 64, 32, B.F32)[0] == SHAPE
+    assert bws(2, 3, 70, 64, 64, 32, 5)[0] == UNSUP          # dtype
+    assert B.lib().mlstm_bwd_chunkwise_workspace_size(1, 1, 64, 64, 64, 32, 0, None) == NULL
+
+
+def bwd_call(a, **over):
+    x = dict(a)
+    x.update(over)
+    B_, H, T, dk, dv, chunk, io = x["dims"]
+    return B.lib().mlstm_bwd_chunkwise(
+        x["q"], x["k"], x["v"], x["i"], x["f"], x["o"], x["C0"], x["n0"], x["m0"], x["dh"],
+        x["gq"], x["gk"], x["gv"], x["gi"], x["gf"], x["go"], x["gC0"], x["gn0"], x["gm0"],
+        B_, H, T, dk, dv, chunk, io, x["ws"], x["wsn"], None)
+
+
+def bwd_args(B_=2, H=3, T=70, dk=64, dv=48, io=B.F32):
+    fa = Fake()
+    es = 2 if io == B.BF16 else 4
+    P = B_ * H
+    a = dict(q=fa(P * T * dk * es), k=fa(P * T * dk * es), v=fa(P * T * dv * es),
+             i=fa(P * T * 4), f=fa(P * T * 4), o=fa(P * T * dv * es),
+             C0=fa(P * dk * dv * 4), n0=fa(P * dk * 4), m0=fa(P * 4), dh=fa(P * T * dv * es),
+             gq=fa(P * T * dk * 4), gk=fa(P * T * dk * 4), gv=fa(P * T * dv * 4), gi=fa(P * T * 4),
+             gf=fa(P * T * 4), go=fa(P * T * dv * 4), gC0=fa(P * dk * dv * 4), gn0=fa(P * dk * 4),
+             gm0=fa(P * 4))
+    s, n = bws(B_, H, T, dk, dv, 32, io)
+    assert s == OK
+    a.update(ws=fa(n), wsn=n, dims=(B_, H, T, dk, dv, 32, io))
+    return a
+
+
+def test_bwd_validation(lib):
+    a = bwd_args()
+    assert bwd_call(a, gq=None) == NULL
+    assert bwd_call(a, dh=None) == NULL
+    assert bwd_call(a, n0=None) == STATE
+    assert bwd_call(a, gm0=None) == STATE
+    assert bwd_call(a, wsn=a["wsn"] - 4) == WS
+    assert bwd_call(a, ws=None) == WS
+    assert bwd_call(a, gq=a["q"]) == ALIAS                      # output over an input
+    assert bwd_call(a, gk=a["gq"] + 64) == ALIAS                # two outputs overlap
+    assert bwd_call(a, gC0=a["ws"]) == ALIAS                    # output over the workspace
+    assert bwd_call(a, dims=(2, 3, 70, 128, 48, 32, B.F32)) == UNSUP
+    assert bwd_call(a, dims=(2, 3, 0, 64, 48, 32, B.F32)) == SHAPE

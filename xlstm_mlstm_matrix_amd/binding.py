@@ -32,6 +32,8 @@ SIGNATURES = {
     "mlstm_fwd_chunkwise": (_i, [_vp] * 13 + [_i] * 7 + [_vp, _sz, _vp]),
     "mlstm_fwd_chunkwise_variant": (_i, [_vp] * 13 + [_i] * 8 + [_vp, _sz, _vp]),
     "mlstm_step": (_i, [_vp] * 13 + [_i] * 5 + [_vp]),
+    "mlstm_bwd_chunkwise_workspace_size": (_i, [_i] * 7 + [ctypes.POINTER(_sz)]),
+    "mlstm_bwd_chunkwise": (_i, [_vp] * 19 + [_i] * 7 + [_vp, _sz, _vp]),
 }
 
 
@@ -158,6 +160,54 @@ def fwd_chunkwise(q, k, v, i_pre, f_pre, o_pre, C0=None, n0=None, m0=None, *, ch
     if return_state:
         return h, (C_T, n_T, m_T)
     return h
+
+
+def bwd_workspace_size(B, H, T, d_qk, d_v, chunk, io: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().mlstm_bwd_chunkwise_workspace_size(B, H, T, d_qk, d_v, chunk, io, ctypes.byref(n)))
+    return n.value
+
+
+def bwd_chunkwise(q, k, v, i_pre, f_pre, o_pre, dh, C0=None, n0=None, m0=None, *, chunk: int = 32,
+                  state_grad: bool = False, workspace=None):
+    """Gradients of a loss L given dL/dh, for the inputs of fwd_chunkwise.
+
+    Same inputs as fwd_chunkwise plus dh [B,H,T,d_v] (the I/O dtype).
+    Returns float32 (dq, dk, dv, di, df, do), and with ``state_grad`` also
+    (dC0, dn0, dm0) -- of the zero state when no initial state is given."""
+    import torch
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    io_t = q.dtype
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("o_pre", o_pre), ("dh", dh)):
+        _req(t, name, io_t, dev)
+    for name, t in (("i_pre", i_pre), ("f_pre", f_pre), ("C0", C0), ("n0", n0), ("m0", m0)):
+        _req(t, name, torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    gq, gk = torch.empty((B, H, T, dk), **f32), torch.empty((B, H, T, dk), **f32)
+    gv, go = torch.empty((B, H, T, dv), **f32), torch.empty((B, H, T, dv), **f32)
+    gi, gf = torch.empty((B, H, T), **f32), torch.empty((B, H, T), **f32)
+    gC0 = gn0 = gm0 = None
+    if state_grad:
+        gC0, gn0, gm0 = (torch.empty((B, H, dk, dv), **f32), torch.empty((B, H, dk), **f32),
+                         torch.empty((B, H), **f32))
+    io = _io(q)
+    nbytes = bwd_workspace_size(B, H, T, dk, dv, chunk, io)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    _check(lib().mlstm_bwd_chunkwise(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(o_pre),
+        _ptr(C0), _ptr(n0), _ptr(m0), _ptr(dh), _ptr(gq), _ptr(gk), _ptr(gv), _ptr(gi), _ptr(gf),
+        _ptr(go), _ptr(gC0), _ptr(gn0), _ptr(gm0), B, H, T, dk, dv, chunk, io,
+        _ptr(workspace), ws_len, _stream(dev)))
+    out = (gq, gk, gv, gi, gf, go)
+    if state_grad:
+        return out + (gC0, gn0, gm0)
+    return out
 
 
 def step(q, k, v, i_pre, f_pre, o_pre, C=None, n=None, m=None, *, h=None, C_out=None,

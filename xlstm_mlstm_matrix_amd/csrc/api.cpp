@@ -286,4 +286,78 @@ mlstm_status_t mlstm_step(const void *q, const void *k, const void *v, const flo
     return e == hipSuccess ? MLSTM_OK : MLSTM_ERR_HIP;
 }
 
+// ---- backward
+
+static mlstm_status_t bwd_check_dims(int B, int H, int T, int d_qk, int d_v, int chunk, mlstm_dtype_t io,
+                              size_t *bytes) {
+    if (B <= 0 || H <= 0 || T <= 0 || d_qk <= 0 || d_v <= 0) return MLSTM_ERR_SHAPE;
+    if (io != MLSTM_F32 && io != MLSTM_BF16) return MLSTM_ERR_UNSUPPORTED;
+    if (!dims_ok(d_qk, d_v) || d_qk > kBwdMaxDim || d_v > kBwdMaxDim || !chunk_ok(chunk))
+        return MLSTM_ERR_UNSUPPORTED;
+    size_t BH, n;
+    if (!mul_ok((size_t)B, (size_t)H, &BH) || BH > (size_t)INT32_MAX) return MLSTM_ERR_SHAPE;
+    if (!mul_ok(BH, (size_t)T, &n) || !mul_ok(n, (size_t)(d_qk > d_v ? d_qk : d_v), &n))
+        return MLSTM_ERR_SHAPE;
+    if (!mul_ok(BH, bwd_ckpt_floats(T, d_qk, d_v), &n) || !mul_ok(n, sizeof(float), bytes))
+        return MLSTM_ERR_SHAPE;
+    return MLSTM_OK;
+}
+
+mlstm_status_t mlstm_bwd_chunkwise_workspace_size(int B, int H, int T, int d_qk, int d_v, int chunk,
+                                                  mlstm_dtype_t io, size_t *bytes) {
+    if (!bytes) return MLSTM_ERR_NULL;
+    return bwd_check_dims(B, H, T, d_qk, d_v, chunk, io, bytes);
+}
+
+mlstm_status_t mlstm_bwd_chunkwise(const void *q, const void *k, const void *v, const float *i_pre,
+                                   const float *f_pre, const void *o_pre, const float *C0,
+                                   const float *n0, const float *m0, const void *dh, float *dq,
+                                   float *dk, float *dv, float *d_i, float *d_f, float *d_o,
+                                   float *dC0, float *dn0, float *dm0, int B, int H, int T, int d_qk,
+                                   int d_v, int chunk, mlstm_dtype_t io, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    if (!q || !k || !v || !i_pre || !f_pre || !o_pre || !dh || !dq || !dk || !dv || !d_i || !d_f ||
+        !d_o)
+        return MLSTM_ERR_NULL;
+    size_t need;
+    mlstm_status_t st = bwd_check_dims(B, H, T, d_qk, d_v, chunk, io, &need);
+    if (st != MLSTM_OK) return st;
+    const int in0 = (C0 != nullptr) + (n0 != nullptr) + (m0 != nullptr);
+    const int out0 = (dC0 != nullptr) + (dn0 != nullptr) + (dm0 != nullptr);
+    if ((in0 != 0 && in0 != 3) || (out0 != 0 && out0 != 3)) return MLSTM_ERR_STATE_ARGS;
+
+    const size_t es = io == MLSTM_BF16 ? 2 : 4;
+    const size_t BH = (size_t)B * H;
+    const size_t nqk = BH * T * d_qk, nv = BH * T * d_v, ng = BH * T;
+    const size_t nC = BH * d_qk * d_v, nn = BH * d_qk;
+    const Range inputs[] = {rng(q, nqk * es), rng(k, nqk * es), rng(v, nv * es), rng(i_pre, ng * 4),
+                            rng(f_pre, ng * 4), rng(o_pre, nv * es), rng(C0, nC * 4), rng(n0, nn * 4),
+                            rng(m0, BH * 4), rng(dh, nv * es)};
+    const Range outs[] = {rng(dq, nqk * 4), rng(dk, nqk * 4), rng(dv, nv * 4), rng(d_i, ng * 4),
+                          rng(d_f, ng * 4), rng(d_o, nv * 4), rng(dC0, nC * 4), rng(dn0, nn * 4),
+                          rng(dm0, BH * 4)};
+    if (!workspace || workspace_bytes < need) return MLSTM_ERR_WORKSPACE;
+    const Range rws = rng(workspace, need);
+    for (const Range &o : outs) {
+        for (const Range &i : inputs)
+            if (overlaps(o, i)) return MLSTM_ERR_ALIAS;
+        if (overlaps(o, rws)) return MLSTM_ERR_ALIAS;
+    }
+    for (size_t o = 0; o < sizeof(outs) / sizeof(outs[0]); ++o)
+        for (size_t o2 = o + 1; o2 < sizeof(outs) / sizeof(outs[0]); ++o2)
+            if (overlaps(outs[o], outs[o2])) return MLSTM_ERR_ALIAS;
+    for (const Range &i : inputs)
+        if (overlaps(rws, i)) return MLSTM_ERR_ALIAS;
+
+    BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.ig = i_pre; a.fg = f_pre; a.o = o_pre;
+    a.C0 = C0; a.n0 = n0; a.m0 = m0; a.dh = dh;
+    a.gq = dq; a.gk = dk; a.gv = dv; a.gi = d_i; a.gf = d_f; a.go = d_o;
+    a.gC0 = dC0; a.gn0 = dn0; a.gm0 = dm0;
+    a.ckpt = static_cast<float *>(workspace);
+    a.BH = (int)BH; a.T = T; a.dk = d_qk; a.dv = d_v;
+    hipError_t e = launch_bwd(a, io == MLSTM_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLSTM_OK : MLSTM_ERR_HIP;
+}
+
 }  // extern "C"

@@ -63,10 +63,34 @@ struct StepArgs {
     int BH, dk, dv;
 };
 
+// Arguments of the backward kernels.
+struct BwdArgs {
+    const void *q, *k, *v;         // [BH, T, d_qk] x2, [BH, T, d_v]   io dtype
+    const float *ig, *fg;          // [BH, T]
+    const void *o;                 // [BH, T, d_v]                     io dtype
+    const float *C0, *n0, *m0;     // initial state, NULL = zero
+    const void *dh;                // [BH, T, d_v]                     io dtype
+    float *gq, *gk, *gv;           // gradients of q, k [BH, T, d_qk], v [BH, T, d_v]
+    float *gi, *gf;                // of i~, f~ [BH, T]
+    float *go;                     // of o~ [BH, T, d_v]
+    float *gC0, *gn0, *gm0;        // of the initial state, NULL = not wanted
+    float *ckpt;                   // workspace: state at every chunk start
+    int BH, T, dk, dv;
+};
+
+// Tokens per chunk and largest head dimensions of the backward kernels, and
+// the floats one pair needs in the backward's workspace.
+constexpr int kBwdChunk = 32;
+constexpr int kBwdMaxDim = 64;
+__host__ __device__ inline size_t bwd_ckpt_floats(int T, int dk, int dv) {
+    return (size_t)((T + kBwdChunk - 1) / kBwdChunk) * ((size_t)dk * dv + dk + 1);
+}
+
 // Launchers (defined in the .hip files).  Return hipSuccess or the launch error.
 hipError_t launch_step(const StepArgs &a, int io_bf16, hipStream_t s);
 hipError_t launch_fused(const FwdArgs &a, int io_bf16, int chunk, int state_only, hipStream_t s);
 hipError_t launch_seg_combine(const FwdArgs &a, float *ws, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs &a, int io_bf16, hipStream_t s);
 
 // Tiling choices shared by the planner and the launchers.
 int prefill_dkp(int dk);                 // d_qk padded to the kernel's compile-time width
