@@ -6,8 +6,9 @@ One step is one chunkwise forward pass (mlstm_fwd_chunkwise) over the
 7B-layer-shaped prefill workload: B=8 H=8 T=4096 d_qk=256 d_v=512 chunk=64,
 bf16 I/O, float32 state, synthetic seeded inputs already resident in HBM.
 `value` is prefill tokens/s (B*T per step).  The same JSON line also carries
-the decode workload (B=256 H=8, 1024 consecutive in-place mlstm_step calls)
-and the long-context prefill (B=1 H=8 T=65536 chunk=128), each with its own
+the decode workload (B=256 H=8, 1024 consecutive in-place mlstm_step calls),
+the long-context prefill (B=1 H=8 T=65536 chunk=128) and the backward pass
+(mlstm_bwd_chunkwise at B=4 H=4 T=1024 d=64 float32), each with its own
 roofline, and the float64 oracle timed on the host cores over a bounded
 sample (`cpu_baseline`).
 
@@ -34,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3  # fp32 vector peak of the chip (the unpacked FMA rate is half of it)
 METRIC = "mLSTM prefill tokens/s + %MFMA peak; decode step state GB/s + %HBM peak"
 CPU_THREADS_MAX = 16  # host cores that go with one GPU
 
@@ -158,6 +160,40 @@ def bench_decode(torch, I, binding, warmup_passes=1, nsteps=None):
     return w, ms, state_bytes, total_bytes
 
 
+def backward_work(w, L=32):
+    """Algorithmic flops of the chunkwise backward (checkpoint pass included):
+    per token-head 6 d_qk d_v multiply-adds (the recomputed read-out, C' a,
+    G* v, G*^T k, the carried-gradient update and the checkpoint pass's state
+    update) plus 3 (d_qk + d_v) per causal partner ((L + 1) / 2 on average:
+    S, a.v, P V, P~ K, P~^T Q, P^T A), 2 flops each."""
+    th = w.B * w.H * w.T
+    return th * 2 * (6 * w.d_qk * w.d_v + 1.5 * (L + 1) * (w.d_qk + w.d_v))
+
+
+def bench_backward(torch, I, binding, steps, warmup):
+    w = I.workload("small_f32")
+    d = I.gen_prefill(w, threads=16)
+    g = {k: (v.cuda().reshape(w.B, w.H, *v.shape[1:]) if v is not None else None) for k, v in d.items()}
+    del d
+    dh = torch.randn((w.B, w.H, w.T, w.d_v), generator=torch.Generator().manual_seed(7)).cuda()
+    args = [g[k] for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")] + [dh, g["C0"], g["n0"], g["m0"]]
+    nbytes = binding.bwd_workspace_size(w.B, w.H, w.T, w.d_qk, w.d_v, 32, binding.F32)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def run():
+        binding.bwd_chunkwise(*args, chunk=32, state_grad=True, workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    with Timer(torch) as tm:
+        for _ in range(steps):
+            run()
+    ms = tm.ms / steps
+    fl = backward_work(w)
+    log(f"backward {w.name}: {ms:.3f} ms/step, {fl / ms / 1e9:.2f} TFLOP/s")
+    return w, ms, fl
+
+
 def cpu_baseline(I, pairs_sample):
     """The float64 oracle on the host cores over a bounded sample of the
     prefill workload: `pairs_sample` (b, h) pairs, full sequence each."""
@@ -189,6 +225,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 7B prefill line (profiling runs of the other workloads)")
     ap.add_argument("--decode-steps", type=int, default=0,
@@ -281,6 +318,17 @@ def main():
             "roofline": {"bound": "hbm", "achieved": tb / msd / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": tb / msd / 1e6 / PEAK_HBM_GBS, "traffic": traffic_record("decode"),
                          "kernel": "mlstm_step_kernel", "algorithmic_bytes_per_launch": tb}}
+
+    if not args.no_backward:
+        wb, msb, flb = bench_backward(torch, I, binding, max(3, args.steps // 4), max(1, args.warmup // 4))
+        rec["backward"] = {
+            "workload": "backward B=4 H=4 T=1024 d_qk=d_v=64 float32 I/O, initial-state gradients "
+                        "(checkpoint pass + reverse pass, 32-token chunks)",
+            "ms_per_step": msb, "tokens_per_s": wb.B * wb.T / msb * 1e3,
+            "roofline": {"bound": "alu", "achieved": flb / msb / 1e9, "peak": PEAK_FP32_TFLOPS,
+                         "unit": "TFLOP/s", "frac": flb / msb / 1e9 / PEAK_FP32_TFLOPS, "traffic": None,
+                         "kernel": "bwd_ckpt_kernel + bwd_kernel (one workgroup per pair)",
+                         "algorithmic_flops_per_launch": flb}}
 
     if not args.no_cpu:
         Pn = max(1, args.cpu_pairs)

@@ -39,6 +39,17 @@ namespace mlstm {
 namespace {
 
 constexpr int L = kBwdChunk, D = kBwdMaxDim, NTH = 256;
+constexpr int LD = D + 4;  // padded row length of the backward kernel's tiles (floats, 16-byte rows)
+
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ float hsum(f32x4 x) { return (x[0] + x[1]) + (x[2] + x[3]); }
+// sum_r x[r] y[r] over n floats (n a multiple of 4, both 16-byte aligned)
+__device__ __forceinline__ float dot(const float *x, const float *y, int n) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int r = 0; r < n; r += 4) acc += ld4(x + r) * ld4(y + r);
+    return hsum(acc);
+}
 
 // In-chunk gate quantities of tokens t0 .. t0 + L - 1 for the stabilizer
 // m_before, by one wavefront (lane j = token j; tokens past T act as i~ =
@@ -76,7 +87,8 @@ __device__ void chunk_gates(const float *ig, const float *fg, int t0, int T, flo
 
 template <typename IO>
 __global__ __launch_bounds__(NTH) void bwd_ckpt_kernel(BwdArgs a) {
-    __shared__ float Cs[D * D], ns[D], Kt[L * D], Vt[L * D], wv[L], gb[L], gu[L], gr[L], last[2];
+    __shared__ __attribute__((aligned(16))) float Cs[D * D], Kt[L * D], Vt[L * D];
+    __shared__ float ns[D], wv[L], gb[L], gu[L], gr[L], last[2];
     const int p = blockIdx.x, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T;
     const int nch = (T + L - 1) / L;
@@ -110,11 +122,12 @@ __global__ __launch_bounds__(NTH) void bwd_ckpt_kernel(BwdArgs a) {
         const float dec = exp_e(m - r_last);
         if (tid < L) wv[tid] = exp_e(gu[tid] - r_last);
         __syncthreads();
-        for (int e = tid; e < dk * dv; e += NTH) {
-            const int row = e / dv, col = e % dv;
-            float acc = dec * Cs[e];
-            for (int j = 0; j < L; ++j) acc = fmaf(wv[j] * Kt[j * dk + row], Vt[j * dv + col], acc);
-            Cs[e] = acc;
+        for (int e = tid; e < dk * dv / 4; e += NTH) {
+            const int row = (4 * e) / dv, col = (4 * e) % dv;
+            f32x4 acc = dec * ld4(&Cs[4 * e]);
+#pragma unroll 4
+            for (int j = 0; j < L; ++j) acc += (wv[j] * Kt[j * dk + row]) * ld4(&Vt[j * dv + col]);
+            *reinterpret_cast<f32x4 *>(&Cs[4 * e]) = acc;
         }
         for (int e = tid; e < dk; e += NTH) {
             float acc = dec * ns[e];
@@ -128,9 +141,11 @@ __global__ __launch_bounds__(NTH) void bwd_ckpt_kernel(BwdArgs a) {
 
 template <typename IO>
 __global__ __launch_bounds__(NTH) void bwd_kernel(BwdArgs a) {
-    __shared__ float Q[L * D], K[L * D], V[L * D], SG[L * D], DH[L * D], NUM[L * D], A[L * D], DQ[L * D],
-        DK[L * D];
-    __shared__ float Cc[D * D], Gs[D * D], P[L * L], PT[L * L];
+    // rows padded to LD floats: column walks (lanes on consecutive rows) then
+    // fall on consecutive banks
+    __shared__ __attribute__((aligned(16))) float Q[L * LD], K[L * LD], V[L * LD], SG[L * LD], DH[L * LD],
+        NUM[L * LD], A[L * LD], DQ[L * LD], DK[L * LD];
+    __shared__ __attribute__((aligned(16))) float Cc[D * LD], Gs[D * LD], P[L * L], PT[L * L];
     __shared__ float nc[D], gs[D], gb[L], gu[L], gr[L], sv[L], fl[L], wv[L], dd[L], den[L], beta[L];
     __shared__ float last[2], carry, red[NTH];
     const int p = blockIdx.x, tid = threadIdx.x;
@@ -144,28 +159,28 @@ __global__ __launch_bounds__(NTH) void bwd_kernel(BwdArgs a) {
     const IO *ogp = static_cast<const IO *>(a.o) + ov;
     const IO *dhg = static_cast<const IO *>(a.dh) + ov;
 
-    for (int e = tid; e < dk * dv; e += NTH) Gs[e] = 0.0f;
+    for (int e = tid; e < D * LD; e += NTH) Gs[e] = 0.0f;
     for (int e = tid; e < dk; e += NTH) gs[e] = 0.0f;
     if (tid == 0) carry = 0.0f;
     __syncthreads();
     for (int c = nch - 1; c >= 0; --c) {
         const int t0 = c * L;
         const float *ck = a.ckpt + ((size_t)p * nch + c) * rec;
-        for (int e = tid; e < dk * dv; e += NTH) Cc[e] = ck[e];
+        for (int e = tid; e < dk * dv; e += NTH) Cc[(e / dv) * LD + e % dv] = ck[e];
         for (int e = tid; e < dk; e += NTH) nc[e] = ck[(size_t)dk * dv + e];
         const float m_prev = ck[(size_t)dk * dv + dk];
         for (int e = tid; e < L * dk; e += NTH) {
-            const int t = t0 + e / dk;
+            const int i = e / dk, t = t0 + i;
             const size_t g = (size_t)t * dk + e % dk;
-            Q[e] = t < T ? to_f(qg[g]) : 0.0f;
-            K[e] = t < T ? to_f(kg[g]) : 0.0f;
+            Q[i * LD + e % dk] = t < T ? to_f(qg[g]) : 0.0f;
+            K[i * LD + e % dk] = t < T ? to_f(kg[g]) : 0.0f;
         }
         for (int e = tid; e < L * dv; e += NTH) {
-            const int t = t0 + e / dv;
+            const int i = e / dv, t = t0 + i, x = i * LD + e % dv;
             const size_t g = (size_t)t * dv + e % dv;
-            V[e] = t < T ? to_f(vg[g]) : 0.0f;
-            SG[e] = t < T ? sigmoid(to_f(ogp[g])) : 0.0f;
-            DH[e] = t < T ? to_f(dhg[g]) : 0.0f;
+            V[x] = t < T ? to_f(vg[g]) : 0.0f;
+            SG[x] = t < T ? sigmoid(to_f(ogp[g])) : 0.0f;
+            DH[x] = t < T ? to_f(dhg[g]) : 0.0f;
         }
         if (tid < 64) chunk_gates(a.ig + og1, a.fg + og1, t0, T, m_prev, gb, gu, gr, last);
         __syncthreads();
@@ -180,26 +195,24 @@ __global__ __launch_bounds__(NTH) void bwd_kernel(BwdArgs a) {
         for (int e = tid; e < L * L; e += NTH) {
             const int i = e / L, j = e % L;
             float s = 0.0f;
-            if (j <= i && t0 + i < T) {
-                for (int r = 0; r < dk; ++r) s = fmaf(Q[i * dk + r], K[j * dk + r], s);
-                s *= exp_e(gu[j] - gr[i]);
-            }
+            if (j <= i && t0 + i < T) s = dot(&Q[i * LD], &K[j * LD], dk) * exp_e(gu[j] - gr[i]);
             P[e] = s;
         }
         __syncthreads();
         // forward read-out and denominator, recomputed
-        for (int e = tid; e < L * dv; e += NTH) {
-            const int i = e / dv, b = e % dv;
-            float acc = 0.0f;
-            for (int r = 0; r < dk; ++r) acc = fmaf(Cc[r * dv + b], Q[i * dk + r], acc);
+        for (int e = tid; e < L * dv / 4; e += NTH) {
+            const int i = (4 * e) / dv, b = (4 * e) % dv;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int r = 0; r < dk; ++r) acc += Q[i * LD + r] * ld4(&Cc[r * LD + b]);
             acc *= sv[i];
-            for (int j = 0; j <= i; ++j) acc = fmaf(P[i * L + j], V[j * dv + b], acc);
-            NUM[e] = acc;
+            for (int j = 0; j <= i; ++j) acc += P[i * L + j] * ld4(&V[j * LD + b]);
+            *reinterpret_cast<f32x4 *>(&NUM[i * LD + b]) = acc;
         }
         if (tid < L) {
             const int i = tid;
             float acc = 0.0f;
-            for (int r = 0; r < dk; ++r) acc = fmaf(nc[r], Q[i * dk + r], acc);
+            for (int r = 0; r < dk; ++r) acc = fmaf(nc[r], Q[i * LD + r], acc);
             acc *= sv[i];
             for (int j = 0; j <= i; ++j) acc += P[i * L + j];
             dd[i] = acc;
@@ -208,17 +221,16 @@ __global__ __launch_bounds__(NTH) void bwd_kernel(BwdArgs a) {
         __syncthreads();
         // a = dh sigmoid(o~) / den, and the output-gate gradient
         for (int e = tid; e < L * dv; e += NTH) {
-            const int i = e / dv;
-            const float sg = SG[e];
-            A[e] = DH[e] * sg / den[i];
+            const int i = e / dv, x = i * LD + e % dv;
+            const float sg = SG[x];
+            A[x] = DH[x] * sg / den[i];
             const int t = t0 + i;
-            if (t < T) a.go[ov + (size_t)t * dv + e % dv] = DH[e] * NUM[e] / den[i] * sg * (1.0f - sg);
+            if (t < T) a.go[ov + (size_t)t * dv + e % dv] = DH[x] * NUM[x] / den[i] * sg * (1.0f - sg);
         }
         __syncthreads();
         if (tid < L) {
             const int i = tid;
-            float an = 0.0f;
-            for (int b = 0; b < dv; ++b) an = fmaf(A[i * dv + b], NUM[i * dv + b], an);
+            const float an = dot(&A[i * LD], &NUM[i * LD], dv);
             beta[i] = fabsf(dd[i]) > fl[i] ? (dd[i] > 0.0f ? -an : an) / den[i] : 0.0f;
         }
         __syncthreads();
@@ -226,43 +238,36 @@ __global__ __launch_bounds__(NTH) void bwd_kernel(BwdArgs a) {
         for (int e = tid; e < L * L; e += NTH) {
             const int i = e / L, j = e % L;
             float s = 0.0f;
-            if (j <= i && t0 + i < T) {
-                for (int b = 0; b < dv; ++b) s = fmaf(A[i * dv + b], V[j * dv + b], s);
-                s = (s + beta[i]) * exp_e(gu[j] - gr[i]);
-            }
+            if (j <= i && t0 + i < T) s = (dot(&A[i * LD], &V[j * LD], dv) + beta[i]) * exp_e(gu[j] - gr[i]);
             PT[e] = s;
         }
         __syncthreads();
         for (int e = tid; e < L * dk; e += NTH) {
             const int i = e / dk, r = e % dk;
-            float acc = 0.0f;
-            for (int b = 0; b < dv; ++b) acc = fmaf(Cc[r * dv + b], A[i * dv + b], acc);
-            acc = sv[i] * fmaf(nc[r], beta[i], acc);
-            for (int j = 0; j <= i; ++j) acc = fmaf(PT[i * L + j], K[j * dk + r], acc);
-            DQ[e] = acc;
+            float acc = sv[i] * fmaf(nc[r], beta[i], dot(&Cc[r * LD], &A[i * LD], dv));
+            for (int j = 0; j <= i; ++j) acc = fmaf(PT[i * L + j], K[j * LD + r], acc);
+            DQ[i * LD + r] = acc;
             const int t = t0 + i;
             if (t < T) a.gq[oqk + (size_t)t * dk + r] = acc;
         }
         for (int e = tid; e < L * dk; e += NTH) {
             const int j = e / dk, r = e % dk;
             float acc = 0.0f;
-            for (int i = j; i < L; ++i) acc = fmaf(PT[i * L + j], Q[i * dk + r], acc);
-            float gv = gs[r];
-            for (int b = 0; b < dv; ++b) gv = fmaf(Gs[r * dv + b], V[j * dv + b], gv);
-            acc = fmaf(wv[j], gv, acc);
-            DK[e] = acc;
+            for (int i = j; i < L; ++i) acc = fmaf(PT[i * L + j], Q[i * LD + r], acc);
+            acc = fmaf(wv[j], gs[r] + dot(&Gs[r * LD], &V[j * LD], dv), acc);
+            DK[j * LD + r] = acc;
             const int t = t0 + j;
             if (t < T) a.gk[oqk + (size_t)t * dk + r] = acc;
         }
-        for (int e = tid; e < L * dv; e += NTH) {
-            const int j = e / dv, b = e % dv;
-            float acc = 0.0f;
-            for (int i = j; i < L; ++i) acc = fmaf(P[i * L + j], A[i * dv + b], acc);
-            float gk = 0.0f;
-            for (int r = 0; r < dk; ++r) gk = fmaf(Gs[r * dv + b], K[j * dk + r], gk);
-            acc = fmaf(wv[j], gk, acc);
+        for (int e = tid; e < L * dv / 4; e += NTH) {
+            const int j = (4 * e) / dv, b = (4 * e) % dv;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, gk = {0.f, 0.f, 0.f, 0.f};
+            for (int i = j; i < L; ++i) acc += P[i * L + j] * ld4(&A[i * LD + b]);
+#pragma unroll 4
+            for (int r = 0; r < dk; ++r) gk += K[j * LD + r] * ld4(&Gs[r * LD + b]);
+            acc += wv[j] * gk;
             const int t = t0 + j;
-            if (t < T) a.gv[ov + (size_t)t * dv + b] = acc;
+            if (t < T) *reinterpret_cast<f32x4 *>(&a.gv[ov + (size_t)t * dv + b]) = acc;
         }
         __syncthreads();
         // gate gradients: di = k.dk; df = reverse cumsum of q.dq - k.dk
@@ -271,12 +276,8 @@ __global__ __launch_bounds__(NTH) void bwd_kernel(BwdArgs a) {
             const bool ok = j < L && t < T;
             float di = 0.0f, x = 0.0f;
             if (ok) {
-                float qd = 0.0f;
-                for (int r = 0; r < dk; ++r) {
-                    di = fmaf(K[j * dk + r], DK[j * dk + r], di);
-                    qd = fmaf(Q[j * dk + r], DQ[j * dk + r], qd);
-                }
-                x = qd - di;
+                di = dot(&K[j * LD], &DK[j * LD], dk);
+                x = dot(&Q[j * LD], &DQ[j * LD], dk) - di;
             }
             float y = x;  // sum over lanes >= j
             for (int o = 1; o < 64; o <<= 1) {
@@ -293,15 +294,16 @@ __global__ __launch_bounds__(NTH) void bwd_kernel(BwdArgs a) {
         }
         // carried gradients for the chunk before (every read of G*, g* is past
         // the barrier above)
-        for (int e = tid; e < dk * dv; e += NTH) {
-            const int r = e / dv, b = e % dv;
-            float acc = dec * Gs[e];
-            for (int i = 0; i < L; ++i) acc = fmaf(sv[i] * Q[i * dk + r], A[i * dv + b], acc);
-            Gs[e] = acc;
+        for (int e = tid; e < dk * dv / 4; e += NTH) {
+            const int r = (4 * e) / dv, b = (4 * e) % dv;
+            f32x4 acc = dec * ld4(&Gs[r * LD + b]);
+#pragma unroll 4
+            for (int i = 0; i < L; ++i) acc += (sv[i] * Q[i * LD + r]) * ld4(&A[i * LD + b]);
+            *reinterpret_cast<f32x4 *>(&Gs[r * LD + b]) = acc;
         }
         for (int e = tid; e < dk; e += NTH) {
             float acc = dec * gs[e];
-            for (int i = 0; i < L; ++i) acc = fmaf(sv[i] * beta[i], Q[i * dk + e], acc);
+            for (int i = 0; i < L; ++i) acc = fmaf(sv[i] * beta[i], Q[i * LD + e], acc);
             gs[e] = acc;
         }
         __syncthreads();
@@ -309,8 +311,9 @@ __global__ __launch_bounds__(NTH) void bwd_kernel(BwdArgs a) {
     // gradients of the initial state
     float part = 0.0f;
     for (int e = tid; e < dk * dv; e += NTH) {
-        if (a.gC0) a.gC0[(size_t)p * dk * dv + e] = Gs[e];
-        if (a.C0) part = fmaf(Gs[e], a.C0[(size_t)p * dk * dv + e], part);
+        const float gx = Gs[(e / dv) * LD + e % dv];
+        if (a.gC0) a.gC0[(size_t)p * dk * dv + e] = gx;
+        if (a.C0) part = fmaf(gx, a.C0[(size_t)p * dk * dv + e], part);
     }
     for (int e = tid; e < dk; e += NTH) {
         if (a.gn0) a.gn0[(size_t)p * dk + e] = gs[e];
