@@ -30,6 +30,9 @@
  *    (a hipStream_t; NULL = the null stream) and the call returns at once.
  *  - q, k, v, o_pre and h have the I/O dtype `io` (float32 or bfloat16);
  *    i_pre, f_pre and the state (C, n, m) are always float32.
+ *  - Every pointer, workspace included, must be 16-byte aligned (the kernels
+ *    move 16 bytes per lane; hipMalloc and torch allocations are 256-byte
+ *    aligned, a view at an offset may not be): MLSTM_ERR_ALIGN otherwise.
  *  - Arguments are validated on the host before any device work.  An invalid
  *    call returns an error status and enqueues nothing.  A HIP launch error
  *    returns MLSTM_ERR_HIP.  No exception crosses the ABI.
@@ -65,7 +68,8 @@ typedef enum {
     MLSTM_ERR_STATE_ARGS = 4,  /* initial or final state given only in part */
     MLSTM_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the query says */
     MLSTM_ERR_ALIAS = 6,       /* buffers overlap in a way the call does not allow */
-    MLSTM_ERR_HIP = 7          /* the HIP runtime reported an error */
+    MLSTM_ERR_HIP = 7,         /* the HIP runtime reported an error */
+    MLSTM_ERR_ALIGN = 8        /* a pointer is not 16-byte aligned */
 } mlstm_status_t;
 
 /* Kernel strategy of the chunkwise forward (the result is the same up to

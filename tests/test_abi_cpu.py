@@ -48,7 +48,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         assert B.status_string(s).startswith(B.STATUS[s])
     assert "unknown" in B.status_string(99)
     assert lib.mlstm_version().decode().startswith("mlstm-gfx950")
@@ -163,7 +163,7 @@ def test_fwd_validation(lib):
     # aliasing: h over an input, partial overlap of state buffers, workspace over an input
     a = fwd_args(); a["h"] = a["v"] + 64
     assert call_fwd(a) == ALIAS
-    a = fwd_args(); a["CT"] = a["C0"] + 4
+    a = fwd_args(); a["CT"] = a["C0"] + 16
     assert call_fwd(a) == ALIAS
     a = fwd_args(); a["nT"] = a["C0"]
     assert call_fwd(a) == ALIAS
@@ -206,7 +206,7 @@ def test_step_validation(lib):
     assert call_step(a) == ALIAS
     a = step_args(); a["h"] = a["o"]
     assert call_step(a) == ALIAS
-    a = step_args(); a["no"] = a["Co"] + 8
+    a = step_args(); a["no"] = a["Co"] + 16
     assert call_step(a) == ALIAS
 
 
@@ -278,3 +278,18 @@ def test_bwd_validation(lib):
     assert bwd_call(a, gC0=a["ws"]) == ALIAS                    # output over the workspace
     assert bwd_call(a, dims=(2, 3, 70, 128, 48, 32, B.F32)) == UNSUP
     assert bwd_call(a, dims=(2, 3, 0, 64, 48, 32, B.F32)) == SHAPE
+
+
+def test_misaligned_pointers_rejected(lib):
+    """Every entry point rejects a pointer off a 16-byte boundary before any
+    device work (fake addresses, never dereferenced)."""
+    ALIGN = 8
+    for key in ("q", "k", "v", "i", "f", "o", "C0", "n0", "m0", "h", "CT", "nT", "mT", "ws"):
+        a = fwd_args(); a[key] += 4
+        assert call_fwd(a) == ALIGN, key
+    for key in ("q", "v", "i", "C", "h", "Co", "mo"):
+        a = step_args(); a[key] += 2
+        assert call_step(a) == ALIGN, key
+    b = bwd_args()
+    for key in ("q", "dh", "gq", "gf", "gC0", "ws"):
+        assert bwd_call(b, **{key: b[key] + 2}) == ALIGN, key

@@ -18,7 +18,7 @@ F32, BF16 = 0, 1
 VARIANTS = {"auto": 0, "fused": 1, "segscan": 2}
 STATUS = {0: "MLSTM_OK", 1: "MLSTM_ERR_NULL", 2: "MLSTM_ERR_SHAPE", 3: "MLSTM_ERR_UNSUPPORTED",
           4: "MLSTM_ERR_STATE_ARGS", 5: "MLSTM_ERR_WORKSPACE", 6: "MLSTM_ERR_ALIAS",
-          7: "MLSTM_ERR_HIP"}
+          7: "MLSTM_ERR_HIP", 8: "MLSTM_ERR_ALIGN"}
 
 # exported entry points and their C signatures (kept in step with include/mlstm.h)
 _vp, _fp, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t

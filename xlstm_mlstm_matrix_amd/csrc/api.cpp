@@ -7,6 +7,8 @@
 
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "common.hpp"
 
 using namespace mlstm;
@@ -22,6 +24,7 @@ const char *kStatus[] = {
     "MLSTM_ERR_WORKSPACE: workspace missing or smaller than the queried size",
     "MLSTM_ERR_ALIAS: buffers overlap in a way this call does not allow",
     "MLSTM_ERR_HIP: the HIP runtime reported an error",
+    "MLSTM_ERR_ALIGN: a pointer is not 16-byte aligned",
 };
 
 constexpr int kMaxDk = 256, kMaxDv = 512;
@@ -36,6 +39,13 @@ Range rng(const void *p, size_t bytes) {
 }
 bool overlaps(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 bool same(Range a, Range b) { return a.lo == b.lo && a.hi == b.hi && a.lo < a.hi; }
+
+// every pointer (NULL allowed) 16-byte aligned
+bool all_aligned(std::initializer_list<const void *> ps) {
+    for (const void *p : ps)
+        if ((uintptr_t)p & 15) return false;
+    return true;
+}
 
 bool mul_ok(size_t a, size_t b, size_t *out) {
     if (a != 0 && b > SIZE_MAX / a) return false;
@@ -166,6 +176,8 @@ mlstm_status_t mlstm_fwd_chunkwise_variant(const void *q, const void *k, const v
     const int in0 = (C0 != nullptr) + (n0 != nullptr) + (m0 != nullptr);
     const int out0 = (C_T != nullptr) + (n_T != nullptr) + (m_T != nullptr);
     if ((in0 != 0 && in0 != 3) || (out0 != 0 && out0 != 3)) return MLSTM_ERR_STATE_ARGS;
+    if (!all_aligned({q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C_T, n_T, m_T, workspace}))
+        return MLSTM_ERR_ALIGN;
 
     const size_t es = io == MLSTM_BF16 ? 2 : 4;
     const size_t BH = (size_t)B * H;
@@ -259,6 +271,8 @@ mlstm_status_t mlstm_step(const void *q, const void *k, const void *v, const flo
     if (!mul_ok((size_t)B, (size_t)H, &BH) || BH > (size_t)INT32_MAX) return MLSTM_ERR_SHAPE;
     const int in0 = (C_in != nullptr) + (n_in != nullptr) + (m_in != nullptr);
     if (in0 != 0 && in0 != 3) return MLSTM_ERR_STATE_ARGS;
+    if (!all_aligned({q, k, v, i_pre, f_pre, o_pre, C_in, n_in, m_in, h, C_out, n_out, m_out}))
+        return MLSTM_ERR_ALIGN;
 
     const size_t es = io == MLSTM_BF16 ? 2 : 4;
     const size_t nC = BH * d_qk * d_v, nn = BH * d_qk;
@@ -325,6 +339,9 @@ mlstm_status_t mlstm_bwd_chunkwise(const void *q, const void *k, const void *v, 
     const int in0 = (C0 != nullptr) + (n0 != nullptr) + (m0 != nullptr);
     const int out0 = (dC0 != nullptr) + (dn0 != nullptr) + (dm0 != nullptr);
     if ((in0 != 0 && in0 != 3) || (out0 != 0 && out0 != 3)) return MLSTM_ERR_STATE_ARGS;
+    if (!all_aligned({q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, dh, dq, dk, dv, d_i, d_f, d_o, dC0, dn0,
+                      dm0, workspace}))
+        return MLSTM_ERR_ALIGN;
 
     const size_t es = io == MLSTM_BF16 ? 2 : 4;
     const size_t BH = (size_t)B * H;
