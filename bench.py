@@ -143,10 +143,13 @@ def bench_decode(torch, I, binding, warmup_passes=1, nsteps=None):
     C, n, m = C0.clone(), n0.clone(), m0.clone()
     h = torch.empty((w.B, w.H, w.d_v), dtype=torch.bfloat16, device="cuda")
     keys = ("q", "k", "v", "i_pre", "f_pre", "o_pre")
+    # one workspace (scratch of the row-split kernel) for the whole run
+    ws = binding.step_workspace(w.B, w.H, w.d_qk, w.d_v, torch.bfloat16, "cuda")
 
     def one_pass():
         for t in range(w.T):
-            binding.step(*(steps[k][t] for k in keys), C, n, m, h=h, C_out=C, n_out=n, m_out=m)
+            binding.step(*(steps[k][t] for k in keys), C, n, m, h=h, C_out=C, n_out=n, m_out=m,
+                         workspace=ws)
 
     for _ in range(warmup_passes):
         one_pass()
@@ -317,7 +320,8 @@ def main():
             "state_GBs": sb / msd / 1e6,
             "roofline": {"bound": "hbm", "achieved": tb / msd / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": tb / msd / 1e6 / PEAK_HBM_GBS, "traffic": traffic_record("decode"),
-                         "kernel": "mlstm_step_kernel", "algorithmic_bytes_per_launch": tb}}
+                         "kernel": "mlstm_step_rows_kernel + mlstm_step_finish_kernel (row split, two launches per step)",
+                         "algorithmic_bytes_per_step": tb}}
 
     if not args.no_backward:
         wb, msb, flb = bench_backward(torch, I, binding, max(3, args.steps // 4), max(1, args.warmup // 4))

@@ -158,7 +158,18 @@ mlstm_status_t mlstm_fwd_chunkwise_variant(const void *q, const void *k, const v
                                            void *stream);
 
 /*
- * One step of the recurrence for B*H independent cells (decode).
+ * Bytes of device workspace mlstm_step can use for this shape (0 when the
+ * shape gains nothing from it; then the workspace argument is ignored).
+ * bytes NULL -> MLSTM_ERR_NULL; unsupported shape -> as mlstm_step.
+ */
+mlstm_status_t mlstm_step_workspace_size(int B, int H, int d_qk, int d_v, mlstm_dtype_t io,
+                                         size_t *bytes);
+
+/*
+ * One step of the recurrence for B*H independent cells (decode): the
+ * per-token update of the memory, normalizer and stabilizer and the gated
+ * read-out (xLSTM note, section "mLSTM (matrix LSTM)" and its example
+ * recurrent step; one token of the forward above).
  *
  *  q, k      [B, H, d_qk]  io dtype;   v, o_pre [B, H, d_v]  io dtype
  *  i_pre, f_pre [B, H]     float32
@@ -168,12 +179,23 @@ mlstm_status_t mlstm_fwd_chunkwise_variant(const void *q, const void *k, const v
  *  C_out, n_out, m_out  state after the token (required).  Each may be
  *            exactly the matching *_in pointer (in-place update, the usual
  *            decode loop); any other overlap is MLSTM_ERR_ALIAS.
+ *  workspace optional device buffer of workspace_bytes.  NULL: one workgroup
+ *            streams each cell's memory.  Given (at least the size
+ *            mlstm_step_workspace_size reports, when that is not 0), each
+ *            cell's memory is split into row blocks streamed by separate
+ *            workgroups, whose partial read-outs a second launch sums there
+ *            (faster for large memories).  Scratch only: no initial contents
+ *            are needed and none are kept, but two calls that may run at the
+ *            same time need separate buffers.  Too small ->
+ *            MLSTM_ERR_WORKSPACE; overlapping any tensor argument ->
+ *            MLSTM_ERR_ALIAS.
  */
 mlstm_status_t mlstm_step(const void *q, const void *k, const void *v,
                           const float *i_pre, const float *f_pre, const void *o_pre,
                           const float *C_in, const float *n_in, const float *m_in,
                           void *h, float *C_out, float *n_out, float *m_out,
-                          int B, int H, int d_qk, int d_v, mlstm_dtype_t io, void *stream);
+                          int B, int H, int d_qk, int d_v, mlstm_dtype_t io,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Gradients of a loss L with respect to every input of mlstm_fwd_chunkwise,

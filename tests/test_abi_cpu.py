@@ -37,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s+(mlstm_\w+)", out))
@@ -187,7 +187,8 @@ def step_args(B_=4, H=2, dk=64, dv=128, io=B.BF16, state=True):
 
 def call_step(a):
     return B.lib().mlstm_step(a["q"], a["k"], a["v"], a["i"], a["f"], a["o"], a["C"], a["n"], a["m"],
-                              a["h"], a["Co"], a["no"], a["mo"], *a["dims"], None)
+                              a["h"], a["Co"], a["no"], a["mo"], *a["dims"], a.get("ws"),
+                              a.get("wsn", 0), None)
 
 
 def test_step_validation(lib):
@@ -208,6 +209,40 @@ def test_step_validation(lib):
     assert call_step(a) == ALIAS
     a = step_args(); a["no"] = a["Co"] + 16
     assert call_step(a) == ALIAS
+
+
+def sws(*args):
+    n = ctypes.c_size_t(12345)
+    s = B.lib().mlstm_step_workspace_size(*args, ctypes.byref(n))
+    return s, n.value
+
+
+def test_step_workspace_query(lib):
+    # d_v = 512: 128 threads per row, 4 rows per pass, 16 rows per thread ->
+    # blocks of 64 rows; partial read-outs [BH][blocks][d_v + 4] float32
+    assert sws(256, 8, 256, 512, B.BF16) == (OK, 2048 * 4 * 516 * 4)
+    assert sws(2, 3, 80, 512, B.F32) == (OK, 6 * 2 * 516 * 4)       # 64 + 16 rows
+    assert sws(2, 3, 256, 256, B.F32) == (OK, 6 * 2 * 260 * 4)      # blocks of 128 rows
+    assert sws(2, 3, 64, 512, B.BF16) == (OK, 0)     # one block: no split
+    assert sws(2, 3, 256, 64, B.BF16) == (OK, 0)     # 32 rows per pass: one block
+    assert sws(0, 3, 64, 64, B.BF16)[0] == SHAPE
+    assert sws(2, 3, 40, 64, B.BF16)[0] == UNSUP
+    assert sws(2, 3, 64, 64, 7)[0] == UNSUP
+    assert B.lib().mlstm_step_workspace_size(1, 1, 64, 64, 0, None) == NULL
+
+
+def test_step_workspace_validation(lib):
+    dims = dict(B_=2, H=3, dk=256, dv=512)
+    need = sws(2, 3, 256, 512, B.BF16)[1]
+    free = lambda a: a["mo"] + (1 << 24)   # past every fake tensor
+    a = step_args(**dims); a["ws"] = free(a); a["wsn"] = need - 4
+    assert call_step(a) == WS
+    a = step_args(**dims); a["ws"] = a["C"]; a["wsn"] = need
+    assert call_step(a) == ALIAS
+    a = step_args(**dims); a["ws"] = a["h"] - 16; a["wsn"] = need
+    assert call_step(a) == ALIAS
+    a = step_args(**dims); a["ws"] = free(a) + 8; a["wsn"] = need
+    assert call_step(a) == 8   # MLSTM_ERR_ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

@@ -11,16 +11,20 @@ from xlstm_mlstm_matrix_amd import binding, inputs as I
 pytestmark = pytest.mark.gpu
 
 
-def run_steps(steps, state, inplace=True):
-    """steps: dict of [S, B, H, ...] device tensors; state: (C, n, m) or None."""
-    S = steps["q"].shape[0]
+def run_steps(steps, state, inplace=True, split=True):
+    """steps: dict of [S, B, H, ...] device tensors; state: (C, n, m) or None.
+    With ``split`` every step uses the row-split kernel where the shape has
+    one, all through one workspace."""
+    S, B, H = steps["q"].shape[:3]
+    dk, dv = steps["q"].shape[-1], steps["v"].shape[-1]
+    ws = binding.step_workspace(B, H, dk, dv, steps["q"].dtype, steps["q"].device) if split else None
     C = n = m = None
     if state is not None:
         C, n, m = (x.clone() for x in state)
     hs = []
     for t in range(S):
         h, C, n, m = binding.step(*(steps[k][t] for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")),
-                                  C, n, m, inplace=inplace)
+                                  C, n, m, inplace=inplace, split=split, workspace=ws)
         hs.append(h)
     torch.cuda.synchronize()
     return torch.stack(hs, dim=2), C, n, m  # h: [B, H, S, d_v]
@@ -45,20 +49,52 @@ def compare_steps(gpu, ref, io, what):
     PT.compare_fwd((flat(h), flat(C), flat(n), flat(m)), ref, io, what)
 
 
+@pytest.mark.parametrize("split", [True, False])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("dk,dv", [(16, 16), (64, 64), (64, 128), (256, 512), (48, 80)])
-def test_steps_vs_oracle(io, dk, dv):
+@pytest.mark.parametrize("dk,dv", [(16, 16), (64, 64), (64, 128), (256, 512), (48, 80),
+                                   (80, 512), (208, 512), (256, 256), (144, 272)])
+def test_steps_vs_oracle(io, dk, dv, split):
+    """Head shapes with one row block (no split), with several (256 x 512: 4
+    blocks of 64 rows; 256 x 256: 2 of 128) and with a ragged last block (80
+    and 208 rows in blocks of 64; 144 rows in blocks of 112 at d_v = 272)."""
     w = I.workload("decode_bf16", io=io, d_qk=dk, d_v=dv)
     steps = PT.cuda(I.gen_decode_steps(w, range(24), B=3))
     state = tuple(x.cuda() for x in I.gen_decode_state(w, B=3))
-    compare_steps(run_steps(steps, state), oracle_steps(steps, state), io, f"step {io} {dk}x{dv}")
+    compare_steps(run_steps(steps, state, split=split), oracle_steps(steps, state), io,
+                  f"step {io} {dk}x{dv} split={split}")
 
 
-def test_steps_from_zero_state_and_out_of_place():
-    w = I.workload("decode_bf16", d_qk=64, d_v=64)
-    steps = PT.cuda(I.gen_decode_steps(w, range(10), B=2))
-    gpu = run_steps(steps, None, inplace=False)
-    compare_steps(gpu, oracle_steps(steps, None), "bf16", "step zero state")
+def test_split_matches_one_workgroup():
+    """The row split sums the same products in another order: it agrees with
+    the one-workgroup kernel to rounding, over a run of in-place steps."""
+    w = I.workload("decode_bf16", io="f32")
+    steps = PT.cuda(I.gen_decode_steps(w, range(12), B=2))
+    state = tuple(x.cuda() for x in I.gen_decode_state(w, B=2))
+    a = run_steps(steps, state, split=True)
+    b = run_steps(steps, state, split=False)
+    for x, y in zip(a, b):
+        scale = y.abs().max().item()
+        assert (x - y).abs().max().item() <= 1e-5 * scale, (x - y).abs().max().item()
+
+
+def test_workspace_is_scratch():
+    """The workspace needs no initial contents (filled with NaN here) and one
+    buffer serves calls of different shapes in stream order."""
+    ws = binding.step_workspace(3, 8, 256, 512, torch.bfloat16, "cuda")
+    ws.view(torch.float32).fill_(float("nan"))
+    for dk, dv, B in ((256, 512, 3), (80, 512, 2), (256, 256, 3), (208, 512, 1), (256, 512, 2)):
+        w = I.workload("decode_bf16", d_qk=dk, d_v=dv)
+        steps = PT.cuda(I.gen_decode_steps(w, range(3), B=B))
+        state = tuple(x.cuda() for x in I.gen_decode_state(w, B=B))
+        C, n, m = (x.clone() for x in state)
+        hs = []
+        for t in range(3):
+            h, C, n, m = binding.step(*(steps[k][t] for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")),
+                                      C, n, m, workspace=ws)
+            hs.append(h)
+        torch.cuda.synchronize()
+        compare_steps((torch.stack(hs, dim=2), C, n, m), oracle_steps(steps, state), "bf16",
+                      f"shared workspace {dk}x{dv} B={B}")
 
 
 def test_inplace_equals_out_of_place_bitwise():
@@ -104,11 +140,12 @@ def test_decode_full_size_sampled():
     inputs_sample = {k: [] for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")}
     gates = {"i_pre": [], "f_pre": []}
     chunk = 64
+    ws = binding.step_workspace(w.B, w.H, w.d_qk, w.d_v, torch.bfloat16, C.device)
     for t0 in range(0, S, chunk):
         st = PT.cuda(I.gen_decode_steps(w, range(t0, min(S, t0 + chunk)), threads=16))
         for t in range(st["q"].shape[0]):
             h, C, n, m = binding.step(*(st[k][t] for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")),
-                                      C, n, m)
+                                      C, n, m, workspace=ws)
             hs_sample.append(h.reshape(w.B * w.H, -1)[pairs].cpu())
         for k in gates:
             gates[k].append(st[k].reshape(st[k].shape[0], -1).cpu())

@@ -31,7 +31,8 @@ SIGNATURES = {
     "mlstm_fwd_chunkwise_schedule": (_i, [_i] * 8 + [ctypes.POINTER(_i)] * 2),
     "mlstm_fwd_chunkwise": (_i, [_vp] * 13 + [_i] * 7 + [_vp, _sz, _vp]),
     "mlstm_fwd_chunkwise_variant": (_i, [_vp] * 13 + [_i] * 8 + [_vp, _sz, _vp]),
-    "mlstm_step": (_i, [_vp] * 13 + [_i] * 5 + [_vp]),
+    "mlstm_step_workspace_size": (_i, [_i] * 5 + [ctypes.POINTER(_sz)]),
+    "mlstm_step": (_i, [_vp] * 13 + [_i] * 5 + [_vp, _sz, _vp]),
     "mlstm_bwd_chunkwise_workspace_size": (_i, [_i] * 7 + [ctypes.POINTER(_sz)]),
     "mlstm_bwd_chunkwise": (_i, [_vp] * 19 + [_i] * 7 + [_vp, _sz, _vp]),
 }
@@ -210,14 +211,31 @@ def bwd_chunkwise(q, k, v, i_pre, f_pre, o_pre, dh, C0=None, n0=None, m0=None, *
     return out
 
 
+def step_workspace_size(B, H, d_qk, d_v, io: int) -> int:
+    """Bytes of workspace mlstm_step can use for this shape (0: none)."""
+    n = ctypes.c_size_t(0)
+    _check(lib().mlstm_step_workspace_size(B, H, d_qk, d_v, io, ctypes.byref(n)))
+    return n.value
+
+
+def step_workspace(B, H, d_qk, d_v, io_dtype, device):
+    """A workspace for mlstm_step (None when the shape uses none): scratch that
+    any later calls on the same stream may reuse."""
+    import torch
+    n = step_workspace_size(B, H, d_qk, d_v, BF16 if io_dtype == torch.bfloat16 else F32)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def step(q, k, v, i_pre, f_pre, o_pre, C=None, n=None, m=None, *, h=None, C_out=None,
-         n_out=None, m_out=None, inplace: bool = True):
+         n_out=None, m_out=None, inplace: bool = True, split: bool = True, workspace=None):
     """One recurrent step for B*H cells.
 
     q, k [B,H,d_qk], v, o_pre [B,H,d_v]; i_pre, f_pre [B,H]; state (C [B,H,d_qk,
     d_v], n [B,H,d_qk], m [B,H]) float32 or None for the zero state.  With
     ``inplace`` (default) and a state given, the state tensors are updated in
-    place.  Returns (h, C_out, n_out, m_out)."""
+    place.  ``split`` runs the row-split kernel where the shape has one, with
+    ``workspace`` (from step_workspace; a fresh one per call when None); ``split=False`` streams each cell with one workgroup.  Returns (h,
+    C_out, n_out, m_out)."""
     import torch
     dev = q.device
     if dev.type != "cuda":
@@ -238,8 +256,13 @@ def step(q, k, v, i_pre, f_pre, o_pre, C=None, n=None, m=None, *, h=None, C_out=
             C_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
             n_out = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
             m_out = torch.empty((B, H), dtype=torch.float32, device=dev)
+    if not split:
+        workspace = None
+    elif workspace is None:
+        workspace = step_workspace(B, H, dk, dv, io_t, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mlstm_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(o_pre),
         _ptr(C), _ptr(n), _ptr(m), _ptr(h), _ptr(C_out), _ptr(n_out), _ptr(m_out),
-        B, H, dk, dv, _io(q), _stream(dev)))
+        B, H, dk, dv, _io(q), _ptr(workspace), ws_bytes, _stream(dev)))
     return h, C_out, n_out, m_out

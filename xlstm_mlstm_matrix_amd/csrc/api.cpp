@@ -257,11 +257,24 @@ mlstm_status_t mlstm_fwd_chunkwise(const void *q, const void *k, const void *v, 
                                        workspace_bytes, stream);
 }
 
+mlstm_status_t mlstm_step_workspace_size(int B, int H, int d_qk, int d_v, mlstm_dtype_t io,
+                                         size_t *bytes) {
+    if (!bytes) return MLSTM_ERR_NULL;
+    *bytes = 0;
+    if (B <= 0 || H <= 0 || d_qk <= 0 || d_v <= 0) return MLSTM_ERR_SHAPE;
+    if (io != MLSTM_F32 && io != MLSTM_BF16) return MLSTM_ERR_UNSUPPORTED;
+    if (!dims_ok(d_qk, d_v)) return MLSTM_ERR_UNSUPPORTED;
+    size_t BH;
+    if (!mul_ok((size_t)B, (size_t)H, &BH) || BH > (size_t)INT32_MAX) return MLSTM_ERR_SHAPE;
+    *bytes = step_workspace_bytes(BH, d_qk, d_v);
+    return MLSTM_OK;
+}
+
 mlstm_status_t mlstm_step(const void *q, const void *k, const void *v, const float *i_pre,
                           const float *f_pre, const void *o_pre, const float *C_in,
                           const float *n_in, const float *m_in, void *h, float *C_out, float *n_out,
                           float *m_out, int B, int H, int d_qk, int d_v, mlstm_dtype_t io,
-                          void *stream) {
+                          void *workspace, size_t workspace_bytes, void *stream) {
     if (!q || !k || !v || !i_pre || !f_pre || !o_pre || !h || !C_out || !n_out || !m_out)
         return MLSTM_ERR_NULL;
     if (B <= 0 || H <= 0 || d_qk <= 0 || d_v <= 0) return MLSTM_ERR_SHAPE;
@@ -271,7 +284,8 @@ mlstm_status_t mlstm_step(const void *q, const void *k, const void *v, const flo
     if (!mul_ok((size_t)B, (size_t)H, &BH) || BH > (size_t)INT32_MAX) return MLSTM_ERR_SHAPE;
     const int in0 = (C_in != nullptr) + (n_in != nullptr) + (m_in != nullptr);
     if (in0 != 0 && in0 != 3) return MLSTM_ERR_STATE_ARGS;
-    if (!all_aligned({q, k, v, i_pre, f_pre, o_pre, C_in, n_in, m_in, h, C_out, n_out, m_out}))
+    if (!all_aligned({q, k, v, i_pre, f_pre, o_pre, C_in, n_in, m_in, h, C_out, n_out, m_out,
+                      workspace}))
         return MLSTM_ERR_ALIGN;
 
     const size_t es = io == MLSTM_BF16 ? 2 : 4;
@@ -296,6 +310,22 @@ mlstm_status_t mlstm_step(const void *q, const void *k, const void *v, const flo
     a.C_in = C_in; a.n_in = n_in; a.m_in = m_in;
     a.h = h; a.C_out = C_out; a.n_out = n_out; a.m_out = m_out;
     a.BH = (int)BH; a.dk = d_qk; a.dv = d_v;
+    a.nb = 1; a.rows = d_qk;
+    // with a workspace, large memories are split into row blocks (one
+    // workgroup each); without one, one workgroup streams each pair
+    const size_t need = step_workspace_bytes(BH, d_qk, d_v);
+    if (workspace && need > 0) {
+        if (workspace_bytes < need) return MLSTM_ERR_WORKSPACE;
+        const Range rws = rng(workspace, need);
+        for (const Range &r : inputs)
+            if (overlaps(rws, r)) return MLSTM_ERR_ALIAS;
+        for (const Range &r : outs)
+            if (overlaps(rws, r)) return MLSTM_ERR_ALIAS;
+        a.rows = step_rows_per_block(d_qk, d_v);
+        a.nb = (d_qk + a.rows - 1) / a.rows;
+        if (BH > (size_t)INT32_MAX / (size_t)a.nb) return MLSTM_ERR_SHAPE;
+        a.part = static_cast<float *>(workspace);
+    }
     hipError_t e = launch_step(a, io == MLSTM_BF16, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MLSTM_OK : MLSTM_ERR_HIP;
 }

@@ -61,6 +61,10 @@ struct StepArgs {
     void *h;
     float *C_out, *n_out, *m_out;
     int BH, dk, dv;
+    // row split (nb > 1): workgroup (pair, block) owns rows [block*rows,
+    // min(dk, (block+1)*rows)); partial read-outs go to part [BH][nb][dv + 4]
+    int nb, rows;
+    float *part;
 };
 
 // Arguments of the backward kernels.
@@ -88,6 +92,9 @@ __host__ __device__ inline size_t bwd_ckpt_floats(int T, int dk, int dv) {
 
 // Launchers (defined in the .hip files).  Return hipSuccess or the launch error.
 hipError_t launch_step(const StepArgs &a, int io_bf16, hipStream_t s);
+// rows per block of the step's row split and the workspace it needs (0: no split)
+int step_rows_per_block(int dk, int dv);
+size_t step_workspace_bytes(size_t BH, int dk, int dv);
 hipError_t launch_fused(const FwdArgs &a, int io_bf16, int chunk, int state_only, hipStream_t s);
 hipError_t launch_seg_combine(const FwdArgs &a, float *ws, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs &a, int io_bf16, hipStream_t s);

@@ -68,24 +68,37 @@ def read_counter(path: str, counter: str):
 
 
 def median_for(readings, regex: str):
-    vals = [v for (n, v) in readings.values() if re.search(regex, n)]
-    if not vals:
+    """Median reading per dispatch of the kernels matching regex; when several
+    kernels match (a step made of more than one launch, each launched once per
+    step) the sum of each kernel's median: the reading per step."""
+    by_name = {}
+    for (n, v) in readings.values():
+        if re.search(regex, n):
+            by_name.setdefault(n, []).append(v)
+    if not by_name:
         raise SystemExit(f"no dispatch matches {regex!r}")
-    return statistics.median(vals), len(vals)
+    return (sum(statistics.median(v) for v in by_name.values()),
+            min(len(v) for v in by_name.values()))
 
 
-def kernel_runs(trace_csv: str, min_len: int = 3):
-    """Runs of consecutive dispatches of one kernel: (name, first dispatch id,
-    durations in ns)."""
+def kernel_runs(trace_csv: str, min_len: int = 3, span: int = 2):
+    """Runs of dispatches of one kernel: (name, first dispatch id, durations
+    in ns).  A run goes on while the kernel's next dispatch comes at most
+    `span` dispatches later, so a kernel that alternates with another one (a
+    step of two launches) still forms one run."""
     with open(trace_csv, newline="") as f:
         rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
-    runs = []
-    for r in rows:
+    runs, open_run = [], {}
+    for i, r in enumerate(rows):
         d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-        if runs and runs[-1][0] == r["Kernel_Name"]:
-            runs[-1][2].append(d)
+        name = r["Kernel_Name"]
+        if name in open_run and i - open_run[name][0] <= span:
+            open_run[name][1][2].append(d)
+            open_run[name][0] = i
         else:
-            runs.append((r["Kernel_Name"], int(r["Dispatch_Id"]), [d]))
+            run = (name, int(r["Dispatch_Id"]), [d])
+            runs.append(run)
+            open_run[name] = [i, run]
     return [x for x in runs if len(x[2]) >= min_len]
 
 
@@ -136,7 +149,7 @@ def traffic(name: str, kernel_regex: str, fetch_csv: str, write_csv: str, out_di
     os.makedirs(out_dir, exist_ok=True)
     with open(os.path.join(out_dir, f"{name}_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
-    md = [f"# HBM traffic of `{kernel_regex}` ({name})", "",
+    md = [f"# HBM traffic of `{kernel_regex}` ({name}, per step: the sum over the matching kernels)", "",
           "Counter passes (repository root, one MI355X), one counter each:", "",
           "```", fetch_cmd, write_cmd, "```", "",
           f"- FETCH_SIZE median per dispatch: {kf:.0f} ({nkf} dispatches)",
