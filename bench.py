@@ -70,7 +70,7 @@ def traffic_record(name):
     with open(p) as f:
         rec = json.load(f)
     from xlstm_mlstm_matrix_amd.rocprof_summary import src_hash
-    if rec.get("kernel_src_sha") != src_hash():
+    if rec.get("kernel_src_sha") != src_hash(name):
         return None
     return rec.get("bytes_per_launch")
 

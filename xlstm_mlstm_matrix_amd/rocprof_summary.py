@@ -38,15 +38,27 @@ PROBE_REGEX = r"neg"
 PROBE_BYTES = 1 << 30
 
 
-def kernel_sources():
+# the device-code files each measured line's kernels are compiled from (a
+# change to any of them invalidates that line's measured traffic)
+KERNEL_FILES = {
+    "prefill_7b": ["common.hpp", "prefill.hip", "prefill_ws.hpp", "prefill_bf16.hpp",
+                   "prefill_kernel.hpp"],
+    "decode": ["common.hpp", "step.hip"],
+}
+
+
+def kernel_sources(name=None):
+    if name is not None:
+        return [os.path.join(CSRC, f) for f in KERNEL_FILES[name]]
     return sorted(os.path.join(CSRC, f) for f in os.listdir(os.path.join(ROOT, CSRC))
                   if f.endswith((".hip", ".hpp", ".cpp")))
 
 
-def src_hash() -> str:
-    """Hash of every kernel source file (a change invalidates measured traffic)."""
+def src_hash(name=None) -> str:
+    """Hash of the kernel source files of one measured line (all of them when
+    name is None)."""
     h = hashlib.sha256()
-    for p in kernel_sources():
+    for p in kernel_sources(name):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -136,7 +148,8 @@ def traffic(name: str, kernel_regex: str, fetch_csv: str, write_csv: str, out_di
     pw, npw = median_for(wr, PROBE_REGEX)
     sf, sw = PROBE_BYTES / pf, PROBE_BYTES / pw  # bytes per counter unit
     rec = {
-        "kernel_regex": kernel_regex, "kernel_src_sha": src_hash(),
+        "kernel_regex": kernel_regex, "kernel_src_sha": src_hash(name),
+        "kernel_files": KERNEL_FILES[name],
         "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
         "dispatches": [nkf, nkw],
         "probe": {"kernel_regex": PROBE_REGEX, "bytes_read": PROBE_BYTES, "bytes_written": PROBE_BYTES,
