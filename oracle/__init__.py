@@ -4,7 +4,9 @@ infrastructure).
 Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg may import this package.  It wraps ``mlstm_ref.c`` (the plain sequential
 recurrence in float64, see that file's header for the equations and their
-sources) through ctypes, and shares no code with the HIP library.
+sources) through ctypes, and shares no code with the HIP library.  The
+submodule ``oracle.layer`` adds the layer's input projections (float64
+matrix products) in front of that recurrence.
 """
 from __future__ import annotations
 
