@@ -16,7 +16,11 @@ head):
 - the (batch, head) cells are ordered head-major: cell p = h*B + b, so every
   per-cell tensor is [H, B, ...];
 - the cell is the oracle's sequential recurrence (``oracle.forward``) from the
-  given state or the zero state.
+  given state or the zero state;
+- with bfloat16 I/O the cell's inputs q, k, v and o~ are bfloat16 tensors,
+  so the float64 projections are rounded to bfloat16 (to nearest, ties to
+  even, straight from float64) before the cell; the gate pre-activations stay
+  float64.
 
 Each projection is a float64 matrix product (a library primitive), nothing
 fused or reordered.
@@ -27,7 +31,16 @@ import numpy as np
 
 from . import forward as cell_forward
 
-__all__ = ["layer_forward", "projections"]
+__all__ = ["layer_forward", "projections", "round_bf16"]
+
+
+def round_bf16(a):
+    """float64 -> the nearest bfloat16 value (8 significant bits, ties to
+    even), returned as float64; normal range only (no overflow or subnormal
+    handling, none occur here)."""
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)                         # a = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
 
 
 def _f64(x):
@@ -56,12 +69,16 @@ def projections(x, W_q, W_k, W_v, W_o, W_i, W_f, b_q, b_k, b_v, b_o, b_i, b_f):
 
 
 def layer_forward(x, W_q, W_k, W_v, W_o, W_i, W_f, b_q, b_k, b_v, b_o, b_i, b_f,
-                  C0=None, n0=None, m0=None, threads: int = 0):
+                  C0=None, n0=None, m0=None, io: str = "f32", threads: int = 0):
     """x [B, T, d_model]; weights and biases as in ``projections``; optional
-    state C0 [H, B, d_qk, d_v], n0 [H, B, d_qk], m0 [H, B].  Returns h [H, B,
-    T, d_v] and the final state (C [H, B, d_qk, d_v], n [H, B, d_qk], m [H,
-    B]), float64."""
+    state C0 [H, B, d_qk, d_v], n0 [H, B, d_qk], m0 [H, B]; io "f32" or
+    "bf16" (the cell's I/O dtype).  Returns h [H, B, T, d_v] and the final
+    state (C [H, B, d_qk, d_v], n [H, B, d_qk], m [H, B]), float64."""
     q, k, v, o, i, f = projections(x, W_q, W_k, W_v, W_o, W_i, W_f, b_q, b_k, b_v, b_o, b_i, b_f)
+    if io == "bf16":
+        q, k, v, o = (round_bf16(a) for a in (q, k, v, o))
+    elif io != "f32":
+        raise ValueError(f"unknown io dtype {io!r}")
     H, B, T, dk = q.shape
     dv = v.shape[-1]
     P = H * B

@@ -101,6 +101,36 @@ def test_single_token_closed_form():
     pin_single_token(L.layer_forward)
 
 
+def test_bf16_rounding():
+    """round_bf16 against torch's own bfloat16 cast on float32 values (one
+    rounding either way there), on ties, and on its defining properties."""
+    import torch
+    rng = np.random.default_rng(11)
+    a = rng.normal(0.0, 1.0, 100000).astype(np.float32).astype(np.float64) * 2.0 ** rng.integers(-20, 20, 100000)
+    t = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(L.round_bf16(a), t)
+    # ties go to the even neighbour: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7
+    assert L.round_bf16(1.0 + 2.0 ** -8) == 1.0
+    assert L.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert L.round_bf16(-(1.0 + 2.0 ** -8)) == -1.0
+    # idempotent, and within half an ulp (2^-9 relative) of the input
+    r = L.round_bf16(a)
+    np.testing.assert_array_equal(L.round_bf16(r), r)
+    assert np.all(np.abs(r - a) <= np.abs(a) * 2.0 ** -8)
+
+
+def test_bf16_io_rounds_the_cell_inputs():
+    """With bf16 I/O the layer equals the cell on the rounded selection
+    outputs."""
+    args, c = selection_case()
+    h, C, n, m = L.layer_forward(*args, io="bf16")
+    rd = {k: (L.round_bf16(c[k]) if k in "qkvo" else c[k]) for k in c}
+    hr, Cr, nr, mr = oracle.forward(rd["q"], rd["k"], rd["v"], rd["i"], rd["f"], rd["o"])
+    np.testing.assert_allclose(h.reshape(H * B, T, DV), hr, rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        L.layer_forward(*args, io="f16")
+
+
 def test_shapes_and_dtypes_of_projections():
     args, _ = selection_case()
     q, k, v, o, i, f = L.projections(*args)
