@@ -20,7 +20,9 @@
  * Three entry points compute it or its gradients:
  *   mlstm_fwd_chunkwise -- a whole sequence, chunkwise-parallel (prefill);
  *   mlstm_step          -- one token of the recurrence (decode);
- *   mlstm_bwd_chunkwise -- gradients of a whole sequence (training).
+ *   mlstm_bwd_chunkwise -- gradients of a whole sequence (training);
+ * and mlstm_layer_fwd runs the layer's input projections in front of the
+ * first of them.
  *
  * Conventions shared by every call:
  *  - All tensor pointers are DEVICE pointers (HIP memory on the current
@@ -28,6 +30,7 @@
  *    caller owns every buffer; the library allocates nothing, keeps no state
  *    between calls and never synchronizes: work is enqueued on `stream`
  *    (a hipStream_t; NULL = the null stream) and the call returns at once.
+ *    (Exception: mlstm_layer_fwd keeps a hipBLASLt handle per device.)
  *  - q, k, v, o_pre and h have the I/O dtype `io` (float32 or bfloat16);
  *    i_pre, f_pre and the state (C, n, m) are always float32.
  *  - Every pointer, workspace included, must be 16-byte aligned (the kernels
@@ -69,7 +72,8 @@ typedef enum {
     MLSTM_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the query says */
     MLSTM_ERR_ALIAS = 6,       /* buffers overlap in a way the call does not allow */
     MLSTM_ERR_HIP = 7,         /* the HIP runtime reported an error */
-    MLSTM_ERR_ALIGN = 8        /* a pointer is not 16-byte aligned */
+    MLSTM_ERR_ALIGN = 8,       /* a pointer is not 16-byte aligned */
+    MLSTM_ERR_BLAS = 9         /* a hipBLASLt call failed (layer projections) */
 } mlstm_status_t;
 
 /* Kernel strategy of the chunkwise forward (the result is the same up to
@@ -238,6 +242,53 @@ mlstm_status_t mlstm_bwd_chunkwise(const void *q, const void *k, const void *v,
                                    int B, int H, int T, int d_qk, int d_v, int chunk,
                                    mlstm_dtype_t io, void *workspace, size_t workspace_bytes,
                                    void *stream);
+
+/*
+ * Bytes of device workspace mlstm_layer_fwd needs for this shape (the
+ * projected q, k, v, o~, the gate pre-activations, the cell's workspace and
+ * 32 MiB for the GEMMs).  Unsupported shape -> as mlstm_layer_fwd.
+ */
+mlstm_status_t mlstm_layer_fwd_workspace_size(int B, int T, int d_model, int H, int d_qk, int d_v,
+                                              int chunk, mlstm_dtype_t io, size_t *bytes);
+
+/*
+ * The mLSTM layer forward: the input projections of the xLSTM notes' example
+ * mLSTM module (section "mLSTM", its listing of the recurrent forward: linear
+ * maps with bias from each token to the query, key, value, output-gate
+ * pre-activation and scalar input- and forget-gate pre-activations), then the
+ * chunkwise cell of mlstm_fwd_chunkwise over every (head, batch) cell.  The
+ * forget pre-activation is the log of the forget gate, as in the cell.
+ *
+ *  x         [B, T, d_model]        io dtype; d_model a multiple of 8
+ *  W_q, W_k  [H, d_qk, d_model]     io dtype (row-major: out x in, per head)
+ *  W_v, W_o  [H, d_v, d_model]      io dtype
+ *  W_i, W_f  [H, d_model]           io dtype
+ *  b_q, b_k  [H, d_qk]; b_v, b_o [H, d_v]; b_i, b_f [H]   float32
+ *  C0, n0, m0  [H, B, d_qk, d_v], [H, B, d_qk], [H, B] float32, or all NULL
+ *  h         [H, B, T, d_v]         io dtype (written)
+ *  C_T, n_T, m_T  [H, B, ...] float32, or all NULL
+ *  chunk, io as for mlstm_fwd_chunkwise (d_qk, d_v, chunk: its rules)
+ *  workspace at least mlstm_layer_fwd_workspace_size bytes
+ *
+ * Cells are ordered head-major (h, then b) in every per-cell tensor: one
+ * head's projection of all tokens is then one GEMM writing the cell's layout.
+ * The projections run on hipBLASLt (fp32 accumulation, q, k, v, o~ rounded to
+ * the io dtype, gate pre-activations kept in float32); the library creates
+ * one hipBLASLt handle per device on first use and keeps it, with the
+ * algorithm chosen per GEMM shape, until the process ends.  Errors: as
+ * mlstm_fwd_chunkwise, plus MLSTM_ERR_BLAS when a hipBLASLt call fails (the
+ * projections enqueued before it may have run); inputs overlapping an output
+ * or the workspace -> MLSTM_ERR_ALIAS.
+ */
+mlstm_status_t mlstm_layer_fwd(const void *x, const void *W_q, const void *W_k, const void *W_v,
+                               const void *W_o, const void *W_i, const void *W_f,
+                               const float *b_q, const float *b_k, const float *b_v,
+                               const float *b_o, const float *b_i, const float *b_f,
+                               const float *C0, const float *n0, const float *m0,
+                               void *h, float *C_T, float *n_T, float *m_T,
+                               int B, int T, int d_model, int H, int d_qk, int d_v, int chunk,
+                               mlstm_dtype_t io, void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 #ifdef __cplusplus
 }

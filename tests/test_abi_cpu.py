@@ -37,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s+(mlstm_\w+)", out))
@@ -48,7 +48,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for s in range(9):
+    for s in range(10):
         assert B.status_string(s).startswith(B.STATUS[s])
     assert "unknown" in B.status_string(99)
     assert lib.mlstm_version().decode().startswith("mlstm-gfx950")
@@ -328,3 +328,68 @@ def test_misaligned_pointers_rejected(lib):
     b = bwd_args()
     for key in ("q", "dh", "gq", "gf", "gC0", "ws"):
         assert bwd_call(b, **{key: b[key] + 2}) == ALIGN, key
+
+
+# ---- layer: host-side validation only (every call below returns before any
+# device work; the fake addresses are never dereferenced)
+
+def lws(*args):
+    n = ctypes.c_size_t(12345)
+    s = B.lib().mlstm_layer_fwd_workspace_size(*args, ctypes.byref(n))
+    return s, n.value
+
+
+def test_layer_workspace_query(lib):
+    # B=2 T=70 d_model=64 H=3 d_qk=16 d_v=32 chunk 32 float32: 32 MiB for the
+    # GEMMs, then q, k, v, o~, i~, f~ of the 3*2 cells (each padded to 256
+    # bytes), then the cell's own workspace
+    s, n = lws(2, 70, 64, 3, 16, 32, 32, B.F32)
+    cell = ctypes.c_size_t(0)
+    assert B.lib().mlstm_fwd_chunkwise_workspace_size(3, 2, 70, 16, 32, 32, B.F32, ctypes.byref(cell)) == OK
+    up = lambda x: (x + 255) // 256 * 256
+    HBT = 3 * 2 * 70
+    assert s == OK
+    assert n == (32 << 20) + 2 * up(HBT * 16 * 4) + 2 * up(HBT * 32 * 4) + 2 * up(HBT * 4) + up(cell.value)
+    assert lws(2, 70, 60, 3, 16, 32, 32, B.F32)[0] == UNSUP    # d_model not a multiple of 8
+    assert lws(2, 70, 64, 3, 24, 32, 32, B.F32)[0] == UNSUP    # d_qk
+    assert lws(2, 70, 64, 3, 16, 32, 48, B.F32)[0] == UNSUP    # chunk
+    assert lws(0, 70, 64, 3, 16, 32, 32, B.F32)[0] == SHAPE
+    assert lws(2, 70, 64, 3, 16, 32, 32, 4)[0] == UNSUP        # dtype
+    assert B.lib().mlstm_layer_fwd_workspace_size(1, 1, 8, 1, 16, 16, 16, 0, None) == NULL
+
+
+def layer_args(B_=2, T=70, D=64, H=3, dk=16, dv=32, io=B.BF16):
+    fa = Fake()
+    es = 2 if io == B.BF16 else 4
+    a = dict(x=fa(B_ * T * D * es), Wq=fa(H * dk * D * es), Wk=fa(H * dk * D * es),
+             Wv=fa(H * dv * D * es), Wo=fa(H * dv * D * es), Wi=fa(H * D * es), Wf=fa(H * D * es),
+             bq=fa(H * dk * 4), bk=fa(H * dk * 4), bv=fa(H * dv * 4), bo=fa(H * dv * 4), bi=fa(H * 4),
+             bf=fa(H * 4), C0=None, n0=None, m0=None, h=fa(H * B_ * T * dv * es),
+             CT=None, nT=None, mT=None, dims=(B_, T, D, H, dk, dv, 32, io))
+    a["wsn"] = lws(*a["dims"])[1]
+    a["ws"] = fa(a["wsn"])
+    return a
+
+
+def call_layer(a):
+    k = ("x", "Wq", "Wk", "Wv", "Wo", "Wi", "Wf", "bq", "bk", "bv", "bo", "bi", "bf", "C0", "n0", "m0",
+         "h", "CT", "nT", "mT")
+    return B.lib().mlstm_layer_fwd(*(a[x] for x in k), *a["dims"], a["ws"], a["wsn"], None)
+
+
+def test_layer_validation(lib):
+    for key in ("x", "Wq", "Wk", "Wv", "Wo", "Wi", "Wf", "bq", "bk", "bv", "bo", "bi", "bf", "h"):
+        a = layer_args(); a[key] = None
+        assert call_layer(a) == NULL, key
+    a = layer_args(); a["dims"] = (2, 70, 60, 3, 16, 32, 32, B.BF16)
+    assert call_layer(a) == UNSUP
+    a = layer_args(); a["wsn"] -= 16
+    assert call_layer(a) == WS
+    a = layer_args(); a["ws"] = None
+    assert call_layer(a) == WS
+    a = layer_args(); a["Wq"] += 8
+    assert call_layer(a) == 8   # MLSTM_ERR_ALIGN
+    a = layer_args(); a["h"] = a["x"]
+    assert call_layer(a) == ALIAS
+    a = layer_args(); a["ws"] = a["Wv"]
+    assert call_layer(a) == ALIAS

@@ -18,7 +18,7 @@ F32, BF16 = 0, 1
 VARIANTS = {"auto": 0, "fused": 1, "segscan": 2}
 STATUS = {0: "MLSTM_OK", 1: "MLSTM_ERR_NULL", 2: "MLSTM_ERR_SHAPE", 3: "MLSTM_ERR_UNSUPPORTED",
           4: "MLSTM_ERR_STATE_ARGS", 5: "MLSTM_ERR_WORKSPACE", 6: "MLSTM_ERR_ALIAS",
-          7: "MLSTM_ERR_HIP", 8: "MLSTM_ERR_ALIGN"}
+          7: "MLSTM_ERR_HIP", 8: "MLSTM_ERR_ALIGN", 9: "MLSTM_ERR_BLAS"}
 
 # exported entry points and their C signatures (kept in step with include/mlstm.h)
 _vp, _fp, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
@@ -35,6 +35,8 @@ SIGNATURES = {
     "mlstm_step": (_i, [_vp] * 13 + [_i] * 5 + [_vp, _sz, _vp]),
     "mlstm_bwd_chunkwise_workspace_size": (_i, [_i] * 7 + [ctypes.POINTER(_sz)]),
     "mlstm_bwd_chunkwise": (_i, [_vp] * 19 + [_i] * 7 + [_vp, _sz, _vp]),
+    "mlstm_layer_fwd_workspace_size": (_i, [_i] * 8 + [ctypes.POINTER(_sz)]),
+    "mlstm_layer_fwd": (_i, [_vp] * 20 + [_i] * 8 + [_vp, _sz, _vp]),
 }
 
 
@@ -209,6 +211,54 @@ def bwd_chunkwise(q, k, v, i_pre, f_pre, o_pre, dh, C0=None, n0=None, m0=None, *
     if state_grad:
         return out + (gC0, gn0, gm0)
     return out
+
+
+def layer_workspace_size(B, T, d_model, H, d_qk, d_v, chunk, io: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().mlstm_layer_fwd_workspace_size(B, T, d_model, H, d_qk, d_v, chunk, io, ctypes.byref(n)))
+    return n.value
+
+
+def layer_fwd(x, W_q, W_k, W_v, W_o, W_i, W_f, b_q, b_k, b_v, b_o, b_i, b_f, C0=None, n0=None,
+              m0=None, *, chunk: int = 64, return_state: bool = True, workspace=None):
+    """The mLSTM layer forward (input projections, then the chunkwise cell).
+
+    x [B,T,d_model]; W_q, W_k [H,d_qk,d_model]; W_v, W_o [H,d_v,d_model];
+    W_i, W_f [H,d_model] (all the I/O dtype); biases float32 b_q, b_k [H,d_qk],
+    b_v, b_o [H,d_v], b_i, b_f [H]; optional state C0 [H,B,d_qk,d_v], n0
+    [H,B,d_qk], m0 [H,B].  Cells are head-major.  Returns h [H,B,T,d_v], or
+    (h, (C_T, n_T, m_T)) with ``return_state``."""
+    import torch
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    io_t = x.dtype
+    B, T, D = x.shape
+    H, dk = W_q.shape[0], W_q.shape[1]
+    dv = W_v.shape[1]
+    for name, t in (("x", x), ("W_q", W_q), ("W_k", W_k), ("W_v", W_v), ("W_o", W_o), ("W_i", W_i),
+                    ("W_f", W_f)):
+        _req(t, name, io_t, dev)
+    for name, t in (("b_q", b_q), ("b_k", b_k), ("b_v", b_v), ("b_o", b_o), ("b_i", b_i), ("b_f", b_f),
+                    ("C0", C0), ("n0", n0), ("m0", m0)):
+        _req(t, name, torch.float32, dev)
+    h = torch.empty((H, B, T, dv), dtype=io_t, device=dev)
+    C_T = n_T = m_T = None
+    if return_state:
+        f32 = dict(dtype=torch.float32, device=dev)
+        C_T, n_T, m_T = (torch.empty((H, B, dk, dv), **f32), torch.empty((H, B, dk), **f32),
+                         torch.empty((H, B), **f32))
+    io = _io(x)
+    if workspace is None:
+        workspace = torch.empty(layer_workspace_size(B, T, D, H, dk, dv, chunk, io), dtype=torch.uint8,
+                                device=dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    _check(lib().mlstm_layer_fwd(
+        _ptr(x), _ptr(W_q), _ptr(W_k), _ptr(W_v), _ptr(W_o), _ptr(W_i), _ptr(W_f),
+        _ptr(b_q), _ptr(b_k), _ptr(b_v), _ptr(b_o), _ptr(b_i), _ptr(b_f),
+        _ptr(C0), _ptr(n0), _ptr(m0), _ptr(h), _ptr(C_T), _ptr(n_T), _ptr(m_T),
+        B, T, D, H, dk, dv, chunk, io, _ptr(workspace), ws_len, _stream(dev)))
+    return (h, (C_T, n_T, m_T)) if return_state else h
 
 
 def step_workspace_size(B, H, d_qk, d_v, io: int) -> int:

@@ -7,9 +7,8 @@
 
 #include <stdint.h>
 
-#include <initializer_list>
-
 #include "common.hpp"
+#include "hostcheck.hpp"
 
 using namespace mlstm;
 
@@ -25,33 +24,12 @@ const char *kStatus[] = {
     "MLSTM_ERR_ALIAS: buffers overlap in a way this call does not allow",
     "MLSTM_ERR_HIP: the HIP runtime reported an error",
     "MLSTM_ERR_ALIGN: a pointer is not 16-byte aligned",
+    "MLSTM_ERR_BLAS: a hipBLASLt call failed",
 };
 
 constexpr int kMaxDk = 256, kMaxDv = 512;
 constexpr int kTargetWorkgroups = 256;  // one workgroup per compute unit of an MI355X
 
-struct Range {
-    uintptr_t lo, hi;  // [lo, hi); empty when lo == hi
-};
-Range rng(const void *p, size_t bytes) {
-    uintptr_t a = (uintptr_t)p;
-    return Range{a, p ? a + bytes : a};
-}
-bool overlaps(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
-bool same(Range a, Range b) { return a.lo == b.lo && a.hi == b.hi && a.lo < a.hi; }
-
-// every pointer (NULL allowed) 16-byte aligned
-bool all_aligned(std::initializer_list<const void *> ps) {
-    for (const void *p : ps)
-        if ((uintptr_t)p & 15) return false;
-    return true;
-}
-
-bool mul_ok(size_t a, size_t b, size_t *out) {
-    if (a != 0 && b > SIZE_MAX / a) return false;
-    *out = a * b;
-    return true;
-}
 
 bool dims_ok(int dk, int dv) {
     return dk >= 16 && dk <= kMaxDk && dk % 16 == 0 && dv >= 16 && dv <= kMaxDv && dv % 16 == 0;

@@ -1,0 +1,262 @@
+// layer.hip -- the mLSTM layer forward: input projections, gates, the cell.
+//
+// The xLSTM notes' example mLSTM module (section "mLSTM", its listing of the
+// recurrent forward) maps each token x_t of width d_model through linear
+// layers with bias to the query, key, value and output-gate pre-activation,
+// and to one input-gate and one forget-gate pre-activation; the forget one is
+// the log of the forget gate in the stabilized recurrence.  Per head h:
+//   q = W_q[h] x + b_q[h],  k = W_k[h] x + b_k[h]          (d_qk)
+//   v = W_v[h] x + b_v[h],  o~ = W_o[h] x + b_o[h]         (d_v)
+//   i~ = W_i[h] . x + b_i[h],  f~ = W_f[h] . x + b_f[h]    (scalars)
+// then the chunkwise cell over each (head, batch) cell.
+//
+// Layout choice: cells are ordered head-major (cell p = h*B + b).  Then one
+// head's projection of every token of every batch is ONE plain GEMM with
+// M = d (the head's width), N = B*T tokens and K = d_model, whose
+// column-major result [d, B*T] is exactly the cell's row-major [B, T, d]
+// block of head h -- no permute pass.  The per-feature bias is hipBLASLt's
+// bias epilogue (one value per output row).  The gate pre-activations of
+// head h are the GEMM [B*T, H] = x W_i^T (column-major, so each head's B*T
+// values are contiguous: the cell's gate layout), float32 out; their biases
+// are added by a small kernel.  The cell is mlstm_fwd_chunkwise with the
+// (batch, head) roles of its B and H swapped.
+//
+// The projections are plain library GEMMs (hipBLASLt, bf16 or fp32 inputs,
+// fp32 accumulation).  The library keeps one hipBLASLt handle per device and
+// the algorithm it picked per GEMM shape, created on first use.
+#include <hipblaslt/hipblaslt.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "common.hpp"
+#include "hostcheck.hpp"
+#include "mlstm.h"
+
+namespace mlstm {
+namespace {
+
+constexpr size_t kGemmWorkspace = size_t(32) << 20;  // hipBLASLt's share of the workspace
+
+__global__ __launch_bounds__(256) void gate_bias_kernel(float *gi, float *gf, const float *bi,
+                                                        const float *bf, size_t per_head, int H) {
+    const size_t n = per_head * (size_t)H;
+    for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < n;
+         x += (size_t)gridDim.x * blockDim.x) {
+        const int h = (int)(x / per_head);
+        gi[x] += bi[h];
+        gf[x] += bf[h];
+    }
+}
+
+struct AlgoKey {
+    int dev, m, n, k, ab, d, bias;
+    bool operator<(const AlgoKey &o) const {
+        return std::tie(dev, m, n, k, ab, d, bias) < std::tie(o.dev, o.m, o.n, o.k, o.ab, o.d, o.bias);
+    }
+};
+
+std::mutex g_mu;
+std::map<int, hipblasLtHandle_t> g_handle;
+std::map<AlgoKey, hipblasLtMatmulAlgo_t> g_algo;
+
+hipblasLtHandle_t handle_for(int dev) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_handle.find(dev);
+    if (it != g_handle.end()) return it->second;
+    hipblasLtHandle_t h = nullptr;
+    if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) return nullptr;
+    g_handle[dev] = h;
+    return h;
+}
+
+// D (column-major m x n, leading dimension m) = A^T B (+ bias[row]), where A
+// is column-major k x m and B column-major k x n, both with leading dimension
+// k.  Row-major [m, k] weights and row-major [n, k] tokens are exactly such
+// A and B, and D then holds one token per column.
+mlstm_status_t gemm_tn(int dev, int m, int n, int k, const void *A, const void *Bm, void *D,
+                       hipDataType ab, hipDataType dt, const float *bias, void *ws, hipStream_t s) {
+    hipblasLtHandle_t h = handle_for(dev);
+    if (!h) return MLSTM_ERR_BLAS;
+    hipblasLtMatmulDesc_t desc = nullptr;
+    hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
+    hipblasLtMatmulPreference_t pref = nullptr;
+    mlstm_status_t st = MLSTM_ERR_BLAS;
+    const hipblasOperation_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
+    const hipblasLtEpilogue_t epi = bias ? HIPBLASLT_EPILOGUE_BIAS : HIPBLASLT_EPILOGUE_DEFAULT;
+    const hipDataType bias_t = HIP_R_32F;
+    const uint64_t wsb = kGemmWorkspace;
+    const float alpha = 1.0f, beta = 0.0f;
+    hipblasLtMatmulAlgo_t algo{};
+    bool have = false;
+    do {
+        if (hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F)) break;
+        if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT))) break;
+        if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN))) break;
+        if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_EPILOGUE, &epi, sizeof(epi))) break;
+        if (bias) {
+            if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)))
+                break;
+            if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bias_t,
+                                                sizeof(bias_t)))
+                break;
+        }
+        if (hipblasLtMatrixLayoutCreate(&la, ab, k, m, k)) break;
+        if (hipblasLtMatrixLayoutCreate(&lb, ab, k, n, k)) break;
+        if (hipblasLtMatrixLayoutCreate(&ld, dt, m, n, m)) break;
+        const AlgoKey key{dev, m, n, k, (int)ab, (int)dt, bias != nullptr};
+        {
+            std::lock_guard<std::mutex> lk(g_mu);
+            auto it = g_algo.find(key);
+            if (it != g_algo.end()) {
+                algo = it->second;
+                have = true;
+            }
+        }
+        if (!have) {
+            if (hipblasLtMatmulPreferenceCreate(&pref)) break;
+            if (hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb,
+                                                      sizeof(wsb)))
+                break;
+            hipblasLtMatmulHeuristicResult_t res[1];
+            int found = 0;
+            if (hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, ld, ld, pref, 1, res, &found) || found < 1)
+                break;
+            algo = res[0].algo;
+            std::lock_guard<std::mutex> lk(g_mu);
+            g_algo[key] = algo;
+        }
+        if (hipblasLtMatmul(h, desc, &alpha, A, la, Bm, lb, &beta, D, ld, D, ld, &algo, ws, kGemmWorkspace, s))
+            break;
+        st = MLSTM_OK;
+    } while (false);
+    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+    if (ld) hipblasLtMatrixLayoutDestroy(ld);
+    if (lb) hipblasLtMatrixLayoutDestroy(lb);
+    if (la) hipblasLtMatrixLayoutDestroy(la);
+    if (desc) hipblasLtMatmulDescDestroy(desc);
+    return st;
+}
+
+struct LayerPlan {
+    size_t es, BT, nq, nv, ng;           // element size; tokens; q/k, v/o, gate element counts
+    size_t off_q, off_k, off_v, off_o, off_i, off_f, off_cell, cell_bytes, total;
+};
+
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
+mlstm_status_t layer_plan(int B, int T, int D, int H, int dk, int dv, int chunk, mlstm_dtype_t io,
+                          LayerPlan *p) {
+    if (B <= 0 || T <= 0 || D <= 0 || H <= 0 || dk <= 0 || dv <= 0) return MLSTM_ERR_SHAPE;
+    if (io != MLSTM_F32 && io != MLSTM_BF16) return MLSTM_ERR_UNSUPPORTED;
+    if (D % 8 != 0) return MLSTM_ERR_UNSUPPORTED;  // rows of x and W 16-byte aligned
+    size_t BT, HBT;
+    if (!mul_ok((size_t)B, (size_t)T, &BT) || BT > (size_t)INT32_MAX) return MLSTM_ERR_SHAPE;
+    if (!mul_ok(BT, (size_t)H, &HBT) || HBT > ((size_t)1 << 40)) return MLSTM_ERR_SHAPE;
+    size_t cell = 0;
+    mlstm_status_t st = mlstm_fwd_chunkwise_workspace_size(H, B, T, dk, dv, chunk, io, &cell);
+    if (st != MLSTM_OK) return st;
+    p->es = io == MLSTM_BF16 ? 2 : 4;
+    p->BT = BT;
+    p->nq = HBT * dk;
+    p->nv = HBT * dv;
+    p->ng = HBT;
+    p->off_q = kGemmWorkspace;
+    p->off_k = p->off_q + up256(p->nq * p->es);
+    p->off_v = p->off_k + up256(p->nq * p->es);
+    p->off_o = p->off_v + up256(p->nv * p->es);
+    p->off_i = p->off_o + up256(p->nv * p->es);
+    p->off_f = p->off_i + up256(p->ng * 4);
+    p->off_cell = p->off_f + up256(p->ng * 4);
+    p->cell_bytes = cell;
+    p->total = p->off_cell + up256(cell);
+    return MLSTM_OK;
+}
+
+}  // namespace
+}  // namespace mlstm
+
+using namespace mlstm;
+
+extern "C" {
+
+mlstm_status_t mlstm_layer_fwd_workspace_size(int B, int T, int d_model, int H, int d_qk, int d_v,
+                                              int chunk, mlstm_dtype_t io, size_t *bytes) {
+    if (!bytes) return MLSTM_ERR_NULL;
+    *bytes = 0;
+    LayerPlan p;
+    const mlstm_status_t st = layer_plan(B, T, d_model, H, d_qk, d_v, chunk, io, &p);
+    if (st == MLSTM_OK) *bytes = p.total;
+    return st;
+}
+
+mlstm_status_t mlstm_layer_fwd(const void *x, const void *W_q, const void *W_k, const void *W_v,
+                               const void *W_o, const void *W_i, const void *W_f, const float *b_q,
+                               const float *b_k, const float *b_v, const float *b_o, const float *b_i,
+                               const float *b_f, const float *C0, const float *n0, const float *m0,
+                               void *h, float *C_T, float *n_T, float *m_T, int B, int T, int d_model,
+                               int H, int d_qk, int d_v, int chunk, mlstm_dtype_t io, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    if (!x || !W_q || !W_k || !W_v || !W_o || !W_i || !W_f || !b_q || !b_k || !b_v || !b_o || !b_i ||
+        !b_f || !h)
+        return MLSTM_ERR_NULL;
+    LayerPlan p;
+    mlstm_status_t st = layer_plan(B, T, d_model, H, d_qk, d_v, chunk, io, &p);
+    if (st != MLSTM_OK) return st;
+    if (!all_aligned({x, W_q, W_k, W_v, W_o, W_i, W_f, b_q, b_k, b_v, b_o, b_i, b_f, workspace}))
+        return MLSTM_ERR_ALIGN;
+    if (!workspace || workspace_bytes < p.total) return MLSTM_ERR_WORKSPACE;
+    // the layer's own inputs must not overlap its outputs or the workspace;
+    // the cell call below checks the state and h against everything it sees
+    const size_t es = p.es, D = (size_t)d_model;
+    const Range ins[] = {rng(x, p.BT * D * es),           rng(W_q, (size_t)H * d_qk * D * es),
+                         rng(W_k, (size_t)H * d_qk * D * es), rng(W_v, (size_t)H * d_v * D * es),
+                         rng(W_o, (size_t)H * d_v * D * es),  rng(W_i, (size_t)H * D * es),
+                         rng(W_f, (size_t)H * D * es),        rng(b_q, (size_t)H * d_qk * 4),
+                         rng(b_k, (size_t)H * d_qk * 4),      rng(b_v, (size_t)H * d_v * 4),
+                         rng(b_o, (size_t)H * d_v * 4),       rng(b_i, (size_t)H * 4),
+                         rng(b_f, (size_t)H * 4)};
+    const size_t nC = (size_t)H * B * d_qk * d_v, nn = (size_t)H * B * d_qk, nm = (size_t)H * B;
+    const Range outs[] = {rng(h, p.nv * es), rng(C_T, nC * 4), rng(n_T, nn * 4), rng(m_T, nm * 4),
+                          rng(workspace, p.total)};
+    for (const Range &i : ins)
+        for (const Range &o : outs)
+            if (overlaps(i, o)) return MLSTM_ERR_ALIAS;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MLSTM_ERR_HIP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    const hipDataType ab = io == MLSTM_BF16 ? HIP_R_16BF : HIP_R_32F;
+    char *q = ws + p.off_q, *k = ws + p.off_k, *v = ws + p.off_v, *o = ws + p.off_o;
+    float *gi = reinterpret_cast<float *>(ws + p.off_i), *gf = reinterpret_cast<float *>(ws + p.off_f);
+    const char *Wq = static_cast<const char *>(W_q), *Wk = static_cast<const char *>(W_k);
+    const char *Wv = static_cast<const char *>(W_v), *Wo = static_cast<const char *>(W_o);
+    const int N = (int)p.BT;
+
+    // projections: head hh of q is the column-major [d_qk, B*T] block at hh*B*T*d_qk
+    for (int hh = 0; hh < H; ++hh) {
+        const size_t wq = (size_t)hh * d_qk * D * es, wv = (size_t)hh * d_v * D * es;
+        const size_t oq = (size_t)hh * p.BT * d_qk * es, ov = (size_t)hh * p.BT * d_v * es;
+        if ((st = gemm_tn(dev, d_qk, N, d_model, Wq + wq, x, q + oq, ab, ab, b_q + (size_t)hh * d_qk, ws, s)))
+            return st;
+        if ((st = gemm_tn(dev, d_qk, N, d_model, Wk + wq, x, k + oq, ab, ab, b_k + (size_t)hh * d_qk, ws, s)))
+            return st;
+        if ((st = gemm_tn(dev, d_v, N, d_model, Wv + wv, x, v + ov, ab, ab, b_v + (size_t)hh * d_v, ws, s)))
+            return st;
+        if ((st = gemm_tn(dev, d_v, N, d_model, Wo + wv, x, o + ov, ab, ab, b_o + (size_t)hh * d_v, ws, s)))
+            return st;
+    }
+    // gate pre-activations: [B*T, H] column-major = [H][B*T], float32
+    if ((st = gemm_tn(dev, N, H, d_model, x, W_i, gi, ab, HIP_R_32F, nullptr, ws, s))) return st;
+    if ((st = gemm_tn(dev, N, H, d_model, x, W_f, gf, ab, HIP_R_32F, nullptr, ws, s))) return st;
+    hipLaunchKernelGGL(gate_bias_kernel, dim3(1024), dim3(256), 0, s, gi, gf, b_i, b_f, p.BT, H);
+    if (hipGetLastError() != hipSuccess) return MLSTM_ERR_HIP;
+
+    // the cell over the H*B head-major cells: its "B" is H and its "H" is B
+    return mlstm_fwd_chunkwise(q, k, v, gi, gf, o, C0, n0, m0, h, C_T, n_T, m_T, H, B, T, d_qk, d_v,
+                               chunk, io, ws + p.off_cell, p.cell_bytes, stream);
+}
+
+}  // extern "C"

@@ -16,7 +16,17 @@ the I/O dtype; bf16 casts round to nearest even):
   in log space (the cell itself applies exp, never a sigmoid);
 * a decode workload draws tensor j of step t from ``SeedSequence([seed, 1, t,
   j])`` (so any single step is reproducible alone) and batch row b of its
-  initial state from ``SeedSequence([seed, 0, b])``.
+  initial state from ``SeedSequence([seed, 0, b])``;
+* a layer workload draws batch row b of its input x[T, d_model] from
+  ``SeedSequence([seed, 2, b])``, weight tensor j (W_q, W_k, W_v, W_o, W_i,
+  W_f, b_q, b_k, b_v, b_o, b_i, b_f) from ``SeedSequence([seed, 3, j])`` and
+  the initial state of cell (h, b) from ``SeedSequence([seed, 4, h, b])``.
+  x ~ N(0, 1); W_q, W_v, W_o ~ N(0, 1/d_model) and W_k ~ N(0, 1/(d_model
+  d_qk)), so q, v, o~ come out near N(0, 1) and k near N(0, 1/d_qk) as in the
+  cell workloads; W_i ~ N(0, i_std^2/d_model) with b_i ~ N(i_mean, 0.1^2);
+  W_f ~ N(0, f_std^2/d_model) with b_f ~ N(f_mean, 0.01^2), the forget input
+  being the log forget gate directly; the other biases ~ N(0, 0.1^2) (b_k
+  scaled by 1/sqrt(d_qk)).
 
 Because the draws are per (b, h) (prefill) or per step (decode), a subset of
 the pairs or steps can be regenerated without drawing the rest, which is how
@@ -32,7 +42,8 @@ from typing import Dict, Iterable, List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "gen_prefill", "gen_decode_state",
-           "gen_decode_step", "to_io_dtype", "logsigmoid"]
+           "gen_decode_step", "to_io_dtype", "logsigmoid", "LayerWorkload", "LAYER_WORKLOADS",
+           "layer_workload", "gen_layer"]
 
 
 @dataclass(frozen=True)
@@ -257,3 +268,96 @@ def gen_decode_steps(w: Workload, steps: Sequence[int], B: Optional[int] = None,
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         parts = list(ex.map(lambda t: gen_decode_step(w, t, B), steps))
     return {key: torch.stack([p[key] for p in parts]) for key in parts[0]}
+
+
+@dataclass(frozen=True)
+class LayerWorkload:
+    """A synthetic mLSTM layer workload (input projections + cell)."""
+    name: str
+    seed: int
+    B: int
+    T: int
+    d_model: int
+    H: int
+    d_qk: int
+    d_v: int
+    chunk: int
+    io: str
+    i_mean: float = -2.0
+    i_std: float = 1.0
+    f_mean: float = -0.05      # log forget gate: b_f ~ N(f_mean, 0.01^2)
+    f_std: float = 0.05        # std of W_f x
+    init_state: Optional[Dict[str, Tuple[str, float, float]]] = None
+    description: str = ""
+
+
+LAYER_WORKLOADS: Dict[str, LayerWorkload] = {w.name: w for w in [
+    LayerWorkload("layer_small", 6, 2, 100, 64, 2, 16, 32, 32, "f32",
+                  init_state={"C0": ("normal", 0.0, 0.1), "n0": ("normal", 0.0, 0.1),
+                              "m0": ("uniform", -1.0, 1.0)},
+                  description="Small mLSTM layer: B=2 T=100 d_model=64 H=2 d_qk=16 d_v=32, random state"),
+    LayerWorkload("layer_7b_bf16", 7, 8, 4096, 4096, 8, 256, 512, 64, "bf16",
+                  description="7B-shaped mLSTM layer, bf16: B=8 T=4096 d_model=4096 H=8 d_qk=256 d_v=512 "
+                              "chunk=64, zero initial state"),
+]}
+
+
+def layer_workload(name: str, **override) -> LayerWorkload:
+    w = LAYER_WORKLOADS[name]
+    if override:
+        d = dict(w.__dict__)
+        d.update(override)
+        w = LayerWorkload(**d)
+    return w
+
+
+def gen_layer(w: LayerWorkload, batches: Optional[Sequence[int]] = None, T: Optional[int] = None,
+              threads: int = 8):
+    """Draw a layer workload: a dict of torch CPU tensors x [len(batches), T,
+    d_model] (default: every batch row), W_q, W_k [H, d_qk, d_model], W_v, W_o
+    [H, d_v, d_model], W_i, W_f [H, d_model] in the I/O dtype, float32 biases
+    b_q, b_k [H, d_qk], b_v, b_o [H, d_v], b_i, b_f [H], and the initial state
+    C0 [H, nb, d_qk, d_v], n0 [H, nb, d_qk], m0 [H, nb] (float32, head-major,
+    None for the zero state).  ``T`` truncates every row to its first T
+    tokens."""
+    import torch
+    batches = list(range(w.B)) if batches is None else list(batches)
+    T = w.T if T is None else T
+    D, H, dk, dv = w.d_model, w.H, w.d_qk, w.d_v
+    cast = torch.bfloat16 if w.io == "bf16" else torch.float32
+    out = {"x": torch.empty((len(batches), T, D), dtype=cast)}
+
+    def row(j):
+        x = _rng(w.seed, 2, batches[j]).standard_normal((w.T, D))
+        out["x"][j] = to_io_dtype(x[:T], w.io)
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(row, range(len(batches))))
+    sd = 1.0 / math.sqrt(D)
+    specs = [("W_q", (H, dk, D), 0.0, sd), ("W_k", (H, dk, D), 0.0, sd / math.sqrt(dk)),
+             ("W_v", (H, dv, D), 0.0, sd), ("W_o", (H, dv, D), 0.0, sd),
+             ("W_i", (H, D), 0.0, w.i_std * sd), ("W_f", (H, D), 0.0, w.f_std * sd),
+             ("b_q", (H, dk), 0.0, 0.1), ("b_k", (H, dk), 0.0, 0.1 / math.sqrt(dk)),
+             ("b_v", (H, dv), 0.0, 0.1), ("b_o", (H, dv), 0.0, 0.1),
+             ("b_i", (H,), w.i_mean, 0.1), ("b_f", (H,), w.f_mean, 0.01)]
+    for j, (name, shape, mean, std) in enumerate(specs):
+        a = _rng(w.seed, 3, j).normal(mean, std, size=shape)
+        if name.startswith("W_"):
+            out[name] = to_io_dtype(a, w.io)
+        else:
+            out[name] = torch.from_numpy(a.astype(np.float32))
+    if w.init_state is None:
+        out["C0"] = out["n0"] = out["m0"] = None
+    else:
+        nb = len(batches)
+        C0 = torch.empty((H, nb, dk, dv), dtype=torch.float32)
+        n0 = torch.empty((H, nb, dk), dtype=torch.float32)
+        m0 = torch.empty((H, nb), dtype=torch.float32)
+        for h in range(H):
+            for j, b in enumerate(batches):
+                rng = _rng(w.seed, 4, h, b)
+                C0[h, j] = torch.from_numpy(_draw_state(rng, w.init_state["C0"], (dk, dv)).astype(np.float32))
+                n0[h, j] = torch.from_numpy(_draw_state(rng, w.init_state["n0"], (dk,)).astype(np.float32))
+                m0[h, j] = float(np.float32(_draw_state(rng, w.init_state["m0"], ())))
+        out["C0"], out["n0"], out["m0"] = C0, n0, m0
+    return out
