@@ -197,6 +197,42 @@ def bench_backward(torch, I, binding, steps, warmup):
     return w, ms, fl
 
 
+def layer_work(w):
+    """Algorithmic flops of one layer call: the projection GEMMs (2 flops per
+    multiply-add, every output of q, k, v, o~ and the two gates) plus the
+    cell's per-token-head flops (as for the prefill line)."""
+    BT = w.B * w.T
+    proj = 2 * BT * w.d_model * w.H * (2 * w.d_qk + 2 * w.d_v + 2)
+    cell = BT * w.H * ((w.chunk + 1) * (w.d_qk + w.d_v) + 4 * w.d_qk * w.d_v + 4 * w.d_qk)
+    return proj, cell
+
+
+def bench_layer(torch, I, binding, steps, warmup):
+    w = I.layer_workload("layer_7b_bf16")
+    t0 = time.time()
+    d = I.gen_layer(w, threads=16)
+    g = {k: (v.cuda() if v is not None else None) for k, v in d.items()}
+    del d
+    log(f"layer: inputs ready in {time.time() - t0:.1f}s")
+    names = ("x", "W_q", "W_k", "W_v", "W_o", "W_i", "W_f", "b_q", "b_k", "b_v", "b_o", "b_i", "b_f")
+    ws = torch.empty(binding.layer_workspace_size(w.B, w.T, w.d_model, w.H, w.d_qk, w.d_v, w.chunk,
+                                                  binding.BF16), dtype=torch.uint8, device="cuda")
+
+    def run():
+        binding.layer_fwd(*(g[k] for k in names), chunk=w.chunk, return_state=True, workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    with Timer(torch) as tm:
+        for _ in range(steps):
+            run()
+    ms = tm.ms / steps
+    proj, cell = layer_work(w)
+    log(f"layer {w.name}: {ms:.3f} ms/step, {(proj + cell) / ms / 1e9:.1f} TFLOP/s "
+        f"({proj / 1e12:.2f} TFLOP projections + {cell / 1e12:.3f} TFLOP cell)")
+    return w, ms, proj, cell
+
+
 def cpu_baseline(I, pairs_sample):
     """The float64 oracle on the host cores over a bounded sample of the
     prefill workload: `pairs_sample` (b, h) pairs, full sequence each."""
@@ -229,6 +265,7 @@ def main():
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 7B prefill line (profiling runs of the other workloads)")
     ap.add_argument("--decode-steps", type=int, default=0,
@@ -239,8 +276,9 @@ def main():
                          "1 GiB read, 1 GiB written), the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the mLSTM path has no "
-              "multi-GPU component in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the mLSTM cells are "
+              "independent per (batch, head) and would shard across GPUs without any exchange, "
+              "but no multi-GPU launcher is implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -333,6 +371,20 @@ def main():
                          "unit": "TFLOP/s", "frac": flb / msb / 1e9 / PEAK_FP32_TFLOPS, "traffic": None,
                          "kernel": "bwd_ckpt_kernel + bwd_kernel (one workgroup per pair)",
                          "algorithmic_flops_per_launch": flb}}
+
+    if not args.no_layer:
+        wl, msl_, projf, cellf = bench_layer(torch, I, binding, max(3, args.steps // 10),
+                                             max(2, args.warmup // 20))
+        rec["layer"] = {
+            "workload": "mLSTM layer forward B=8 T=4096 d_model=4096 H=8 d_qk=256 d_v=512 chunk=64 bf16: "
+                        "per-head projections (hipBLASLt) + gate bias + chunkwise cell",
+            "ms_per_step": msl_, "tokens_per_s": wl.B * wl.T / msl_ * 1e3,
+            "roofline": {"bound": "mfma", "achieved": (projf + cellf) / msl_ / 1e9,
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": (projf + cellf) / msl_ / 1e9 / PEAK_BF16_TFLOPS, "traffic": None,
+                         "kernel": "hipBLASLt GEMMs (4 per head + 2 gate) + gate_bias_kernel + mlstm_ws_kernel",
+                         "algorithmic_flops_per_step": projf + cellf,
+                         "projection_flops": projf, "cell_flops": cellf}}
 
     if not args.no_cpu:
         Pn = max(1, args.cpu_pairs)
