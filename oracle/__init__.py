@@ -6,7 +6,8 @@ leg may import this package.  It wraps ``mlstm_ref.c`` (the plain sequential
 recurrence in float64, see that file's header for the equations and their
 sources) through ctypes, and shares no code with the HIP library.  The
 submodule ``oracle.layer`` adds the layer's input projections (float64
-matrix products) in front of that recurrence.
+matrix products) in front of that recurrence; ``oracle.slstm`` wraps
+``slstm_ref.c``, the float64 sLSTM cell.
 """
 from __future__ import annotations
 
