@@ -233,6 +233,35 @@ def bench_layer(torch, I, binding, steps, warmup):
     return w, ms, proj, cell
 
 
+def slstm_work(w):
+    """Algorithmic flops of one sLSTM call: per token and group, the memory
+    mixing (4 matrix-vector products d x d, 2 flops per multiply-add) and
+    about 12 flops per cell for the gates and the update (exp, tanh and the
+    sigmoid counted as one each)."""
+    return w.B * w.H * w.T * (8 * w.d * w.d + 12 * w.d)
+
+
+def bench_slstm(torch, I, binding, steps, warmup):
+    w = I.slstm_workload("slstm_bf16")
+    d = I.gen_slstm(w, threads=16)
+    gx, R = d["gx"].cuda(), d["R"].cuda()
+    h = torch.empty((w.B, w.H, w.T, w.d), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        binding.slstm_fwd(gx, R, return_state=False, h=h)
+
+    for _ in range(warmup):
+        run()
+    with Timer(torch) as tm:
+        for _ in range(steps):
+            run()
+    ms = tm.ms / steps
+    fl = slstm_work(w)
+    log(f"slstm {w.name}: {ms:.3f} ms/call, {w.B * w.T / ms * 1e3:.3e} tokens/s, "
+        f"{ms * 1e3 / w.T:.3f} us per sequential step")
+    return w, ms, fl
+
+
 def cpu_baseline(I, pairs_sample):
     """The float64 oracle on the host cores over a bounded sample of the
     prefill workload: `pairs_sample` (b, h) pairs, full sequence each."""
@@ -266,6 +295,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
+    ap.add_argument("--no-slstm", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 7B prefill line (profiling runs of the other workloads)")
     ap.add_argument("--decode-steps", type=int, default=0,
@@ -385,6 +415,17 @@ def main():
                          "kernel": "hipBLASLt GEMMs (4 per head + 2 gate) + gate_bias_kernel + mlstm_ws_kernel",
                          "algorithmic_flops_per_step": projf + cellf,
                          "projection_flops": projf, "cell_flops": cellf}}
+
+    if not args.no_slstm:
+        ws_, mss, fls = bench_slstm(torch, I, binding, 3, 1)
+        rec["slstm"] = {
+            "workload": "sLSTM cell forward B=16 H=8 T=4096 d=128 bf16 I/O, zero state "
+                        "(sequential in T: one workgroup per (batch, head) group)",
+            "ms_per_step": mss, "tokens_per_s": ws_.B * ws_.T / mss * 1e3,
+            "us_per_sequential_step": mss * 1e3 / ws_.T,
+            "roofline": {"bound": "alu", "achieved": fls / mss / 1e9, "peak": PEAK_FP32_TFLOPS,
+                         "unit": "TFLOP/s", "frac": fls / mss / 1e9 / PEAK_FP32_TFLOPS, "traffic": None,
+                         "kernel": "slstm_kernel<bf16, 128>", "algorithmic_flops_per_launch": fls}}
 
     if not args.no_cpu:
         Pn = max(1, args.cpu_pairs)

@@ -21,8 +21,9 @@
  *   mlstm_fwd_chunkwise -- a whole sequence, chunkwise-parallel (prefill);
  *   mlstm_step          -- one token of the recurrence (decode);
  *   mlstm_bwd_chunkwise -- gradients of a whole sequence (training);
- * and mlstm_layer_fwd runs the layer's input projections in front of the
- * first of them.
+ * mlstm_layer_fwd runs the layer's input projections in front of the first
+ * of them, and mlstm_slstm_fwd is the forward of xLSTM's other cell, the
+ * sLSTM.
  *
  * Conventions shared by every call:
  *  - All tensor pointers are DEVICE pointers (HIP memory on the current
@@ -289,6 +290,36 @@ mlstm_status_t mlstm_layer_fwd(const void *x, const void *W_q, const void *W_k, 
                                int B, int T, int d_model, int H, int d_qk, int d_v, int chunk,
                                mlstm_dtype_t io, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/*
+ * The sLSTM cell forward, the scalar-memory cell of xLSTM (xLSTM note,
+ * section "sLSTM": exponential input and forget gates with the log-space
+ * stabilizer m_t = max(f~_t + m_{t-1}, i~_t) and a normalization; a scalar
+ * memory with memory mixing).  Per (batch, head) group of d cells and token t:
+ *   pre_g = gx[b,h,t,g] + R[h,g] h_{t-1}      g = 0..3: z, i, f, o (row j of
+ *                                            R[h,g] feeds cell j)
+ *   m_t = max(f~ + m_{t-1}, i~),  f' = e^{f~ + m_{t-1} - m_t},  i' = e^{i~ - m_t}
+ *   c_t = f' c_{t-1} + i' tanh(z~),  n_t = f' n_{t-1} + i',
+ *   h_t = sigmoid(o~) c_t / n_t               (elementwise over the d cells)
+ * c and n are kept stabilized (times e^{-m_t}); h does not depend on it.
+ *
+ *  gx        [B, H, T, 4, d]  io dtype: the input part (W_g x_t + b_g) of
+ *            every pre-activation, gate order z, i, f, o
+ *  R         [H, 4, d, d]     io dtype: recurrent (memory-mixing) weights
+ *  c0, n0, m0, h0  [B, H, d] float32, all four or all NULL (zero state)
+ *  h         [B, H, T, d]     io dtype (written)
+ *  c_T, n_T, m_T, h_T  [B, H, d] float32, all four or all NULL; each may be
+ *            exactly its initial-state pointer (in place)
+ *  d         multiple of 16, at most 128 (the four d x d matrices of a head
+ *            live in one compute unit's registers)
+ *
+ * Errors as for the other calls (MLSTM_ERR_STATE_ARGS for an incomplete
+ * state set).
+ */
+mlstm_status_t mlstm_slstm_fwd(const void *gx, const void *R, const float *c0, const float *n0,
+                               const float *m0, const float *h0, void *h, float *c_T,
+                               float *n_T, float *m_T, float *h_T, int B, int H, int T, int d,
+                               mlstm_dtype_t io, void *stream);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s+(mlstm_\w+)", out))
@@ -393,3 +393,44 @@ def test_layer_validation(lib):
     assert call_layer(a) == ALIAS
     a = layer_args(); a["ws"] = a["Wv"]
     assert call_layer(a) == ALIAS
+
+
+# ---- sLSTM: host-side validation only
+
+def slstm_args(B_=2, H=3, T=50, d=32, io=B.BF16, state=True):
+    fa = Fake()
+    es = 2 if io == B.BF16 else 4
+    ns = B_ * H * d * 4
+    a = dict(gx=fa(B_ * H * T * 4 * d * es), R=fa(H * 4 * d * d * es),
+             c0=fa(ns) if state else None, n0=fa(ns) if state else None,
+             m0=fa(ns) if state else None, h0=fa(ns) if state else None,
+             h=fa(B_ * H * T * d * es), cT=fa(ns), nT=fa(ns), mT=fa(ns), hT=fa(ns),
+             dims=(B_, H, T, d, io))
+    return a
+
+
+def call_slstm(a):
+    k = ("gx", "R", "c0", "n0", "m0", "h0", "h", "cT", "nT", "mT", "hT")
+    return B.lib().mlstm_slstm_fwd(*(a[x] for x in k), *a["dims"], None)
+
+
+def test_slstm_validation(lib):
+    for key in ("gx", "R", "h"):
+        a = slstm_args(); a[key] = None
+        assert call_slstm(a) == NULL, key
+    for dims, st in (((2, 3, 50, 24, B.BF16), UNSUP), ((2, 3, 50, 144, B.BF16), UNSUP),
+                     ((2, 3, 0, 32, B.BF16), SHAPE), ((2, 3, 50, 32, 3), UNSUP)):
+        a = slstm_args(); a["dims"] = dims
+        assert call_slstm(a) == st, dims
+    a = slstm_args(); a["m0"] = None
+    assert call_slstm(a) == STATE
+    a = slstm_args(); a["hT"] = None
+    assert call_slstm(a) == STATE
+    a = slstm_args(); a["R"] += 8
+    assert call_slstm(a) == 8   # MLSTM_ERR_ALIGN
+    a = slstm_args(); a["h"] = a["gx"]
+    assert call_slstm(a) == ALIAS
+    a = slstm_args(); a["cT"] = a["n0"]
+    assert call_slstm(a) == ALIAS
+    a = slstm_args(); a["cT"] = a["c0"] + 16
+    assert call_slstm(a) == ALIAS

@@ -37,6 +37,7 @@ SIGNATURES = {
     "mlstm_bwd_chunkwise": (_i, [_vp] * 19 + [_i] * 7 + [_vp, _sz, _vp]),
     "mlstm_layer_fwd_workspace_size": (_i, [_i] * 8 + [ctypes.POINTER(_sz)]),
     "mlstm_layer_fwd": (_i, [_vp] * 20 + [_i] * 8 + [_vp, _sz, _vp]),
+    "mlstm_slstm_fwd": (_i, [_vp] * 11 + [_i] * 5 + [_vp]),
 }
 
 
@@ -259,6 +260,37 @@ def layer_fwd(x, W_q, W_k, W_v, W_o, W_i, W_f, b_q, b_k, b_v, b_o, b_i, b_f, C0=
         _ptr(C0), _ptr(n0), _ptr(m0), _ptr(h), _ptr(C_T), _ptr(n_T), _ptr(m_T),
         B, T, D, H, dk, dv, chunk, io, _ptr(workspace), ws_len, _stream(dev)))
     return (h, (C_T, n_T, m_T)) if return_state else h
+
+
+def slstm_fwd(gx, R, c0=None, n0=None, m0=None, h0=None, *, return_state: bool = True, h=None,
+              c_T=None, n_T=None, m_T=None, h_T=None):
+    """The sLSTM cell forward.
+
+    gx [B,H,T,4,d] (input part of the z, i, f, o pre-activations) and R
+    [H,4,d,d] (recurrent weights) in the I/O dtype; optional state c0, n0,
+    m0, h0 [B,H,d] float32.  Returns h [B,H,T,d], or (h, (c_T, n_T, m_T,
+    h_T)) with ``return_state``."""
+    import torch
+    dev = gx.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    io_t = gx.dtype
+    B, H, T, four, d = gx.shape
+    if four != 4:
+        raise ValueError("gx must be [B, H, T, 4, d]")
+    _req(gx, "gx", io_t, dev)
+    _req(R, "R", io_t, dev)
+    for name, t in (("c0", c0), ("n0", n0), ("m0", m0), ("h0", h0)):
+        _req(t, name, torch.float32, dev)
+    if h is None:
+        h = torch.empty((B, H, T, d), dtype=io_t, device=dev)
+    if return_state and c_T is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        c_T, n_T, m_T, h_T = (torch.empty((B, H, d), **f32) for _ in range(4))
+    _check(lib().mlstm_slstm_fwd(
+        _ptr(gx), _ptr(R), _ptr(c0), _ptr(n0), _ptr(m0), _ptr(h0), _ptr(h),
+        _ptr(c_T), _ptr(n_T), _ptr(m_T), _ptr(h_T), B, H, T, d, _io(gx), _stream(dev)))
+    return (h, (c_T, n_T, m_T, h_T)) if return_state else h
 
 
 def step_workspace_size(B, H, d_qk, d_v, io: int) -> int:

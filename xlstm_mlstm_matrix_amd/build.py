@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmlstm.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "step.hip", "prefill.hip", "backward.hip", "layer.hip"]
+SOURCES = ["api.cpp", "step.hip", "prefill.hip", "backward.hip", "layer.hip", "slstm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror", "-Wno-unused-command-line-argument",

@@ -26,7 +26,14 @@ the I/O dtype; bf16 casts round to nearest even):
   cell workloads; W_i ~ N(0, i_std^2/d_model) with b_i ~ N(i_mean, 0.1^2);
   W_f ~ N(0, f_std^2/d_model) with b_f ~ N(f_mean, 0.01^2), the forget input
   being the log forget gate directly; the other biases ~ N(0, 0.1^2) (b_k
-  scaled by 1/sqrt(d_qk)).
+  scaled by 1/sqrt(d_qk));
+* an sLSTM workload draws the input pre-activations gx[T, 4, d] of group
+  (b, h) from ``SeedSequence([seed, 5, b, h])`` (z~ ~ N(0, 1), i~ ~
+  N(i_mean, i_std), f~ = logsigmoid(N(f_mean, f_std)), o~ ~ N(0, 1)), the
+  recurrent weights R[h] [4, d, d] ~ N(0, r_scale^2/d) from
+  ``SeedSequence([seed, 6, h])`` and the state of group (b, h) from
+  ``SeedSequence([seed, 7, b, h])`` (c0 ~ N(0, 0.5), n0 ~ U(0.5, 1.5), m0 ~
+  U(-1, 1), h0 ~ N(0, 0.3)).
 
 Because the draws are per (b, h) (prefill) or per step (decode), a subset of
 the pairs or steps can be regenerated without drawing the rest, which is how
@@ -43,7 +50,8 @@ import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "gen_prefill", "gen_decode_state",
            "gen_decode_step", "to_io_dtype", "logsigmoid", "LayerWorkload", "LAYER_WORKLOADS",
-           "layer_workload", "gen_layer"]
+           "layer_workload", "gen_layer", "SlstmWorkload", "SLSTM_WORKLOADS", "slstm_workload",
+           "gen_slstm"]
 
 
 @dataclass(frozen=True)
@@ -360,4 +368,85 @@ def gen_layer(w: LayerWorkload, batches: Optional[Sequence[int]] = None, T: Opti
                 n0[h, j] = torch.from_numpy(_draw_state(rng, w.init_state["n0"], (dk,)).astype(np.float32))
                 m0[h, j] = float(np.float32(_draw_state(rng, w.init_state["m0"], ())))
         out["C0"], out["n0"], out["m0"] = C0, n0, m0
+    return out
+
+
+@dataclass(frozen=True)
+class SlstmWorkload:
+    """A synthetic sLSTM cell workload."""
+    name: str
+    seed: int
+    B: int
+    H: int
+    T: int
+    d: int
+    io: str
+    state: bool
+    i_mean: float = -2.0
+    i_std: float = 1.0
+    f_mean: float = 3.0        # f~ = logsigmoid(N(f_mean, f_std))
+    f_std: float = 1.0
+    r_scale: float = 1.0
+    description: str = ""
+
+
+SLSTM_WORKLOADS: Dict[str, SlstmWorkload] = {w.name: w for w in [
+    SlstmWorkload("slstm_small", 8, 2, 2, 100, 32, "f32", True,
+                  description="Small sLSTM cell: B=2 H=2 T=100 d=32 float32, random state"),
+    SlstmWorkload("slstm_bf16", 9, 16, 8, 4096, 128, "bf16", False,
+                  description="sLSTM cell, bf16 I/O: B=16 H=8 T=4096 d=128, zero state"),
+]}
+
+
+def slstm_workload(name: str, **override) -> SlstmWorkload:
+    w = SLSTM_WORKLOADS[name]
+    if override:
+        d = dict(w.__dict__)
+        d.update(override)
+        w = SlstmWorkload(**d)
+    return w
+
+
+def gen_slstm(w: SlstmWorkload, groups: Optional[Sequence[Tuple[int, int]]] = None,
+              T: Optional[int] = None, threads: int = 8):
+    """Draw an sLSTM workload: gx [B, H, T, 4, d] (I/O dtype), R [H, 4, d, d]
+    (I/O dtype) and the state c0, n0, m0, h0 [B, H, d] float32 (None for the
+    zero state), as torch CPU tensors.  ``groups`` restricts gx and the state
+    to those (b, h) groups, returned as [1, len(groups), ...] (R stays
+    [H, ...]; group p uses head groups[p][1])."""
+    import torch
+    T = w.T if T is None else T
+    d = w.d
+    cast = torch.bfloat16 if w.io == "bf16" else torch.float32
+    if groups is None:
+        groups = [(b, h) for b in range(w.B) for h in range(w.H)]
+        shape = (w.B, w.H)
+    else:
+        shape = (1, len(groups))
+    gx = torch.empty((len(groups), T, 4, d), dtype=cast)
+    st = [torch.empty((len(groups), d), dtype=torch.float32) for _ in range(4)] if w.state else None
+
+    def group(p):
+        b, h = groups[p]
+        rng = _rng(w.seed, 5, b, h)
+        z = rng.standard_normal((w.T, d))
+        i = rng.normal(w.i_mean, w.i_std, size=(w.T, d))
+        f = logsigmoid(rng.normal(w.f_mean, w.f_std, size=(w.T, d)))
+        o = rng.standard_normal((w.T, d))
+        gx[p] = to_io_dtype(np.stack([z, i, f, o], axis=1)[:T], w.io)
+        if st is not None:
+            r2 = _rng(w.seed, 7, b, h)
+            vals = (r2.normal(0.0, 0.5, d), r2.uniform(0.5, 1.5, d), r2.uniform(-1.0, 1.0, d),
+                    r2.normal(0.0, 0.3, d))
+            for x, v in zip(st, vals):
+                x[p] = torch.from_numpy(v.astype(np.float32))
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(group, range(len(groups))))
+    R = torch.stack([to_io_dtype(_rng(w.seed, 6, h).normal(0.0, w.r_scale / math.sqrt(d), (4, d, d)), w.io)
+                     for h in range(w.H)])
+    out = {"gx": gx.reshape(*shape, T, 4, d), "R": R}
+    names = ("c0", "n0", "m0", "h0")
+    for k, x in zip(names, st or (None,) * 4):
+        out[k] = None if x is None else x.reshape(*shape, d)
     return out
