@@ -173,14 +173,16 @@ def backward_work(w, L=32):
     return th * 2 * (6 * w.d_qk * w.d_v + 1.5 * (L + 1) * (w.d_qk + w.d_v))
 
 
-def bench_backward(torch, I, binding, steps, warmup):
-    w = I.workload("small_f32")
+def bench_backward(torch, I, binding, steps, warmup, name="small_f32"):
+    w = I.workload(name)
     d = I.gen_prefill(w, threads=16)
     g = {k: (v.cuda().reshape(w.B, w.H, *v.shape[1:]) if v is not None else None) for k, v in d.items()}
     del d
-    dh = torch.randn((w.B, w.H, w.T, w.d_v), generator=torch.Generator().manual_seed(7)).cuda()
+    io_t = torch.bfloat16 if w.io == "bf16" else torch.float32
+    dh = torch.randn((w.B, w.H, w.T, w.d_v), generator=torch.Generator().manual_seed(7)).to(io_t).cuda()
     args = [g[k] for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")] + [dh, g["C0"], g["n0"], g["m0"]]
-    nbytes = binding.bwd_workspace_size(w.B, w.H, w.T, w.d_qk, w.d_v, 32, binding.F32)
+    nbytes = binding.bwd_workspace_size(w.B, w.H, w.T, w.d_qk, w.d_v, 32,
+                                        binding.BF16 if w.io == "bf16" else binding.F32)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
     def run():
@@ -401,6 +403,15 @@ def main():
                          "unit": "TFLOP/s", "frac": flb / msb / 1e9 / PEAK_FP32_TFLOPS, "traffic": None,
                          "kernel": "bwd_ckpt_kernel + bwd_kernel (one workgroup per pair)",
                          "algorithmic_flops_per_launch": flb}}
+        wb7, msb7, flb7 = bench_backward(torch, I, binding, 2, 1, name="prefill_7b_bf16")
+        rec["backward_7b"] = {
+            "workload": "backward B=8 H=8 T=4096 d_qk=256 d_v=512 bf16 I/O, zero state "
+                        "(checkpoint pass + reverse pass, 32-token chunks, state in global scratch)",
+            "ms_per_step": msb7, "tokens_per_s": wb7.B * wb7.T / msb7 * 1e3,
+            "roofline": {"bound": "alu", "achieved": flb7 / msb7 / 1e9, "peak": PEAK_FP32_TFLOPS,
+                         "unit": "TFLOP/s", "frac": flb7 / msb7 / 1e9 / PEAK_FP32_TFLOPS, "traffic": None,
+                         "kernel": "bwd_ckpt_big_kernel + bwd_big_kernel (one workgroup per pair)",
+                         "algorithmic_flops_per_launch": flb7}}
 
     if not args.no_layer:
         wl, msl_, projf, cellf = bench_layer(torch, I, binding, max(3, args.steps // 10),

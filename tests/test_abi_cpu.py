@@ -265,8 +265,14 @@ def test_bwd_workspace_query(lib):
     s, n = bws(2, 3, 70, 64, 48, 32, B.F32)
     # the state (C', n', m) at every 32-token chunk start of every pair
     assert s == OK and n == 6 * 3 * (64 * 48 + 64 + 1) * 4
-    assert bws(2, 3, 70, 128, 64, 32, B.F32)[0] == UNSUP     # d_qk above this version's 64
-    assert bws(2, 3, 70, 64, 80, 32, B.BF16)[0] == UNSUP     # d_v above 64
+    # heads above 64: records padded to 4 floats, then the per-pair scratch
+    # (G* [dk][dv], four [32][dk + 4] and five [32][dv + 4] tiles)
+    s, n = bws(2, 3, 70, 128, 64, 32, B.F32)
+    rec = (128 * 64 + 128 + 1 + 3) // 4 * 4
+    assert s == OK and n == 6 * (3 * rec + 128 * 64 + 32 * (4 * 132 + 5 * 68)) * 4
+    assert bws(2, 3, 70, 256, 512, 32, B.BF16)[0] == OK
+    assert bws(2, 3, 70, 272, 64, 32, B.F32)[0] == UNSUP     # d_qk above 256
+    assert bws(2, 3, 70, 64, 528, 32, B.BF16)[0] == UNSUP    # d_v above 512
     assert bws(2, 3, 70, 24, 64, 32, B.F32)[0] == UNSUP      # not a multiple of 16
     assert bws(2, 3, 70, 64, 64, 48, B.F32)[0] == UNSUP      # chunk
     assert bws(2, 3, 0, 64, 64, 32, B.F32)[0] == SHAPE
@@ -311,7 +317,7 @@ def test_bwd_validation(lib):
     assert bwd_call(a, gq=a["q"]) == ALIAS                      # output over an input
     assert bwd_call(a, gk=a["gq"] + 64) == ALIAS                # two outputs overlap
     assert bwd_call(a, gC0=a["ws"]) == ALIAS                    # output over the workspace
-    assert bwd_call(a, dims=(2, 3, 70, 128, 48, 32, B.F32)) == UNSUP
+    assert bwd_call(a, dims=(2, 3, 70, 272, 48, 32, B.F32)) == UNSUP
     assert bwd_call(a, dims=(2, 3, 0, 64, 48, 32, B.F32)) == SHAPE
 
 

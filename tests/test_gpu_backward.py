@@ -125,7 +125,25 @@ def test_matches_autograd_free_identities():
     np.testing.assert_allclose(df, rev, rtol=1e-3, atol=1e-3 * np.abs(df).max())
 
 
+@pytest.mark.parametrize("dk,dv,io", [(128, 64, "f32"), (64, 128, "f32"), (80, 96, "f32"),
+                                      (256, 512, "f32"), (256, 512, "bf16")])
+def test_large_heads(dk, dv, io):
+    """Heads above 64 (state and tiles in the workspace), with a random initial
+    state and a ragged last chunk."""
+    w, d, dh = case("small_f32", pairs=[(0, 1), (2, 3)], T=70, d_qk=dk, d_v=dv, io=io)
+    out = run_gpu(d, dh, io == "f32")
+    ref = run_oracle(d, dh)
+    compare(out, ref[:len(out)], io, f"large heads {dk}x{dv} {io}", state_grad=io == "f32")
+
+
+def test_7b_heads_bf16():
+    """The 7B layer's heads and distributions (bf16, d_qk 256, d_v 512) over
+    200 tokens of two pairs, from the zero state."""
+    w, d, dh = case("prefill_7b_bf16", pairs=[(0, 0), (7, 5)], T=200)
+    compare(run_gpu(d, dh, False), run_oracle(d, dh)[:6], "bf16", "7b heads", state_grad=False)
+
+
 def test_unsupported_head_dim_raises():
-    w, d, dh = case("small_f32", pairs=[(0, 0)], T=40, d_qk=128, d_v=64)
+    w, d, dh = case("small_f32", pairs=[(0, 0)], T=40, d_qk=272, d_v=64)
     with pytest.raises(binding.MlstmError):
         run_gpu(d, dh, False)

@@ -314,7 +314,7 @@ static mlstm_status_t bwd_check_dims(int B, int H, int T, int d_qk, int d_v, int
                               size_t *bytes) {
     if (B <= 0 || H <= 0 || T <= 0 || d_qk <= 0 || d_v <= 0) return MLSTM_ERR_SHAPE;
     if (io != MLSTM_F32 && io != MLSTM_BF16) return MLSTM_ERR_UNSUPPORTED;
-    if (!dims_ok(d_qk, d_v) || d_qk > kBwdMaxDim || d_v > kBwdMaxDim || !chunk_ok(chunk))
+    if (!dims_ok(d_qk, d_v) || d_qk > kBwdMaxDk || d_v > kBwdMaxDv || !chunk_ok(chunk))
         return MLSTM_ERR_UNSUPPORTED;
     size_t BH, n;
     if (!mul_ok((size_t)B, (size_t)H, &BH) || BH > (size_t)INT32_MAX) return MLSTM_ERR_SHAPE;

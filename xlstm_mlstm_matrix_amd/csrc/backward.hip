@@ -29,9 +29,10 @@
 //
 // Two launches.  The first runs the forward state recurrence per pair and
 // stores the state (C', n', m) at every chunk start in the workspace; the
-// second walks the chunks backwards.  One workgroup owns one pair and keeps
-// its tiles, the chunk-start state and G* in LDS (float32 throughout), so
-// this version covers d_qk, d_v <= 64.
+// second walks the chunks backwards.  One workgroup owns one pair.  For
+// d_qk, d_v <= 64 it keeps its tiles, the chunk-start state and G* in LDS
+// (float32 throughout); larger heads (d_qk <= 256, d_v <= 512) run the same
+// steps with them in a per-pair region of the workspace.
 #include "common.hpp"
 
 namespace mlstm {
@@ -328,9 +329,269 @@ __global__ __launch_bounds__(NTH) void bwd_kernel(BwdArgs a) {
     if (tid == 0 && a.gm0) a.gm0[p] = red[0];
 }
 
+// ---- heads above 64: the same two passes with the state, the carried
+// gradient and the tiles in a per-pair region of the workspace (global memory,
+// served from the caches) instead of LDS, 1024 threads per pair.  Workspace of
+// pair p: [nch records of bwd_rec_floats (16-byte aligned)][scratch].
+
+constexpr int NTB = 1024;
+
+template <typename IO>
+__global__ __launch_bounds__(NTB) void bwd_ckpt_big_kernel(BwdArgs a) {
+    __shared__ float wv[L], gb[L], gu[L], gr[L], last[2];
+    const int p = blockIdx.x, tid = threadIdx.x;
+    const int dk = a.dk, dv = a.dv, T = a.T;
+    const int nch = (T + L - 1) / L;
+    const size_t rec = bwd_rec_floats(dk, dv);
+    float *ck = a.ckpt + (size_t)p * bwd_ckpt_floats(T, dk, dv);
+    float *Kt = ck + (size_t)nch * rec;       // [L][dk], then Vt [L][dv]: the scratch's start
+    float *Vt = Kt + (size_t)L * dk;
+    const IO *kg = static_cast<const IO *>(a.k) + (size_t)p * T * dk;
+    const IO *vg = static_cast<const IO *>(a.v) + (size_t)p * T * dv;
+    const float *igp = a.ig + (size_t)p * T, *fgp = a.fg + (size_t)p * T;
+
+    // record 0: the initial state
+    for (int e = tid; e < dk * dv; e += NTB) ck[e] = a.C0 ? a.C0[(size_t)p * dk * dv + e] : 0.0f;
+    for (int e = tid; e < dk; e += NTB) ck[(size_t)dk * dv + e] = a.n0 ? a.n0[(size_t)p * dk + e] : 0.0f;
+    float m = a.m0 ? a.m0[p] : 0.0f;
+    if (tid == 0) ck[(size_t)dk * dv + dk] = m;
+    // record c + 1 from record c (the state after the last chunk is not needed)
+    for (int c = 0; c + 1 < nch; ++c) {
+        const int t0 = c * L;
+        const float *r = ck + (size_t)c * rec;
+        float *r1 = ck + (size_t)(c + 1) * rec;
+        for (int e = tid; e < L * dk; e += NTB) {
+            const int t = t0 + e / dk;
+            Kt[e] = t < T ? to_f(kg[(size_t)t * dk + e % dk]) : 0.0f;
+        }
+        for (int e = tid; e < L * dv; e += NTB) {
+            const int t = t0 + e / dv;
+            Vt[e] = t < T ? to_f(vg[(size_t)t * dv + e % dv]) : 0.0f;
+        }
+        if (tid < 64) chunk_gates(igp, fgp, t0, T, m, gb, gu, gr, last);
+        __syncthreads();  // tiles, gates and record c (written by other threads) visible
+        const float b_last = last[0], r_last = last[1];
+        const float dec = exp_e(m - r_last);
+        if (tid < L) wv[tid] = exp_e(gu[tid] - r_last);
+        __syncthreads();
+        for (int e = tid; e < dk * dv / 4; e += NTB) {
+            const int row = (4 * e) / dv, col = (4 * e) % dv;
+            f32x4 acc = dec * ld4(&r[4 * e]);
+#pragma unroll 4
+            for (int j = 0; j < L; ++j) acc += (wv[j] * Kt[j * dk + row]) * ld4(&Vt[j * dv + col]);
+            *reinterpret_cast<f32x4 *>(&r1[4 * e]) = acc;
+        }
+        for (int e = tid; e < dk; e += NTB) {
+            float acc = dec * r[(size_t)dk * dv + e];
+            for (int j = 0; j < L; ++j) acc = fmaf(wv[j], Kt[j * dk + e], acc);
+            r1[(size_t)dk * dv + e] = acc;
+        }
+        m = b_last + r_last;
+        if (tid == 0) r1[(size_t)dk * dv + dk] = m;
+        __syncthreads();  // the tiles are rewritten next chunk
+    }
+}
+
+template <typename IO>
+__global__ __launch_bounds__(NTB) void bwd_big_kernel(BwdArgs a) {
+    __shared__ float P[L * L], PT[L * L];
+    __shared__ float nc_s[kBwdMaxDk], gs[kBwdMaxDk], gb[L], gu[L], gr[L], sv[L], fl[L], wv[L], dd[L],
+        den[L], beta[L];
+    __shared__ float last[2], carry, red[NTB];
+    const int p = blockIdx.x, tid = threadIdx.x;
+    const int dk = a.dk, dv = a.dv, T = a.T;
+    const int nch = (T + L - 1) / L;
+    const size_t rec = bwd_rec_floats(dk, dv);
+    const int lk = dk + 4, lv = dv + 4;   // row strides of the dk- and dv-wide tiles
+    float *ckp = a.ckpt + (size_t)p * bwd_ckpt_floats(T, dk, dv);
+    float *Gs = ckp + (size_t)nch * rec;  // G* [dk][dv]
+    float *Q = Gs + (size_t)dk * dv, *K = Q + L * lk, *DQ = K + L * lk, *DK = DQ + L * lk;
+    float *V = DK + L * lk, *SG = V + L * lv, *DH = SG + L * lv, *NUM = DH + L * lv, *A = NUM + L * lv;
+    const size_t oqk = (size_t)p * T * dk, ov = (size_t)p * T * dv, og1 = (size_t)p * T;
+    const IO *qg = static_cast<const IO *>(a.q) + oqk;
+    const IO *kg = static_cast<const IO *>(a.k) + oqk;
+    const IO *vg = static_cast<const IO *>(a.v) + ov;
+    const IO *ogp = static_cast<const IO *>(a.o) + ov;
+    const IO *dhg = static_cast<const IO *>(a.dh) + ov;
+
+    for (int e = tid; e < dk * dv; e += NTB) Gs[e] = 0.0f;
+    for (int e = tid; e < dk; e += NTB) gs[e] = 0.0f;
+    if (tid == 0) carry = 0.0f;
+    __syncthreads();
+    for (int c = nch - 1; c >= 0; --c) {
+        const int t0 = c * L;
+        const float *Cc = ckp + (size_t)c * rec;  // C' at the chunk start, rows of dv floats
+        for (int e = tid; e < dk; e += NTB) nc_s[e] = Cc[(size_t)dk * dv + e];
+        const float m_prev = Cc[(size_t)dk * dv + dk];
+        for (int e = tid; e < L * dk; e += NTB) {
+            const int i = e / dk, t = t0 + i;
+            const size_t g = (size_t)t * dk + e % dk;
+            Q[i * lk + e % dk] = t < T ? to_f(qg[g]) : 0.0f;
+            K[i * lk + e % dk] = t < T ? to_f(kg[g]) : 0.0f;
+        }
+        for (int e = tid; e < L * dv; e += NTB) {
+            const int i = e / dv, t = t0 + i, x = i * lv + e % dv;
+            const size_t g = (size_t)t * dv + e % dv;
+            V[x] = t < T ? to_f(vg[g]) : 0.0f;
+            SG[x] = t < T ? sigmoid(to_f(ogp[g])) : 0.0f;
+            DH[x] = t < T ? to_f(dhg[g]) : 0.0f;
+        }
+        if (tid < 64) chunk_gates(a.ig + og1, a.fg + og1, t0, T, m_prev, gb, gu, gr, last);
+        __syncthreads();
+        const float r_last = last[1];
+        const float dec = exp_e(m_prev - r_last);
+        if (tid < L) {
+            sv[tid] = exp_e(m_prev - gr[tid]);
+            fl[tid] = exp_e(-(gb[tid] + gr[tid]));
+            wv[tid] = exp_e(gu[tid] - r_last);
+        }
+        for (int e = tid; e < L * L; e += NTB) {
+            const int i = e / L, j = e % L;
+            float s = 0.0f;
+            if (j <= i && t0 + i < T) s = dot(&Q[i * lk], &K[j * lk], dk) * exp_e(gu[j] - gr[i]);
+            P[e] = s;
+        }
+        __syncthreads();
+        for (int e = tid; e < L * dv / 4; e += NTB) {
+            const int i = (4 * e) / dv, b = (4 * e) % dv;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int r = 0; r < dk; ++r) acc += Q[i * lk + r] * ld4(&Cc[(size_t)r * dv + b]);
+            acc *= sv[i];
+            for (int j = 0; j <= i; ++j) acc += P[i * L + j] * ld4(&V[j * lv + b]);
+            *reinterpret_cast<f32x4 *>(&NUM[i * lv + b]) = acc;
+        }
+        if (tid < L) {
+            const int i = tid;
+            float acc = 0.0f;
+            for (int r = 0; r < dk; ++r) acc = fmaf(nc_s[r], Q[i * lk + r], acc);
+            acc *= sv[i];
+            for (int j = 0; j <= i; ++j) acc += P[i * L + j];
+            dd[i] = acc;
+            den[i] = fmaxf(fabsf(acc), fl[i]);
+        }
+        __syncthreads();
+        for (int e = tid; e < L * dv; e += NTB) {
+            const int i = e / dv, x = i * lv + e % dv;
+            const float sg = SG[x];
+            A[x] = DH[x] * sg / den[i];
+            const int t = t0 + i;
+            if (t < T) a.go[ov + (size_t)t * dv + e % dv] = DH[x] * NUM[x] / den[i] * sg * (1.0f - sg);
+        }
+        __syncthreads();
+        if (tid < L) {
+            const int i = tid;
+            const float an = dot(&A[i * lv], &NUM[i * lv], dv);
+            beta[i] = fabsf(dd[i]) > fl[i] ? (dd[i] > 0.0f ? -an : an) / den[i] : 0.0f;
+        }
+        __syncthreads();
+        for (int e = tid; e < L * L; e += NTB) {
+            const int i = e / L, j = e % L;
+            float s = 0.0f;
+            if (j <= i && t0 + i < T) s = (dot(&A[i * lv], &V[j * lv], dv) + beta[i]) * exp_e(gu[j] - gr[i]);
+            PT[e] = s;
+        }
+        __syncthreads();
+        for (int e = tid; e < L * dk; e += NTB) {
+            const int i = e / dk, r = e % dk;
+            float acc = sv[i] * fmaf(nc_s[r], beta[i], dot(&Cc[(size_t)r * dv], &A[i * lv], dv));
+            for (int j = 0; j <= i; ++j) acc = fmaf(PT[i * L + j], K[j * lk + r], acc);
+            DQ[i * lk + r] = acc;
+            const int t = t0 + i;
+            if (t < T) a.gq[oqk + (size_t)t * dk + r] = acc;
+        }
+        for (int e = tid; e < L * dk; e += NTB) {
+            const int j = e / dk, r = e % dk;
+            float acc = 0.0f;
+            for (int i = j; i < L; ++i) acc = fmaf(PT[i * L + j], Q[i * lk + r], acc);
+            acc = fmaf(wv[j], gs[r] + dot(&Gs[(size_t)r * dv], &V[j * lv], dv), acc);
+            DK[j * lk + r] = acc;
+            const int t = t0 + j;
+            if (t < T) a.gk[oqk + (size_t)t * dk + r] = acc;
+        }
+        for (int e = tid; e < L * dv / 4; e += NTB) {
+            const int j = (4 * e) / dv, b = (4 * e) % dv;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, gkv = {0.f, 0.f, 0.f, 0.f};
+            for (int i = j; i < L; ++i) acc += P[i * L + j] * ld4(&A[i * lv + b]);
+#pragma unroll 4
+            for (int r = 0; r < dk; ++r) gkv += K[j * lk + r] * ld4(&Gs[(size_t)r * dv + b]);
+            acc += wv[j] * gkv;
+            const int t = t0 + j;
+            if (t < T) *reinterpret_cast<f32x4 *>(&a.gv[ov + (size_t)t * dv + b]) = acc;
+        }
+        __syncthreads();
+        if (tid < 64) {
+            const int j = tid, t = t0 + j;
+            const bool ok = j < L && t < T;
+            float di = 0.0f, x = 0.0f;
+            if (ok) {
+                di = dot(&K[j * lk], &DK[j * lk], dk);
+                x = dot(&Q[j * lk], &DQ[j * lk], dk) - di;
+            }
+            float y = x;  // sum over lanes >= j
+            for (int o = 1; o < 64; o <<= 1) {
+                const float z = __shfl_down(y, o, 64);
+                if (j + o < 64) y += z;
+            }
+            const float cin = carry;
+            if (ok) {
+                a.gi[og1 + t] = di;
+                a.gf[og1 + t] = y + cin;
+            }
+            const float tot = __shfl(y, 0, 64);
+            if (j == 0) carry = cin + tot;
+        }
+        for (int e = tid; e < dk * dv / 4; e += NTB) {
+            const int r = (4 * e) / dv, b = (4 * e) % dv;
+            f32x4 acc = dec * ld4(&Gs[(size_t)r * dv + b]);
+#pragma unroll 4
+            for (int i = 0; i < L; ++i) acc += (sv[i] * Q[i * lk + r]) * ld4(&A[i * lv + b]);
+            *reinterpret_cast<f32x4 *>(&Gs[(size_t)r * dv + b]) = acc;
+        }
+        for (int e = tid; e < dk; e += NTB) {
+            float acc = dec * gs[e];
+            for (int i = 0; i < L; ++i) acc = fmaf(sv[i] * beta[i], Q[i * lk + e], acc);
+            gs[e] = acc;
+        }
+        __syncthreads();
+    }
+    float part = 0.0f;
+    for (int e = tid; e < dk * dv; e += NTB) {
+        const float gx = Gs[e];
+        if (a.gC0) a.gC0[(size_t)p * dk * dv + e] = gx;
+        if (a.C0) part = fmaf(gx, a.C0[(size_t)p * dk * dv + e], part);
+    }
+    for (int e = tid; e < dk; e += NTB) {
+        if (a.gn0) a.gn0[(size_t)p * dk + e] = gs[e];
+        if (a.n0) part = fmaf(gs[e], a.n0[(size_t)p * dk + e], part);
+    }
+    red[tid] = part;
+    __syncthreads();
+    for (int w = NTB / 2; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0 && a.gm0) a.gm0[p] = red[0];
+}
+
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs &a, int io_bf16, hipStream_t s) {
+    if (bwd_big(a.dk, a.dv)) {
+        dim3 grid(a.BH), block(NTB);
+        if (io_bf16) {
+            hipLaunchKernelGGL(bwd_ckpt_big_kernel<bf16>, grid, block, 0, s, a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(bwd_big_kernel<bf16>, grid, block, 0, s, a);
+        } else {
+            hipLaunchKernelGGL(bwd_ckpt_big_kernel<float>, grid, block, 0, s, a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(bwd_big_kernel<float>, grid, block, 0, s, a);
+        }
+        return hipGetLastError();
+    }
     dim3 grid(a.BH), block(NTH);
     if (io_bf16) {
         hipLaunchKernelGGL(bwd_ckpt_kernel<bf16>, grid, block, 0, s, a);

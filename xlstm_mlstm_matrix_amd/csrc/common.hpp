@@ -85,9 +85,23 @@ struct BwdArgs {
 // Tokens per chunk and largest head dimensions of the backward kernels, and
 // the floats one pair needs in the backward's workspace.
 constexpr int kBwdChunk = 32;
-constexpr int kBwdMaxDim = 64;
+constexpr int kBwdMaxDim = 64;          // both head dims up to this: tiles and state in LDS
+constexpr int kBwdMaxDk = 256, kBwdMaxDv = 512;  // larger heads: tiles and state in global scratch
+__host__ __device__ inline bool bwd_big(int dk, int dv) { return dk > kBwdMaxDim || dv > kBwdMaxDim; }
+// floats of one checkpoint record (C', n', m); padded to 16 bytes for large heads,
+// whose kernels read its rows with 16-byte loads
+__host__ __device__ inline size_t bwd_rec_floats(int dk, int dv) {
+    const size_t r = (size_t)dk * dv + dk + 1;
+    return bwd_big(dk, dv) ? (r + 3) / 4 * 4 : r;
+}
+// per-pair scratch of the large-head kernels: G* [dk][dv], tiles Q, K, DQ, DK
+// [L][dk + 4] and V, SG, DH, NUM, A [L][dv + 4] (0 for small heads)
+__host__ __device__ inline size_t bwd_scratch_floats(int dk, int dv) {
+    if (!bwd_big(dk, dv)) return 0;
+    return (size_t)dk * dv + (size_t)kBwdChunk * (4 * ((size_t)dk + 4) + 5 * ((size_t)dv + 4));
+}
 __host__ __device__ inline size_t bwd_ckpt_floats(int T, int dk, int dv) {
-    return (size_t)((T + kBwdChunk - 1) / kBwdChunk) * ((size_t)dk * dv + dk + 1);
+    return (size_t)((T + kBwdChunk - 1) / kBwdChunk) * bwd_rec_floats(dk, dv) + bwd_scratch_floats(dk, dv);
 }
 
 // Launchers (defined in the .hip files).  Return hipSuccess or the launch error.
