@@ -329,269 +329,530 @@ __global__ __launch_bounds__(NTH) void bwd_kernel(BwdArgs a) {
     if (tid == 0 && a.gm0) a.gm0[p] = red[0];
 }
 
-// ---- heads above 64: the same two passes with the state, the carried
-// gradient and the tiles in a per-pair region of the workspace (global memory,
-// served from the caches) instead of LDS, 1024 threads per pair.  Workspace of
-// pair p: [nch records of bwd_rec_floats (16-byte aligned)][scratch].
+// ---- heads above 64 (d_qk <= 256, d_v <= 512).  The pair's state is too
+// large for one compute unit, and only the carried gradient G* is sequential
+// over chunks: everything else of a chunk follows from its checkpointed
+// state.  So, after the checkpoint pass:
+//   A (pair, chunk): P, the read-out, a, beta, P~ and do~            -> workspace
+//   B (pair, 64 value columns): the reverse scan of G*, g* over the chunks,
+//     storing the value entering every chunk; dC0, dn0 and dm0 partials
+//   C (pair, chunk): dq, dk, dv, di~ and the in-chunk part of df~
+//   D (pair): df~'s carry across chunks and dm0
+// Tiles live in LDS in float32; the state, a, G* come from the workspace
+// through the caches.  Workspace layout: bwd_big_layout.
 
-constexpr int NTB = 1024;
+constexpr int NTA = 512, NTB2 = 256, BVB = 64;
 
+// load rows t0 .. t0 + L - 1 of a [T, d] input as float32 into a [L][ld] tile
+// (zero past T)
 template <typename IO>
-__global__ __launch_bounds__(NTB) void bwd_ckpt_big_kernel(BwdArgs a) {
-    __shared__ float wv[L], gb[L], gu[L], gr[L], last[2];
-    const int p = blockIdx.x, tid = threadIdx.x;
+__device__ __forceinline__ void load_tile(float *dst, int ld, const IO *src, int d, int t0, int T, int tid,
+                                          int nt) {
+    for (int e = tid; e < L * d; e += nt) {
+        const int i = e / d, t = t0 + i;
+        dst[i * ld + e % d] = t < T ? to_f(src[(size_t)t * d + e % d]) : 0.0f;
+    }
+}
+template <typename IO>
+__device__ __forceinline__ f32x4 ld4_io(const IO *p) {
+    return f32x4{to_f(p[0]), to_f(p[1]), to_f(p[2]), to_f(p[3])};
+}
+
+// Checkpoint pass for large heads: one workgroup per (block of BVB value
+// columns, pair).  The state recurrence is separable by value column, so each
+// workgroup carries its [d_qk][BVB] block of C' in registers (a 4 x 16 tile
+// per thread) and writes it to the record of every chunk start; block 0 also
+// carries n' and writes m (every block computes the same gates).
+template <typename IO>
+__global__ __launch_bounds__(256) void bwd_ckpt_big_kernel(BwdArgs a) {
+    constexpr int LK = kBwdMaxDk + 4;
+    __shared__ __attribute__((aligned(16))) float Ks[L * LK], Vs[L * BVB];
+    __shared__ float ns[kBwdMaxDk], wv[L], gb[L], gu[L], gr[L], last[2];
+    const int blk = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T;
-    const int nch = (T + L - 1) / L;
-    const size_t rec = bwd_rec_floats(dk, dv);
-    float *ck = a.ckpt + (size_t)p * bwd_ckpt_floats(T, dk, dv);
-    float *Kt = ck + (size_t)nch * rec;       // [L][dk], then Vt [L][dv]: the scratch's start
-    float *Vt = Kt + (size_t)L * dk;
+    const int c0 = blk * BVB, w = min(BVB, dv - c0);
+    const BwdBigLayout lay = bwd_big_layout(T, dk, dv);
+    const int nch = (int)lay.nch;
+    const size_t rec = lay.rec;
+    float *base = a.ckpt + (size_t)p * lay.total;
     const IO *kg = static_cast<const IO *>(a.k) + (size_t)p * T * dk;
     const IO *vg = static_cast<const IO *>(a.v) + (size_t)p * T * dv;
     const float *igp = a.ig + (size_t)p * T, *fgp = a.fg + (size_t)p * T;
-
-    // record 0: the initial state
-    for (int e = tid; e < dk * dv; e += NTB) ck[e] = a.C0 ? a.C0[(size_t)p * dk * dv + e] : 0.0f;
-    for (int e = tid; e < dk; e += NTB) ck[(size_t)dk * dv + e] = a.n0 ? a.n0[(size_t)p * dk + e] : 0.0f;
+    // this thread's tile: rows 4*rg .. +3, block columns 16*cg .. +15
+    const int rg = tid >> 2, cg = tid & 3;
+    const bool act = 4 * rg < dk && 16 * cg < w;
+    float cr[4][16];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int b = 0; b < 16; ++b)
+            cr[e][b] = (act && a.C0) ? a.C0[(size_t)p * dk * dv + (size_t)(4 * rg + e) * dv + c0 + 16 * cg + b]
+                                     : 0.0f;
+    if (blk == 0)
+        for (int e = tid; e < dk; e += 256) ns[e] = a.n0 ? a.n0[(size_t)p * dk + e] : 0.0f;
     float m = a.m0 ? a.m0[p] : 0.0f;
-    if (tid == 0) ck[(size_t)dk * dv + dk] = m;
-    // record c + 1 from record c (the state after the last chunk is not needed)
-    for (int c = 0; c + 1 < nch; ++c) {
+    for (int c = 0; c < nch; ++c) {
         const int t0 = c * L;
-        const float *r = ck + (size_t)c * rec;
-        float *r1 = ck + (size_t)(c + 1) * rec;
-        for (int e = tid; e < L * dk; e += NTB) {
-            const int t = t0 + e / dk;
-            Kt[e] = t < T ? to_f(kg[(size_t)t * dk + e % dk]) : 0.0f;
+        float *r = base + (size_t)c * rec;
+        // the state at this chunk's start
+        if (act)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int b = 0; b < 16; b += 4)
+                    *reinterpret_cast<f32x4 *>(&r[(size_t)(4 * rg + e) * dv + c0 + 16 * cg + b]) =
+                        f32x4{cr[e][b], cr[e][b + 1], cr[e][b + 2], cr[e][b + 3]};
+        __syncthreads();  // ns of the previous chunk complete
+        if (blk == 0) {
+            for (int e = tid; e < dk; e += 256) r[(size_t)dk * dv + e] = ns[e];
+            if (tid == 0) r[(size_t)dk * dv + dk] = m;
         }
-        for (int e = tid; e < L * dv; e += NTB) {
-            const int t = t0 + e / dv;
-            Vt[e] = t < T ? to_f(vg[(size_t)t * dv + e % dv]) : 0.0f;
+        if (c + 1 == nch) break;  // the state after the last chunk is not needed
+        load_tile(Ks, LK, kg, dk, t0, T, tid, 256);
+        for (int e = tid; e < L * w; e += 256) {
+            const int j = e / w, t = t0 + j;
+            Vs[j * BVB + e % w] = t < T ? to_f(vg[(size_t)t * dv + c0 + e % w]) : 0.0f;
         }
         if (tid < 64) chunk_gates(igp, fgp, t0, T, m, gb, gu, gr, last);
-        __syncthreads();  // tiles, gates and record c (written by other threads) visible
+        __syncthreads();
         const float b_last = last[0], r_last = last[1];
         const float dec = exp_e(m - r_last);
         if (tid < L) wv[tid] = exp_e(gu[tid] - r_last);
         __syncthreads();
-        for (int e = tid; e < dk * dv / 4; e += NTB) {
-            const int row = (4 * e) / dv, col = (4 * e) % dv;
-            f32x4 acc = dec * ld4(&r[4 * e]);
-#pragma unroll 4
-            for (int j = 0; j < L; ++j) acc += (wv[j] * Kt[j * dk + row]) * ld4(&Vt[j * dv + col]);
-            *reinterpret_cast<f32x4 *>(&r1[4 * e]) = acc;
+        if (act) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int b = 0; b < 16; ++b) cr[e][b] *= dec;
+            for (int j = 0; j < L; ++j) {
+                float kw[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kw[e] = wv[j] * Ks[j * LK + 4 * rg + e];
+#pragma unroll
+                for (int b = 0; b < 16; b += 4) {
+                    const f32x4 vv = ld4(&Vs[j * BVB + 16 * cg + b]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) cr[e][b + x] = fmaf(kw[e], vv[x], cr[e][b + x]);
+                }
+            }
         }
-        for (int e = tid; e < dk; e += NTB) {
-            float acc = dec * r[(size_t)dk * dv + e];
-            for (int j = 0; j < L; ++j) acc = fmaf(wv[j], Kt[j * dk + e], acc);
-            r1[(size_t)dk * dv + e] = acc;
-        }
+        if (blk == 0)
+            for (int e = tid; e < dk; e += 256) {
+                float acc = dec * ns[e];
+                for (int j = 0; j < L; ++j) acc = fmaf(wv[j], Ks[j * LK + e], acc);
+                ns[e] = acc;
+            }
         m = b_last + r_last;
-        if (tid == 0) r1[(size_t)dk * dv + dk] = m;
         __syncthreads();  // the tiles are rewritten next chunk
     }
 }
 
+// Pass A: one workgroup per (chunk, pair).
 template <typename IO>
-__global__ __launch_bounds__(NTB) void bwd_big_kernel(BwdArgs a) {
-    __shared__ float P[L * L], PT[L * L];
-    __shared__ float nc_s[kBwdMaxDk], gs[kBwdMaxDk], gb[L], gu[L], gr[L], sv[L], fl[L], wv[L], dd[L],
-        den[L], beta[L];
-    __shared__ float last[2], carry, red[NTB];
-    const int p = blockIdx.x, tid = threadIdx.x;
-    const int dk = a.dk, dv = a.dv, T = a.T;
-    const int nch = (T + L - 1) / L;
-    const size_t rec = bwd_rec_floats(dk, dv);
-    const int lk = dk + 4, lv = dv + 4;   // row strides of the dk- and dv-wide tiles
-    float *ckp = a.ckpt + (size_t)p * bwd_ckpt_floats(T, dk, dv);
-    float *Gs = ckp + (size_t)nch * rec;  // G* [dk][dv]
-    float *Q = Gs + (size_t)dk * dv, *K = Q + L * lk, *DQ = K + L * lk, *DK = DQ + L * lk;
-    float *V = DK + L * lk, *SG = V + L * lv, *DH = SG + L * lv, *NUM = DH + L * lv, *A = NUM + L * lv;
+__global__ __launch_bounds__(NTA) void bwd_a_kernel(BwdArgs a) {
+    constexpr int LK = kBwdMaxDk + 4;
+    __shared__ __attribute__((aligned(16))) float Q[L * LK], K[L * LK];
+    __shared__ float P[L * L], part[L * (kBwdMaxDv / 4)];
+    __shared__ float gb[L], gu[L], gr[L], sv[L], fl[L], dd[L], den[L], beta[L], last[2];
+    const int c = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+    const int dk = a.dk, dv = a.dv, T = a.T, t0 = c * L;
+    const BwdBigLayout lay = bwd_big_layout(T, dk, dv);
+    const float *base = a.ckpt + (size_t)p * lay.total;
+    float *wbase = a.ckpt + (size_t)p * lay.total;
+    const float *Cc = base + (size_t)c * lay.rec;  // C' rows of dv floats, then n', m
+    const float *ncg = Cc + (size_t)dk * dv;
+    const float m_prev = ncg[dk];
+    float *Aw = wbase + lay.off_a + (size_t)c * L * dv;
+    float *Pw = wbase + lay.off_p + (size_t)c * 2 * L * L;
+    float *Sw = wbase + lay.off_s + (size_t)c * 4 * L;
     const size_t oqk = (size_t)p * T * dk, ov = (size_t)p * T * dv, og1 = (size_t)p * T;
-    const IO *qg = static_cast<const IO *>(a.q) + oqk;
-    const IO *kg = static_cast<const IO *>(a.k) + oqk;
     const IO *vg = static_cast<const IO *>(a.v) + ov;
     const IO *ogp = static_cast<const IO *>(a.o) + ov;
     const IO *dhg = static_cast<const IO *>(a.dh) + ov;
 
-    for (int e = tid; e < dk * dv; e += NTB) Gs[e] = 0.0f;
-    for (int e = tid; e < dk; e += NTB) gs[e] = 0.0f;
-    if (tid == 0) carry = 0.0f;
+    load_tile(Q, LK, static_cast<const IO *>(a.q) + oqk, dk, t0, T, tid, NTA);
+    load_tile(K, LK, static_cast<const IO *>(a.k) + oqk, dk, t0, T, tid, NTA);
+    if (tid < 64) chunk_gates(a.ig + og1, a.fg + og1, t0, T, m_prev, gb, gu, gr, last);
     __syncthreads();
+    const float r_last = last[1];
+    if (tid < L) {
+        sv[tid] = exp_e(m_prev - gr[tid]);
+        fl[tid] = exp_e(-(gb[tid] + gr[tid]));
+    }
+    for (int e = tid; e < L * L; e += NTA) {
+        const int i = e / L, j = e % L;
+        float s = 0.0f;
+        if (j <= i && t0 + i < T) s = dot(&Q[i * LK], &K[j * LK], dk) * exp_e(gu[j] - gr[i]);
+        P[e] = s;
+    }
+    __syncthreads();
+    if (tid < L) {
+        const int i = tid;
+        float acc = 0.0f;
+        for (int r = 0; r < dk; ++r) acc = fmaf(ncg[r], Q[i * LK + r], acc);
+        acc *= sv[i];
+        for (int j = 0; j <= i; ++j) acc += P[i * L + j];
+        dd[i] = acc;
+        den[i] = fmaxf(fabsf(acc), fl[i]);
+    }
+    __syncthreads();
+    // read-out, a and do~: thread (b4, g) takes value columns 4*b4 .. +3 of rows
+    // g, g + G, ... (G groups); its four columns of C' serve all its rows
+    const int NB4 = dv / 4, G = NTA / NB4;
+    const int b4 = tid % NB4, g = tid / NB4;
+    if (g < G) {
+        constexpr int RM = 8;  // rows per thread: L / G <= 8 since dv <= 512
+        f32x4 acc[RM];
+#pragma unroll
+        for (int k = 0; k < RM; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < dk; ++r) {
+            const f32x4 cv = ld4(&Cc[(size_t)r * dv + 4 * b4]);
+#pragma unroll
+            for (int k = 0; k < RM; ++k) {
+                const int i = g + k * G;
+                if (i < L) acc[k] += Q[i * LK + r] * cv;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < RM; ++k) {
+            const int i = g + k * G;
+            if (i >= L) break;
+            const int t = t0 + i;
+            f32x4 num = sv[i] * acc[k];
+            for (int j = 0; j <= i; ++j)
+                if (P[i * L + j] != 0.0f) num += P[i * L + j] * ld4_io(vg + (size_t)(t0 + j) * dv + 4 * b4);
+            f32x4 av = {0.f, 0.f, 0.f, 0.f};
+            if (t < T) {
+                const f32x4 dh = ld4_io(dhg + (size_t)t * dv + 4 * b4);
+                const f32x4 og = ld4_io(ogp + (size_t)t * dv + 4 * b4);
+                f32x4 go;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float sg = sigmoid(og[e]);
+                    av[e] = dh[e] * sg / den[i];
+                    go[e] = dh[e] * num[e] / den[i] * sg * (1.0f - sg);
+                }
+                *reinterpret_cast<f32x4 *>(&a.go[ov + (size_t)t * dv + 4 * b4]) = go;
+            }
+            *reinterpret_cast<f32x4 *>(&Aw[i * dv + 4 * b4]) = av;
+            part[i * NB4 + b4] = hsum(av * num);
+        }
+    }
+    __syncthreads();  // a rows in the workspace and the row partials visible
+    if (tid < L) {
+        const int i = tid;
+        float an = 0.0f;
+        for (int b = 0; b < NB4; ++b) an += part[i * NB4 + b];
+        beta[i] = fabsf(dd[i]) > fl[i] ? (dd[i] > 0.0f ? -an : an) / den[i] : 0.0f;
+        Sw[i] = sv[i];
+        Sw[L + i] = exp_e(gu[i] - r_last);
+        Sw[2 * L + i] = beta[i];
+        if (i == 0) Sw[3 * L] = exp_e(m_prev - r_last);
+    }
+    __syncthreads();
+    // P~_ij = (a_i.v_j + beta_i) e^{u_j - r_i}; P and P~ to the workspace
+    for (int e = tid; e < L * L; e += NTA) {
+        const int i = e / L, j = e % L;
+        float s = 0.0f;
+        if (j <= i && t0 + i < T) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const IO *vj = vg + (size_t)(t0 + j) * dv;
+            for (int b = 0; b < dv; b += 4) acc += ld4(&Aw[i * dv + b]) * ld4_io(vj + b);
+            s = (hsum(acc) + beta[i]) * exp_e(gu[j] - gr[i]);
+        }
+        Pw[e] = P[e];
+        Pw[L * L + e] = s;
+    }
+}
+
+// Pass B: one workgroup per (block of BVB value columns, pair): G* and g*
+// backwards over the chunks, G*'s [d_qk][BVB] block in registers (a 4 x 16
+// tile per thread, as in the checkpoint pass); block 0 also carries g*.
+template <typename IO>
+__global__ __launch_bounds__(NTB2) void bwd_b_kernel(BwdArgs a) {
+    constexpr int LK = kBwdMaxDk + 4;
+    __shared__ __attribute__((aligned(16))) float Qs[L * LK], As[L * BVB];
+    __shared__ float gs[kBwdMaxDk], sq[L], sqb[L], red[NTB2];
+    __shared__ float decs;
+    const int blk = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+    const int dk = a.dk, dv = a.dv, T = a.T;
+    const int c0 = blk * BVB, w = min(BVB, dv - c0);  // this block's columns [c0, c0 + w)
+    const BwdBigLayout lay = bwd_big_layout(T, dk, dv);
+    const int nch = (int)lay.nch;
+    float *base = a.ckpt + (size_t)p * lay.total;
+    const IO *qg = static_cast<const IO *>(a.q) + (size_t)p * T * dk;
+    const int rg = tid >> 2, cg = tid & 3;
+    const bool act = 4 * rg < dk && 16 * cg < w;
+    float gr[4][16];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int b = 0; b < 16; ++b) gr[e][b] = 0.0f;
+    for (int e = tid; e < dk; e += NTB2) gs[e] = 0.0f;
     for (int c = nch - 1; c >= 0; --c) {
         const int t0 = c * L;
-        const float *Cc = ckp + (size_t)c * rec;  // C' at the chunk start, rows of dv floats
-        for (int e = tid; e < dk; e += NTB) nc_s[e] = Cc[(size_t)dk * dv + e];
-        const float m_prev = Cc[(size_t)dk * dv + dk];
-        for (int e = tid; e < L * dk; e += NTB) {
-            const int i = e / dk, t = t0 + i;
-            const size_t g = (size_t)t * dk + e % dk;
-            Q[i * lk + e % dk] = t < T ? to_f(qg[g]) : 0.0f;
-            K[i * lk + e % dk] = t < T ? to_f(kg[g]) : 0.0f;
-        }
-        for (int e = tid; e < L * dv; e += NTB) {
-            const int i = e / dv, t = t0 + i, x = i * lv + e % dv;
-            const size_t g = (size_t)t * dv + e % dv;
-            V[x] = t < T ? to_f(vg[g]) : 0.0f;
-            SG[x] = t < T ? sigmoid(to_f(ogp[g])) : 0.0f;
-            DH[x] = t < T ? to_f(dhg[g]) : 0.0f;
-        }
-        if (tid < 64) chunk_gates(a.ig + og1, a.fg + og1, t0, T, m_prev, gb, gu, gr, last);
-        __syncthreads();
-        const float r_last = last[1];
-        const float dec = exp_e(m_prev - r_last);
+        float *Gw = base + lay.off_g + (size_t)c * lay.grec;
+        const float *Sw = base + lay.off_s + (size_t)c * 4 * L;
+        const float *Aw = base + lay.off_a + (size_t)c * L * dv;
+        // the carried gradients entering chunk c
+        if (act)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int b = 0; b < 16; b += 4)
+                    *reinterpret_cast<f32x4 *>(&Gw[(size_t)(4 * rg + e) * dv + c0 + 16 * cg + b]) =
+                        f32x4{gr[e][b], gr[e][b + 1], gr[e][b + 2], gr[e][b + 3]};
+        __syncthreads();  // gs of the previous step complete
+        if (blk == 0)
+            for (int e = tid; e < dk; e += NTB2) Gw[(size_t)dk * dv + e] = gs[e];
+        load_tile(Qs, LK, qg, dk, t0, T, tid, NTB2);
+        for (int e = tid; e < L * w; e += NTB2) As[(e / w) * BVB + e % w] = Aw[(e / w) * dv + c0 + e % w];
         if (tid < L) {
-            sv[tid] = exp_e(m_prev - gr[tid]);
-            fl[tid] = exp_e(-(gb[tid] + gr[tid]));
-            wv[tid] = exp_e(gu[tid] - r_last);
+            sq[tid] = Sw[tid];                    // sv_i
+            sqb[tid] = Sw[tid] * Sw[2 * L + tid];  // sv_i beta_i
         }
-        for (int e = tid; e < L * L; e += NTB) {
-            const int i = e / L, j = e % L;
-            float s = 0.0f;
-            if (j <= i && t0 + i < T) s = dot(&Q[i * lk], &K[j * lk], dk) * exp_e(gu[j] - gr[i]);
-            P[e] = s;
-        }
+        if (tid == 0) decs = Sw[3 * L];
         __syncthreads();
-        for (int e = tid; e < L * dv / 4; e += NTB) {
-            const int i = (4 * e) / dv, b = (4 * e) % dv;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int r = 0; r < dk; ++r) acc += Q[i * lk + r] * ld4(&Cc[(size_t)r * dv + b]);
-            acc *= sv[i];
-            for (int j = 0; j <= i; ++j) acc += P[i * L + j] * ld4(&V[j * lv + b]);
-            *reinterpret_cast<f32x4 *>(&NUM[i * lv + b]) = acc;
-        }
-        if (tid < L) {
-            const int i = tid;
-            float acc = 0.0f;
-            for (int r = 0; r < dk; ++r) acc = fmaf(nc_s[r], Q[i * lk + r], acc);
-            acc *= sv[i];
-            for (int j = 0; j <= i; ++j) acc += P[i * L + j];
-            dd[i] = acc;
-            den[i] = fmaxf(fabsf(acc), fl[i]);
-        }
-        __syncthreads();
-        for (int e = tid; e < L * dv; e += NTB) {
-            const int i = e / dv, x = i * lv + e % dv;
-            const float sg = SG[x];
-            A[x] = DH[x] * sg / den[i];
-            const int t = t0 + i;
-            if (t < T) a.go[ov + (size_t)t * dv + e % dv] = DH[x] * NUM[x] / den[i] * sg * (1.0f - sg);
-        }
-        __syncthreads();
-        if (tid < L) {
-            const int i = tid;
-            const float an = dot(&A[i * lv], &NUM[i * lv], dv);
-            beta[i] = fabsf(dd[i]) > fl[i] ? (dd[i] > 0.0f ? -an : an) / den[i] : 0.0f;
-        }
-        __syncthreads();
-        for (int e = tid; e < L * L; e += NTB) {
-            const int i = e / L, j = e % L;
-            float s = 0.0f;
-            if (j <= i && t0 + i < T) s = (dot(&A[i * lv], &V[j * lv], dv) + beta[i]) * exp_e(gu[j] - gr[i]);
-            PT[e] = s;
-        }
-        __syncthreads();
-        for (int e = tid; e < L * dk; e += NTB) {
-            const int i = e / dk, r = e % dk;
-            float acc = sv[i] * fmaf(nc_s[r], beta[i], dot(&Cc[(size_t)r * dv], &A[i * lv], dv));
-            for (int j = 0; j <= i; ++j) acc = fmaf(PT[i * L + j], K[j * lk + r], acc);
-            DQ[i * lk + r] = acc;
-            const int t = t0 + i;
-            if (t < T) a.gq[oqk + (size_t)t * dk + r] = acc;
-        }
-        for (int e = tid; e < L * dk; e += NTB) {
-            const int j = e / dk, r = e % dk;
-            float acc = 0.0f;
-            for (int i = j; i < L; ++i) acc = fmaf(PT[i * L + j], Q[i * lk + r], acc);
-            acc = fmaf(wv[j], gs[r] + dot(&Gs[(size_t)r * dv], &V[j * lv], dv), acc);
-            DK[j * lk + r] = acc;
-            const int t = t0 + j;
-            if (t < T) a.gk[oqk + (size_t)t * dk + r] = acc;
-        }
-        for (int e = tid; e < L * dv / 4; e += NTB) {
-            const int j = (4 * e) / dv, b = (4 * e) % dv;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, gkv = {0.f, 0.f, 0.f, 0.f};
-            for (int i = j; i < L; ++i) acc += P[i * L + j] * ld4(&A[i * lv + b]);
-#pragma unroll 4
-            for (int r = 0; r < dk; ++r) gkv += K[j * lk + r] * ld4(&Gs[(size_t)r * dv + b]);
-            acc += wv[j] * gkv;
-            const int t = t0 + j;
-            if (t < T) *reinterpret_cast<f32x4 *>(&a.gv[ov + (size_t)t * dv + b]) = acc;
-        }
-        __syncthreads();
-        if (tid < 64) {
-            const int j = tid, t = t0 + j;
-            const bool ok = j < L && t < T;
-            float di = 0.0f, x = 0.0f;
-            if (ok) {
-                di = dot(&K[j * lk], &DK[j * lk], dk);
-                x = dot(&Q[j * lk], &DQ[j * lk], dk) - di;
+        const float dec = decs;
+        if (act) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int b = 0; b < 16; ++b) gr[e][b] *= dec;
+            for (int i = 0; i < L; ++i) {
+                float qa[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qa[e] = sq[i] * Qs[i * LK + 4 * rg + e];
+#pragma unroll
+                for (int b = 0; b < 16; b += 4) {
+                    const f32x4 av = ld4(&As[i * BVB + 16 * cg + b]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) gr[e][b + x] = fmaf(qa[e], av[x], gr[e][b + x]);
+                }
             }
-            float y = x;  // sum over lanes >= j
-            for (int o = 1; o < 64; o <<= 1) {
-                const float z = __shfl_down(y, o, 64);
-                if (j + o < 64) y += z;
+        }
+        if (blk == 0)
+            for (int e = tid; e < dk; e += NTB2) {
+                float acc = dec * gs[e];
+                for (int i = 0; i < L; ++i) acc = fmaf(sqb[i], Qs[i * LK + e], acc);
+                gs[e] = acc;
             }
-            const float cin = carry;
-            if (ok) {
-                a.gi[og1 + t] = di;
-                a.gf[og1 + t] = y + cin;
-            }
-            const float tot = __shfl(y, 0, 64);
-            if (j == 0) carry = cin + tot;
-        }
-        for (int e = tid; e < dk * dv / 4; e += NTB) {
-            const int r = (4 * e) / dv, b = (4 * e) % dv;
-            f32x4 acc = dec * ld4(&Gs[(size_t)r * dv + b]);
-#pragma unroll 4
-            for (int i = 0; i < L; ++i) acc += (sv[i] * Q[i * lk + r]) * ld4(&A[i * lv + b]);
-            *reinterpret_cast<f32x4 *>(&Gs[(size_t)r * dv + b]) = acc;
-        }
-        for (int e = tid; e < dk; e += NTB) {
-            float acc = dec * gs[e];
-            for (int i = 0; i < L; ++i) acc = fmaf(sv[i] * beta[i], Q[i * lk + e], acc);
-            gs[e] = acc;
-        }
         __syncthreads();
     }
+    // G*, g* after the first chunk: the initial state's gradients
     float part = 0.0f;
-    for (int e = tid; e < dk * dv; e += NTB) {
-        const float gx = Gs[e];
-        if (a.gC0) a.gC0[(size_t)p * dk * dv + e] = gx;
-        if (a.C0) part = fmaf(gx, a.C0[(size_t)p * dk * dv + e], part);
-    }
-    for (int e = tid; e < dk; e += NTB) {
-        if (a.gn0) a.gn0[(size_t)p * dk + e] = gs[e];
-        if (a.n0) part = fmaf(gs[e], a.n0[(size_t)p * dk + e], part);
-    }
+    if (act)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+                const size_t x = (size_t)p * dk * dv + (size_t)(4 * rg + e) * dv + c0 + 16 * cg + b;
+                if (a.gC0) a.gC0[x] = gr[e][b];
+                if (a.C0) part = fmaf(gr[e][b], a.C0[x], part);
+            }
+    if (blk == 0 && a.gn0)
+        for (int e = tid; e < dk; e += NTB2) a.gn0[(size_t)p * dk + e] = gs[e];
     red[tid] = part;
     __syncthreads();
-    for (int w = NTB / 2; w > 0; w >>= 1) {
-        if (tid < w) red[tid] += red[tid + w];
+    for (int s2 = NTB2 / 2; s2 > 0; s2 >>= 1) {
+        if (tid < s2) red[tid] += red[tid + s2];
         __syncthreads();
     }
-    if (tid == 0 && a.gm0) a.gm0[p] = red[0];
+    if (tid == 0) base[lay.off_m + blk] = red[0];
+}
+
+// Pass C: one workgroup per (chunk, pair).
+template <typename IO>
+__global__ __launch_bounds__(NTA) void bwd_c_kernel(BwdArgs a) {
+    constexpr int LK = kBwdMaxDk + 4;
+    __shared__ __attribute__((aligned(16))) float Q[L * LK], K[L * LK], DQ[L * LK], DK[L * LK];
+    __shared__ float P[L * L], PT[L * L], sv[L], wv[L], beta[L];
+    const int c = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+    const int dk = a.dk, dv = a.dv, T = a.T, t0 = c * L;
+    const BwdBigLayout lay = bwd_big_layout(T, dk, dv);
+    float *base = a.ckpt + (size_t)p * lay.total;
+    const float *Cc = base + (size_t)c * lay.rec;
+    const float *ncg = Cc + (size_t)dk * dv;
+    const float *Aw = base + lay.off_a + (size_t)c * L * dv;
+    const float *Pw = base + lay.off_p + (size_t)c * 2 * L * L;
+    const float *Sw = base + lay.off_s + (size_t)c * 4 * L;
+    const float *Gw = base + lay.off_g + (size_t)c * lay.grec;  // G* entering chunk c, then g*
+    const float *gsw = Gw + (size_t)dk * dv;
+    const size_t oqk = (size_t)p * T * dk, ov = (size_t)p * T * dv, og1 = (size_t)p * T;
+    const IO *vg = static_cast<const IO *>(a.v) + ov;
+
+    load_tile(Q, LK, static_cast<const IO *>(a.q) + oqk, dk, t0, T, tid, NTA);
+    load_tile(K, LK, static_cast<const IO *>(a.k) + oqk, dk, t0, T, tid, NTA);
+    for (int e = tid; e < L * L; e += NTA) {
+        P[e] = Pw[e];
+        PT[e] = Pw[L * L + e];
+    }
+    if (tid < L) {
+        sv[tid] = Sw[tid];
+        wv[tid] = Sw[L + tid];
+        beta[tid] = Sw[2 * L + tid];
+    }
+    __syncthreads();
+    // dq and dk: thread (r4, g) takes rows 4*r4 .. +3 of C' (of G*) and token
+    // rows g, g + G, ...
+    const int NR4 = dk / 4, G = NTA / NR4;
+    const int r4 = tid % NR4, g = tid / NR4;
+    constexpr int RM = 8;  // token rows per thread: at most L / G with G >= 4
+    constexpr int RQ = 4;  // token rows per thread here: L / G with G >= 8
+    if (g < G) {
+        // [token row][row of C' or G*]: four-wide partial sums over the value
+        // columns, reduced once at the end
+        f32x4 aq[RQ][4], ak[RQ][4];
+#pragma unroll
+        for (int k = 0; k < RQ; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) aq[k][e] = ak[k][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < dv; b += 4) {
+            f32x4 cr[4], gr4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                cr[e] = ld4(&Cc[(size_t)(4 * r4 + e) * dv + b]);
+                gr4[e] = ld4(&Gw[(size_t)(4 * r4 + e) * dv + b]);
+            }
+#pragma unroll
+            for (int k = 0; k < RQ; ++k) {
+                const int i = g + k * G;
+                if (i < L) {
+                    const f32x4 av = ld4(&Aw[i * dv + b]);
+                    const f32x4 vv = ld4_io(vg + (size_t)min(t0 + i, T - 1) * dv + b);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        aq[k][e] += cr[e] * av;
+                        ak[k][e] += gr4[e] * vv;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < RQ; ++k) {
+            const int i = g + k * G;
+            if (i >= L) break;
+            const int t = t0 + i;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * r4 + e;
+                float q_ = sv[i] * fmaf(ncg[r], beta[i], hsum(aq[k][e]));
+                for (int j = 0; j <= i; ++j) q_ = fmaf(PT[i * L + j], K[j * LK + r], q_);
+                float k_ = 0.0f;
+                for (int i2 = i; i2 < L; ++i2) k_ = fmaf(PT[i2 * L + i], Q[i2 * LK + r], k_);
+                // token row i as the key: its value row is V_i (zero past T)
+                k_ = fmaf(wv[i], (t < T ? hsum(ak[k][e]) : 0.0f) + gsw[r], k_);
+                DQ[i * LK + r] = q_;
+                DK[i * LK + r] = k_;
+                if (t < T) {
+                    a.gq[oqk + (size_t)t * dk + r] = q_;
+                    a.gk[oqk + (size_t)t * dk + r] = k_;
+                }
+            }
+        }
+    }
+    // dv: thread (b4, g) takes value columns 4*b4 .. +3 and token rows g, g + G2, ...
+    const int NB4 = dv / 4, G2 = NTA / NB4;
+    const int b4 = tid % NB4, g2 = tid / NB4;
+    if (g2 < G2) {
+        f32x4 acc[RM];
+#pragma unroll
+        for (int k = 0; k < RM; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < dk; ++r) {
+            const f32x4 gv4 = ld4(&Gw[(size_t)r * dv + 4 * b4]);
+#pragma unroll
+            for (int k = 0; k < RM; ++k) {
+                const int j = g2 + k * G2;
+                if (j < L) acc[k] += K[j * LK + r] * gv4;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < RM; ++k) {
+            const int j = g2 + k * G2;
+            if (j >= L) break;
+            const int t = t0 + j;
+            f32x4 o = wv[j] * acc[k];
+            for (int i = j; i < L; ++i)
+                if (P[i * L + j] != 0.0f) o += P[i * L + j] * ld4(&Aw[i * dv + 4 * b4]);
+            if (t < T) *reinterpret_cast<f32x4 *>(&a.gv[ov + (size_t)t * dv + 4 * b4]) = o;
+        }
+    }
+    __syncthreads();
+    // gate gradients: di = k.dk; the in-chunk part of df (reverse cumsum of
+    // q.dq - k.dk) and the chunk's total, for the carry of pass D
+    if (tid < 64) {
+        const int j = tid, t = t0 + j;
+        const bool ok = j < L && t < T;
+        float di = 0.0f, x = 0.0f;
+        if (ok) {
+            di = dot(&K[j * LK], &DK[j * LK], dk);
+            x = dot(&Q[j * LK], &DQ[j * LK], dk) - di;
+        }
+        float y = x;  // sum over lanes >= j
+        for (int o = 1; o < 64; o <<= 1) {
+            const float z = __shfl_down(y, o, 64);
+            if (j + o < 64) y += z;
+        }
+        if (ok) {
+            a.gi[og1 + t] = di;
+            a.gf[og1 + t] = y;
+        }
+        if (j == 0) base[lay.off_x + c] = y;
+    }
+}
+
+// Pass D: one wavefront per pair: df~'s carry from the later chunks, and dm0.
+__global__ __launch_bounds__(64) void bwd_d_kernel(BwdArgs a) {
+    const int p = blockIdx.x, lane = threadIdx.x;
+    const int dk = a.dk, dv = a.dv, T = a.T;
+    const BwdBigLayout lay = bwd_big_layout(T, dk, dv);
+    const int nch = (int)lay.nch;
+    const float *base = a.ckpt + (size_t)p * lay.total;
+    const size_t og1 = (size_t)p * T;
+    float carry = 0.0f;
+    for (int c = nch - 1; c >= 0; --c) {
+        const int t = c * L + lane;
+        if (lane < L && t < T) a.gf[og1 + t] += carry;
+        carry += base[lay.off_x + c];
+    }
+    if (a.gm0) {
+        float part = 0.0f;
+        if (a.n0)
+            for (int e = lane; e < dk; e += 64) part = fmaf(a.gn0[(size_t)p * dk + e], a.n0[(size_t)p * dk + e], part);
+        for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+        if (lane == 0) {
+            float s = part;
+            const int nb = (dv + BVB - 1) / BVB;
+            for (int b = 0; b < nb; ++b) s += base[lay.off_m + b];
+            a.gm0[p] = s;
+        }
+    }
+}
+
+template <typename IO>
+hipError_t launch_bwd_big(const BwdArgs &a, hipStream_t s) {
+    const int nch = (a.T + L - 1) / L, nb = (a.dv + BVB - 1) / BVB;
+    hipLaunchKernelGGL(bwd_ckpt_big_kernel<IO>, dim3(nb, a.BH), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_a_kernel<IO>, dim3(nch, a.BH), dim3(NTA), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_b_kernel<IO>, dim3(nb, a.BH), dim3(NTB2), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_c_kernel<IO>, dim3(nch, a.BH), dim3(NTA), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_d_kernel, dim3(a.BH), dim3(64), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs &a, int io_bf16, hipStream_t s) {
-    if (bwd_big(a.dk, a.dv)) {
-        dim3 grid(a.BH), block(NTB);
-        if (io_bf16) {
-            hipLaunchKernelGGL(bwd_ckpt_big_kernel<bf16>, grid, block, 0, s, a);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(bwd_big_kernel<bf16>, grid, block, 0, s, a);
-        } else {
-            hipLaunchKernelGGL(bwd_ckpt_big_kernel<float>, grid, block, 0, s, a);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(bwd_big_kernel<float>, grid, block, 0, s, a);
-        }
-        return hipGetLastError();
-    }
+    if (bwd_big(a.dk, a.dv)) return io_bf16 ? launch_bwd_big<bf16>(a, s) : launch_bwd_big<float>(a, s);
     dim3 grid(a.BH), block(NTH);
     if (io_bf16) {
         hipLaunchKernelGGL(bwd_ckpt_kernel<bf16>, grid, block, 0, s, a);

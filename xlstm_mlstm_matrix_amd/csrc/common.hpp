@@ -94,14 +94,35 @@ __host__ __device__ inline size_t bwd_rec_floats(int dk, int dv) {
     const size_t r = (size_t)dk * dv + dk + 1;
     return bwd_big(dk, dv) ? (r + 3) / 4 * 4 : r;
 }
-// per-pair scratch of the large-head kernels: G* [dk][dv], tiles Q, K, DQ, DK
-// [L][dk + 4] and V, SG, DH, NUM, A [L][dv + 4] (0 for small heads)
-__host__ __device__ inline size_t bwd_scratch_floats(int dk, int dv) {
-    if (!bwd_big(dk, dv)) return 0;
-    return (size_t)dk * dv + (size_t)kBwdChunk * (4 * ((size_t)dk + 4) + 5 * ((size_t)dv + 4));
+// Workspace of one pair for heads above 64, in floats from the pair's base;
+// every section starts 16-byte aligned.  Per chunk c: the state at its start
+// (C', n', m), the rows a_i = dh sigmoid(o~)/den, the matrices P and P~, the
+// scalars (sv, w, beta; dec), the carried gradients entering it (G*, g*) and
+// the sum over its tokens of q.dq - k.dk; then one dm0 partial per block of 64
+// value columns and the checkpoint pass's K, V tiles.
+struct BwdBigLayout {
+    size_t nch, rec, grec;
+    size_t off_a, off_p, off_s, off_g, off_x, off_m, off_tile, total;
+};
+__host__ __device__ inline BwdBigLayout bwd_big_layout(int T, int dk, int dv) {
+    const size_t L = kBwdChunk;
+    BwdBigLayout o;
+    o.nch = ((size_t)T + L - 1) / L;
+    o.rec = bwd_rec_floats(dk, dv);
+    o.grec = ((size_t)dk * dv + dk + 3) / 4 * 4;
+    o.off_a = o.nch * o.rec;
+    o.off_p = o.off_a + o.nch * L * dv;
+    o.off_s = o.off_p + o.nch * 2 * L * L;
+    o.off_g = o.off_s + o.nch * 4 * L;
+    o.off_x = o.off_g + o.nch * o.grec;
+    o.off_m = o.off_x + (o.nch + 3) / 4 * 4;
+    o.off_tile = o.off_m + 64;
+    o.total = o.off_tile + L * ((size_t)dk + dv);
+    return o;
 }
 __host__ __device__ inline size_t bwd_ckpt_floats(int T, int dk, int dv) {
-    return (size_t)((T + kBwdChunk - 1) / kBwdChunk) * bwd_rec_floats(dk, dv) + bwd_scratch_floats(dk, dv);
+    if (bwd_big(dk, dv)) return bwd_big_layout(T, dk, dv).total;
+    return (size_t)((T + kBwdChunk - 1) / kBwdChunk) * bwd_rec_floats(dk, dv);
 }
 
 // Launchers (defined in the .hip files).  Return hipSuccess or the launch error.
