@@ -226,9 +226,13 @@ mlstm_status_t mlstm_step(const void *q, const void *k, const void *v,
  *  workspace device buffer of at least mlstm_bwd_chunkwise_workspace_size
  *            bytes; contents on entry are irrelevant.
  *
- * Gradients are float32 for either io dtype.  This version keeps one
- * sequence's tiles and carried gradient in one compute unit: 1 <= d_qk,
- * d_v <= 64 (multiples of 16); larger heads return MLSTM_ERR_UNSUPPORTED.
+ * Gradients are float32 for either io dtype.  Supported heads: d_qk <= 256
+ * and d_v <= 512, multiples of 16 (both <= 64: one compute unit per
+ * sequence; larger: the chunks' local terms in parallel and the carried
+ * gradient scanned by blocks of value columns, with the per-chunk states,
+ * rows and carried gradients kept in the workspace, about
+ * T/32 * (2 d_qk d_v + 32 d_v) floats per sequence).  Larger heads return
+ * MLSTM_ERR_UNSUPPORTED.
  * Errors as for mlstm_fwd_chunkwise; every output must overlap no input, no
  * other output and no workspace (MLSTM_ERR_ALIAS).
  */

@@ -27,12 +27,13 @@
 // with w_j = e^{u_j - r_{L-1}}; after the first chunk G* and g* are the
 // gradients of the initial state (C0, n0) and dm0 = <dC0, C0> + dn0 . n0.
 //
-// Two launches.  The first runs the forward state recurrence per pair and
-// stores the state (C', n', m) at every chunk start in the workspace; the
-// second walks the chunks backwards.  One workgroup owns one pair.  For
-// d_qk, d_v <= 64 it keeps its tiles, the chunk-start state and G* in LDS
-// (float32 throughout); larger heads (d_qk <= 256, d_v <= 512) run the same
-// steps with them in a per-pair region of the workspace.
+// For d_qk, d_v <= 64, two launches: the first runs the forward state
+// recurrence per pair and stores the state (C', n', m) at every chunk start
+// in the workspace; the second walks the chunks backwards, one workgroup per
+// pair with its tiles, the chunk-start state and G* in LDS (float32
+// throughout).  Larger heads (d_qk <= 256, d_v <= 512) split the same work
+// into chunk-parallel passes and column-block scans (see the section on heads
+// above 64 below).
 #include "common.hpp"
 
 namespace mlstm {
