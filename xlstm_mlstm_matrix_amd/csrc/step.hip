@@ -39,6 +39,12 @@ namespace {
 constexpr int NTH = 512;
 constexpr int UNROLL = 16;
 
+// buffer descriptor word 3 (32-bit data format) and the non-temporal cache
+// policy of the row-split kernel's buffer accesses
+constexpr int kBufFlags = 0x00020000;
+constexpr int kNT = 2;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // streaming (non-temporal) 16-byte accesses: the memory is touched once per step
 __device__ __forceinline__ f32x4 ld_c(const float *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
@@ -175,13 +181,26 @@ __global__ __launch_bounds__(NTH) void mlstm_step_rows_kernel(StepArgs a) {
     const float nv = STATE ? a.n_in[pk + tr] : 0.0f;
     const f32x4 vv = ld4(static_cast<const IO *>(a.v) + (size_t)bh * dv + 4 * c4);
 
-    const size_t base = pk * dv + 4 * c4;
+    // The block's rows of C' through buffer descriptors: one 32-bit lane
+    // offset per row instead of a 64-bit address (registers for the loads in
+    // flight), and the hardware's range check on the block turns rows past
+    // its end into zero loads and dropped stores.
+    const int nbytes = nr * dv * 4;
+    const int voff = active ? (r0 * dv + 4 * c4) * 4 : nbytes;  // idle lanes: past the end
+    const int rstep = RPI * dv * 4;
+    const float *cin = STATE ? a.C_in : a.C_out;  // (not read without a state)
+    const __amdgpu_buffer_rsrc_t rin =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(cin + pk * dv), 0, nbytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(a.C_out + pk * dv, 0, nbytes, kBufFlags);
     __builtin_amdgcn_sched_barrier(0);  // keep the issue order: small loads, then the memory's
     f32x4 cv[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u)
-        cv[u] = STATE ? ld_c(a.C_in + base + (size_t)min(r0 + u * RPI, nr - 1) * dv)
-                      : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < UNROLL; ++u) {
+        if constexpr (STATE)
+            cv[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, voff + u * rstep, 0, kNT));
+        else
+            cv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     const float m_old = STATE ? a.m_in[bh] : 0.0f;
@@ -205,14 +224,13 @@ __global__ __launch_bounds__(NTH) void mlstm_step_rows_kernel(StepArgs a) {
     __syncthreads();
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float *Cout = a.C_out + base;
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
         const int r = r0 + u * RPI;
         if (active && r < nr) {
             const f32x4 c = fp * cv[u] + (ip * ks[r]) * vv;
             acc += c * qs[r];
-            st_c(Cout + (size_t)r * dv, c);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, c), rout, voff + u * rstep, 0, kNT);
         }
     }
     if (active) *reinterpret_cast<f32x4 *>(&red[r0 * dv + 4 * c4]) = acc;
