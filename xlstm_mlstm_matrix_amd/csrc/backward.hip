@@ -450,24 +450,27 @@ __global__ __launch_bounds__(256) void bwd_ckpt_big_kernel(BwdArgs a) {
     }
 }
 
-// Pass A: one workgroup per (chunk, pair).
+// Pass A: one workgroup per (chunk, pair).  The read-out's contractions (Q C'
+// and the causal P V, outputs [token][value column]) run as GEMMs staged
+// through LDS in steps of BK rows, each thread owning 4 x 8 outputs; a and do~
+// follow in registers, and P~'s a.v products are a staged [L][L] product over
+// the value columns.
 template <typename IO>
 __global__ __launch_bounds__(NTA) void bwd_a_kernel(BwdArgs a) {
-    constexpr int LK = kBwdMaxDk + 4;
-    __shared__ __attribute__((aligned(16))) float Q[L * LK], K[L * LK];
-    __shared__ float P[L * L], part[L * (kBwdMaxDv / 4)];
+    constexpr int LK = kBwdMaxDk + 4, BK = 16, NBGM = kBwdMaxDv / 8;
+    __shared__ __attribute__((aligned(16))) float Q[L * LK], K[L * LK], stage[BK * kBwdMaxDv];
+    __shared__ float P[L * L], part[L * NBGM];
     __shared__ float gb[L], gu[L], gr[L], sv[L], fl[L], dd[L], den[L], beta[L], last[2];
     const int c = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T, t0 = c * L;
     const BwdBigLayout lay = bwd_big_layout(T, dk, dv);
-    const float *base = a.ckpt + (size_t)p * lay.total;
-    float *wbase = a.ckpt + (size_t)p * lay.total;
+    float *base = a.ckpt + (size_t)p * lay.total;
     const float *Cc = base + (size_t)c * lay.rec;  // C' rows of dv floats, then n', m
     const float *ncg = Cc + (size_t)dk * dv;
     const float m_prev = ncg[dk];
-    float *Aw = wbase + lay.off_a + (size_t)c * L * dv;
-    float *Pw = wbase + lay.off_p + (size_t)c * 2 * L * L;
-    float *Sw = wbase + lay.off_s + (size_t)c * 4 * L;
+    float *Aw = base + lay.off_a + (size_t)c * L * dv;
+    float *Pw = base + lay.off_p + (size_t)c * 2 * L * L;
+    float *Sw = base + lay.off_s + (size_t)c * 4 * L;
     const size_t oqk = (size_t)p * T * dk, ov = (size_t)p * T * dv, og1 = (size_t)p * T;
     const IO *vg = static_cast<const IO *>(a.v) + ov;
     const IO *ogp = static_cast<const IO *>(a.o) + ov;
@@ -498,73 +501,139 @@ __global__ __launch_bounds__(NTA) void bwd_a_kernel(BwdArgs a) {
         dd[i] = acc;
         den[i] = fmaxf(fabsf(acc), fl[i]);
     }
-    __syncthreads();
-    // read-out, a and do~: thread (b4, g) takes value columns 4*b4 .. +3 of rows
-    // g, g + G, ... (G groups); its four columns of C' serve all its rows
-    const int NB4 = dv / 4, G = NTA / NB4;
-    const int b4 = tid % NB4, g = tid / NB4;
-    if (g < G) {
-        constexpr int RM = 8;  // rows per thread: L / G <= 8 since dv <= 512
-        f32x4 acc[RM];
+
+    // ---- the read-out num: thread (ig, bg) owns token rows 4ig .. +3 and value columns 8bg .. +7
+    const int NBG = dv / 8;
+    const int ig = tid / NBG, bg = tid % NBG;
+    const bool act = ig < L / 4;
+    float acc[4][8];
 #pragma unroll
-        for (int k = 0; k < RM; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int r = 0; r < dk; ++r) {
-            const f32x4 cv = ld4(&Cc[(size_t)r * dv + 4 * b4]);
+    for (int x = 0; x < 4; ++x)
 #pragma unroll
-            for (int k = 0; k < RM; ++k) {
-                const int i = g + k * G;
-                if (i < L) acc[k] += Q[i * LK + r] * cv;
+        for (int y = 0; y < 8; ++y) acc[x][y] = 0.0f;
+    // sum_r q_i[r] C'[r][b]
+    for (int r0 = 0; r0 < dk; r0 += BK) {
+        __syncthreads();
+        for (int e = tid; e < BK * dv / 4; e += NTA) {
+            const int k = (4 * e) / dv, b = (4 * e) % dv;
+            *reinterpret_cast<f32x4 *>(&stage[k * dv + b]) = ld4(&Cc[(size_t)(r0 + k) * dv + b]);
+        }
+        __syncthreads();
+        if (act) {
+#pragma unroll 4
+            for (int k = 0; k < BK; ++k) {
+                const f32x4 c0v = ld4(&stage[k * dv + 8 * bg]), c1v = ld4(&stage[k * dv + 8 * bg + 4]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float qv = Q[(4 * ig + x) * LK + r0 + k];
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        acc[x][y] = fmaf(qv, c0v[y], acc[x][y]);
+                        acc[x][4 + y] = fmaf(qv, c1v[y], acc[x][4 + y]);
+                    }
+                }
             }
         }
+    }
+    if (act)
 #pragma unroll
-        for (int k = 0; k < RM; ++k) {
-            const int i = g + k * G;
-            if (i >= L) break;
-            const int t = t0 + i;
-            f32x4 num = sv[i] * acc[k];
-            for (int j = 0; j <= i; ++j)
-                if (P[i * L + j] != 0.0f) num += P[i * L + j] * ld4_io(vg + (size_t)(t0 + j) * dv + 4 * b4);
-            f32x4 av = {0.f, 0.f, 0.f, 0.f};
-            if (t < T) {
-                const f32x4 dh = ld4_io(dhg + (size_t)t * dv + 4 * b4);
-                const f32x4 og = ld4_io(ogp + (size_t)t * dv + 4 * b4);
-                f32x4 go;
+        for (int x = 0; x < 4; ++x)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float sg = sigmoid(og[e]);
-                    av[e] = dh[e] * sg / den[i];
-                    go[e] = dh[e] * num[e] / den[i] * sg * (1.0f - sg);
+            for (int y = 0; y < 8; ++y) acc[x][y] *= sv[4 * ig + x];
+    // + sum_{j <= i} P_ij v_j[b]
+    for (int j0 = 0; j0 < L; j0 += BK) {
+        __syncthreads();
+        for (int e = tid; e < BK * dv / 4; e += NTA) {
+            const int k = (4 * e) / dv, b = (4 * e) % dv, t = t0 + j0 + k;
+            *reinterpret_cast<f32x4 *>(&stage[k * dv + b]) =
+                t < T ? ld4_io(vg + (size_t)t * dv + b) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        __syncthreads();
+        if (act) {
+#pragma unroll 4
+            for (int k = 0; k < BK; ++k) {
+                const f32x4 v0 = ld4(&stage[k * dv + 8 * bg]), v1 = ld4(&stage[k * dv + 8 * bg + 4]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float pv = P[(4 * ig + x) * L + j0 + k];  // zero unless j <= i
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        acc[x][y] = fmaf(pv, v0[y], acc[x][y]);
+                        acc[x][4 + y] = fmaf(pv, v1[y], acc[x][4 + y]);
+                    }
                 }
-                *reinterpret_cast<f32x4 *>(&a.go[ov + (size_t)t * dv + 4 * b4]) = go;
             }
-            *reinterpret_cast<f32x4 *>(&Aw[i * dv + 4 * b4]) = av;
-            part[i * NB4 + b4] = hsum(av * num);
+        }
+    }
+    // a = dh sigmoid(o~) / den and do~ in registers; a to the workspace; row
+    // partials of a.num for beta
+    if (act) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int i = 4 * ig + x, t = t0 + i;
+            float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, go[8];
+            if (t < T) {
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const f32x4 dh = ld4_io(dhg + (size_t)t * dv + 8 * bg + 4 * h2);
+                    const f32x4 og = ld4_io(ogp + (size_t)t * dv + 8 * bg + 4 * h2);
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        const float sg = sigmoid(og[y]);
+                        av[4 * h2 + y] = dh[y] * sg / den[i];
+                        go[4 * h2 + y] = dh[y] * acc[x][4 * h2 + y] / den[i] * sg * (1.0f - sg);
+                    }
+                }
+                float *o = a.go + ov + (size_t)t * dv + 8 * bg;
+                *reinterpret_cast<f32x4 *>(o) = f32x4{go[0], go[1], go[2], go[3]};
+                *reinterpret_cast<f32x4 *>(o + 4) = f32x4{go[4], go[5], go[6], go[7]};
+            }
+            *reinterpret_cast<f32x4 *>(&Aw[i * dv + 8 * bg]) = f32x4{av[0], av[1], av[2], av[3]};
+            *reinterpret_cast<f32x4 *>(&Aw[i * dv + 8 * bg + 4]) = f32x4{av[4], av[5], av[6], av[7]};
+            float an = 0.0f;
+#pragma unroll
+            for (int y = 0; y < 8; ++y) an = fmaf(av[y], acc[x][y], an);
+            part[i * NBGM + bg] = an;
         }
     }
     __syncthreads();  // a rows in the workspace and the row partials visible
     if (tid < L) {
         const int i = tid;
         float an = 0.0f;
-        for (int b = 0; b < NB4; ++b) an += part[i * NB4 + b];
+        for (int b = 0; b < NBG; ++b) an += part[i * NBGM + b];
         beta[i] = fabsf(dd[i]) > fl[i] ? (dd[i] > 0.0f ? -an : an) / den[i] : 0.0f;
         Sw[i] = sv[i];
         Sw[L + i] = exp_e(gu[i] - r_last);
         Sw[2 * L + i] = beta[i];
         if (i == 0) Sw[3 * L] = exp_e(m_prev - r_last);
     }
-    __syncthreads();
-    // P~_ij = (a_i.v_j + beta_i) e^{u_j - r_i}; P and P~ to the workspace
-    for (int e = tid; e < L * L; e += NTA) {
-        const int i = e / L, j = e % L;
-        float s = 0.0f;
-        if (j <= i && t0 + i < T) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const IO *vj = vg + (size_t)(t0 + j) * dv;
-            for (int b = 0; b < dv; b += 4) acc += ld4(&Aw[i * dv + b]) * ld4_io(vj + b);
-            s = (hsum(acc) + beta[i]) * exp_e(gu[j] - gr[i]);
+    // ---- P~_ij = (a_i.v_j + beta_i) e^{u_j - r_i}: thread (i, jq) owns j = 2jq, 2jq + 1
+    const int pi = tid >> 4, pj = 2 * (tid & 15);
+    float pa0 = 0.0f, pa1 = 0.0f;
+    float *At = stage, *Vt = stage + BK * L;
+    for (int b0 = 0; b0 < dv; b0 += BK) {
+        __syncthreads();
+        for (int e = tid; e < L * BK; e += NTA) {
+            const int i = e / BK, k = e % BK, t = t0 + i;
+            At[k * L + i] = Aw[i * dv + b0 + k];
+            Vt[k * L + i] = t < T ? to_f(vg[(size_t)t * dv + b0 + k]) : 0.0f;
         }
-        Pw[e] = P[e];
-        Pw[L * L + e] = s;
+        __syncthreads();
+#pragma unroll 4
+        for (int k = 0; k < BK; ++k) {
+            const float av = At[k * L + pi];
+            pa0 = fmaf(av, Vt[k * L + pj], pa0);
+            pa1 = fmaf(av, Vt[k * L + pj + 1], pa1);
+        }
+    }
+    // P and P~ to the workspace (beta is in LDS since the barriers above)
+    {
+        const int i = pi;
+        const bool row = t0 + i < T;
+        Pw[i * L + pj] = P[i * L + pj];
+        Pw[i * L + pj + 1] = P[i * L + pj + 1];
+        Pw[L * L + i * L + pj] = (pj <= i && row) ? (pa0 + beta[i]) * exp_e(gu[pj] - gr[i]) : 0.0f;
+        Pw[L * L + i * L + pj + 1] = (pj + 1 <= i && row) ? (pa1 + beta[i]) * exp_e(gu[pj + 1] - gr[i]) : 0.0f;
     }
 }
 
@@ -666,12 +735,21 @@ __global__ __launch_bounds__(NTB2) void bwd_b_kernel(BwdArgs a) {
     if (tid == 0) base[lay.off_m + blk] = red[0];
 }
 
-// Pass C: one workgroup per (chunk, pair).
+// Pass C: one workgroup per (chunk, pair).  Its contractions with the state
+// are small GEMMs staged through LDS in steps of BK: C' a and G* v (outputs
+// [token][d_qk], contraction over the value columns) share one loop, the
+// state and token tiles stored step-major so that a wavefront reads one
+// contiguous row of the state tile while the token values are broadcast;
+// dv's G*^T k and P^T a (outputs [token][value column]) loop over rows of G*
+// and of a.  Each thread owns 4 x 4 outputs of the first pair and 4 x 8 of
+// dv.  q.dq and k.dk are summed on the fly into per-row partials.
 template <typename IO>
 __global__ __launch_bounds__(NTA) void bwd_c_kernel(BwdArgs a) {
-    constexpr int LK = kBwdMaxDk + 4;
-    __shared__ __attribute__((aligned(16))) float Q[L * LK], K[L * LK], DQ[L * LK], DK[L * LK];
-    __shared__ float P[L * L], PT[L * L], sv[L], wv[L], beta[L];
+    constexpr int LK = kBwdMaxDk + 4, BK = 16, SB = kBwdMaxDk * BK, NRGM = kBwdMaxDk / 4;
+    __shared__ __attribute__((aligned(16))) float Q[L * LK], K[L * LK];
+    __shared__ __attribute__((aligned(16))) float stage[2 * SB + 2 * L * BK];
+    __shared__ float P[L * L], PT[L * L], sv[L], wv[L], beta[L], gsv[kBwdMaxDk];
+    __shared__ float pq[L * NRGM], pk[L * NRGM];
     const int c = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T, t0 = c * L;
     const BwdBigLayout lay = bwd_big_layout(T, dk, dv);
@@ -682,7 +760,6 @@ __global__ __launch_bounds__(NTA) void bwd_c_kernel(BwdArgs a) {
     const float *Pw = base + lay.off_p + (size_t)c * 2 * L * L;
     const float *Sw = base + lay.off_s + (size_t)c * 4 * L;
     const float *Gw = base + lay.off_g + (size_t)c * lay.grec;  // G* entering chunk c, then g*
-    const float *gsw = Gw + (size_t)dk * dv;
     const size_t oqk = (size_t)p * T * dk, ov = (size_t)p * T * dv, og1 = (size_t)p * T;
     const IO *vg = static_cast<const IO *>(a.v) + ov;
 
@@ -692,97 +769,160 @@ __global__ __launch_bounds__(NTA) void bwd_c_kernel(BwdArgs a) {
         P[e] = Pw[e];
         PT[e] = Pw[L * L + e];
     }
+    for (int e = tid; e < dk; e += NTA) gsv[e] = Gw[(size_t)dk * dv + e];
     if (tid < L) {
         sv[tid] = Sw[tid];
         wv[tid] = Sw[L + tid];
         beta[tid] = Sw[2 * L + tid];
     }
-    __syncthreads();
-    // dq and dk: thread (r4, g) takes rows 4*r4 .. +3 of C' (of G*) and token
-    // rows g, g + G, ...
-    const int NR4 = dk / 4, G = NTA / NR4;
-    const int r4 = tid % NR4, g = tid / NR4;
-    constexpr int RM = 8;  // token rows per thread: at most L / G with G >= 4
-    constexpr int RQ = 4;  // token rows per thread here: L / G with G >= 8
-    if (g < G) {
-        // [token row][row of C' or G*]: four-wide partial sums over the value
-        // columns, reduced once at the end
-        f32x4 aq[RQ][4], ak[RQ][4];
+
+    // ---- dq and dk: thread (ig, rg) owns token rows 4ig .. +3 and rows 4rg .. +3 of d_qk
+    const int NRG = dk / 4;
+    const int ig = tid / NRG, rg = tid % NRG;
+    const bool act1 = ig < L / 4;
+    float aq[4][4], ak[4][4];
 #pragma unroll
-        for (int k = 0; k < RQ; ++k)
+    for (int x = 0; x < 4; ++x)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) aq[k][e] = ak[k][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int b = 0; b < dv; b += 4) {
-            f32x4 cr[4], gr4[4];
+        for (int e = 0; e < 4; ++e) aq[x][e] = ak[x][e] = 0.0f;
+    float *Ct = stage, *Gt = stage + SB, *At = stage + 2 * SB, *Vt = At + L * BK;
+    for (int b0 = 0; b0 < dv; b0 += BK) {
+        __syncthreads();  // (first pass: the tiles above; then: the previous step's reads)
+        // Ct[k][r] = C'[r][b0 + k], Gt likewise: each row of the state gives BK
+        // consecutive floats, stored transposed
+        for (int e = tid; e < dk * (BK / 4); e += NTA) {
+            const int r = e / (BK / 4), k4 = e % (BK / 4);
+            const f32x4 cv = ld4(&Cc[(size_t)r * dv + b0 + 4 * k4]);
+            const f32x4 gv = ld4(&Gw[(size_t)r * dv + b0 + 4 * k4]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                cr[e] = ld4(&Cc[(size_t)(4 * r4 + e) * dv + b]);
-                gr4[e] = ld4(&Gw[(size_t)(4 * r4 + e) * dv + b]);
-            }
-#pragma unroll
-            for (int k = 0; k < RQ; ++k) {
-                const int i = g + k * G;
-                if (i < L) {
-                    const f32x4 av = ld4(&Aw[i * dv + b]);
-                    const f32x4 vv = ld4_io(vg + (size_t)min(t0 + i, T - 1) * dv + b);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        aq[k][e] += cr[e] * av;
-                        ak[k][e] += gr4[e] * vv;
-                    }
-                }
+            for (int x = 0; x < 4; ++x) {
+                Ct[(4 * k4 + x) * dk + r] = cv[x];
+                Gt[(4 * k4 + x) * dk + r] = gv[x];
             }
         }
+        // At[k][i] = a_i[b0 + k], Vt[k][j] = v_j[b0 + k] (zero past T)
+        for (int e = tid; e < L * BK; e += NTA) {
+            const int i = e / BK, k = e % BK, t = t0 + i;
+            At[k * L + i] = Aw[i * dv + b0 + k];
+            Vt[k * L + i] = t < T ? to_f(vg[(size_t)t * dv + b0 + k]) : 0.0f;
+        }
+        __syncthreads();
+        if (act1) {
+#pragma unroll 4
+            for (int k = 0; k < BK; ++k) {
+                const f32x4 c4 = ld4(&Ct[k * dk + 4 * rg]);
+                const f32x4 g4 = ld4(&Gt[k * dk + 4 * rg]);
+                const f32x4 a4 = ld4(&At[k * L + 4 * ig]);
+                const f32x4 v4 = ld4(&Vt[k * L + 4 * ig]);
 #pragma unroll
-        for (int k = 0; k < RQ; ++k) {
-            const int i = g + k * G;
-            if (i >= L) break;
-            const int t = t0 + i;
+                for (int x = 0; x < 4; ++x)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        aq[x][e] = fmaf(a4[x], c4[e], aq[x][e]);
+                        ak[x][e] = fmaf(v4[x], g4[e], ak[x][e]);
+                    }
+            }
+        }
+    }
+    if (act1) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int i = 4 * ig + x, t = t0 + i;
+            float sq = 0.0f, sk = 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 4 * r4 + e;
-                float q_ = sv[i] * fmaf(ncg[r], beta[i], hsum(aq[k][e]));
+                const int r = 4 * rg + e;
+                float q_ = sv[i] * fmaf(ncg[r], beta[i], aq[x][e]);
                 for (int j = 0; j <= i; ++j) q_ = fmaf(PT[i * L + j], K[j * LK + r], q_);
                 float k_ = 0.0f;
                 for (int i2 = i; i2 < L; ++i2) k_ = fmaf(PT[i2 * L + i], Q[i2 * LK + r], k_);
-                // token row i as the key: its value row is V_i (zero past T)
-                k_ = fmaf(wv[i], (t < T ? hsum(ak[k][e]) : 0.0f) + gsw[r], k_);
-                DQ[i * LK + r] = q_;
-                DK[i * LK + r] = k_;
+                k_ = fmaf(wv[i], ak[x][e] + gsv[r], k_);
                 if (t < T) {
                     a.gq[oqk + (size_t)t * dk + r] = q_;
                     a.gk[oqk + (size_t)t * dk + r] = k_;
                 }
+                sq = fmaf(Q[i * LK + r], q_, sq);
+                sk = fmaf(K[i * LK + r], k_, sk);
+            }
+            pq[i * NRGM + rg] = sq;
+            pk[i * NRGM + rg] = sk;
+        }
+    }
+
+    // ---- dv: thread (jg, bg) owns token rows 4jg .. +3 and value columns 8bg .. +7
+    const int NBG = dv / 8;
+    const int jg = tid / NBG, bg = tid % NBG;
+    const bool act2 = jg < L / 4;
+    float acc[4][8];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 8; ++y) acc[x][y] = 0.0f;
+    float *Rt = stage;  // [BK][dv] rows of G*, then of a
+    // w_j sum_r k_j[r] G*[r][b]
+    for (int r0 = 0; r0 < dk; r0 += BK) {
+        __syncthreads();
+        for (int e = tid; e < BK * dv / 4; e += NTA) {
+            const int k = (4 * e) / dv, b = (4 * e) % dv;
+            *reinterpret_cast<f32x4 *>(&Rt[k * dv + b]) = ld4(&Gw[(size_t)(r0 + k) * dv + b]);
+        }
+        __syncthreads();
+        if (act2) {
+#pragma unroll 4
+            for (int k = 0; k < BK; ++k) {
+                const f32x4 g0 = ld4(&Rt[k * dv + 8 * bg]), g1 = ld4(&Rt[k * dv + 8 * bg + 4]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float kv = K[(4 * jg + x) * LK + r0 + k];
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        acc[x][y] = fmaf(kv, g0[y], acc[x][y]);
+                        acc[x][4 + y] = fmaf(kv, g1[y], acc[x][4 + y]);
+                    }
+                }
             }
         }
     }
-    // dv: thread (b4, g) takes value columns 4*b4 .. +3 and token rows g, g + G2, ...
-    const int NB4 = dv / 4, G2 = NTA / NB4;
-    const int b4 = tid % NB4, g2 = tid / NB4;
-    if (g2 < G2) {
-        f32x4 acc[RM];
+    if (act2)
 #pragma unroll
-        for (int k = 0; k < RM; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int r = 0; r < dk; ++r) {
-            const f32x4 gv4 = ld4(&Gw[(size_t)r * dv + 4 * b4]);
+        for (int x = 0; x < 4; ++x)
 #pragma unroll
-            for (int k = 0; k < RM; ++k) {
-                const int j = g2 + k * G2;
-                if (j < L) acc[k] += K[j * LK + r] * gv4;
+            for (int y = 0; y < 8; ++y) acc[x][y] *= wv[4 * jg + x];
+    // + sum_{i >= j} P_ij a_i[b]
+    for (int i0 = 0; i0 < L; i0 += BK) {
+        __syncthreads();
+        for (int e = tid; e < BK * dv / 4; e += NTA) {
+            const int k = (4 * e) / dv, b = (4 * e) % dv;
+            *reinterpret_cast<f32x4 *>(&Rt[k * dv + b]) = ld4(&Aw[(size_t)(i0 + k) * dv + b]);
+        }
+        __syncthreads();
+        if (act2) {
+#pragma unroll 4
+            for (int k = 0; k < BK; ++k) {
+                const f32x4 a0 = ld4(&Rt[k * dv + 8 * bg]), a1 = ld4(&Rt[k * dv + 8 * bg + 4]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float pv = P[(i0 + k) * L + 4 * jg + x];  // zero unless i >= j
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        acc[x][y] = fmaf(pv, a0[y], acc[x][y]);
+                        acc[x][4 + y] = fmaf(pv, a1[y], acc[x][4 + y]);
+                    }
+                }
             }
         }
-#pragma unroll
-        for (int k = 0; k < RM; ++k) {
-            const int j = g2 + k * G2;
-            if (j >= L) break;
-            const int t = t0 + j;
-            f32x4 o = wv[j] * acc[k];
-            for (int i = j; i < L; ++i)
-                if (P[i * L + j] != 0.0f) o += P[i * L + j] * ld4(&Aw[i * dv + 4 * b4]);
-            if (t < T) *reinterpret_cast<f32x4 *>(&a.gv[ov + (size_t)t * dv + 4 * b4]) = o;
-        }
     }
-    __syncthreads();
+    if (act2)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int t = t0 + 4 * jg + x;
+            if (t < T) {
+                float *o = a.gv + ov + (size_t)t * dv + 8 * bg;
+                *reinterpret_cast<f32x4 *>(o) = f32x4{acc[x][0], acc[x][1], acc[x][2], acc[x][3]};
+                *reinterpret_cast<f32x4 *>(o + 4) = f32x4{acc[x][4], acc[x][5], acc[x][6], acc[x][7]};
+            }
+        }
+    __syncthreads();  // the row partials of q.dq and k.dk complete
     // gate gradients: di = k.dk; the in-chunk part of df (reverse cumsum of
     // q.dq - k.dk) and the chunk's total, for the carry of pass D
     if (tid < 64) {
@@ -790,8 +930,12 @@ __global__ __launch_bounds__(NTA) void bwd_c_kernel(BwdArgs a) {
         const bool ok = j < L && t < T;
         float di = 0.0f, x = 0.0f;
         if (ok) {
-            di = dot(&K[j * LK], &DK[j * LK], dk);
-            x = dot(&Q[j * LK], &DQ[j * LK], dk) - di;
+            float sq = 0.0f;
+            for (int r = 0; r < NRG; ++r) {
+                di += pk[j * NRGM + r];
+                sq += pq[j * NRGM + r];
+            }
+            x = sq - di;
         }
         float y = x;  // sum over lanes >= j
         for (int o = 1; o < 64; o <<= 1) {
