@@ -335,14 +335,20 @@ __global__ __launch_bounds__(NTH) void bwd_kernel(BwdArgs a) {
 // over chunks: everything else of a chunk follows from its checkpointed
 // state.  So, after the checkpoint pass:
 //   A (pair, chunk): P, the read-out, a, beta, P~ and do~            -> workspace
-//   B (pair, 64 value columns): the reverse scan of G*, g* over the chunks,
+//   B (pair, BVB value columns): the reverse scan of G*, g* over the chunks,
 //     storing the value entering every chunk; dC0, dn0 and dm0 partials
 //   C (pair, chunk): dq, dk, dv, di~ and the in-chunk part of df~
 //   D (pair): df~'s carry across chunks and dm0
 // Tiles live in LDS in float32; the state, a, G* come from the workspace
 // through the caches.  Workspace layout: bwd_big_layout.
 
-constexpr int NTA = 512, NTB2 = 256, BVB = 64;
+#ifndef BWD_BVB
+#define BWD_BVB 128
+#endif
+// value columns per workgroup of the two scans (128 measured fastest: 64 and
+// 32 re-read the K or Q tile more often, 256 halves the workgroups), and their
+// threads (a 4 x 16 tile of the block per thread, rows up to 256)
+constexpr int NTA = 512, BVB = BWD_BVB, CG = BVB / 16, NTS = 64 * CG;
 
 // load rows t0 .. t0 + L - 1 of a [T, d] input as float32 into a [L][ld] tile
 // (zero past T)
@@ -365,7 +371,7 @@ __device__ __forceinline__ f32x4 ld4_io(const IO *p) {
 // per thread) and writes it to the record of every chunk start; block 0 also
 // carries n' and writes m (every block computes the same gates).
 template <typename IO>
-__global__ __launch_bounds__(256) void bwd_ckpt_big_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTS) void bwd_ckpt_big_kernel(BwdArgs a) {
     constexpr int LK = kBwdMaxDk + 4;
     __shared__ __attribute__((aligned(16))) float Ks[L * LK], Vs[L * BVB];
     __shared__ float ns[kBwdMaxDk], wv[L], gb[L], gu[L], gr[L], last[2];
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_big_kernel(BwdArgs a) {
     const IO *vg = static_cast<const IO *>(a.v) + (size_t)p * T * dv;
     const float *igp = a.ig + (size_t)p * T, *fgp = a.fg + (size_t)p * T;
     // this thread's tile: rows 4*rg .. +3, block columns 16*cg .. +15
-    const int rg = tid >> 2, cg = tid & 3;
+    const int rg = tid / CG, cg = tid % CG;
     const bool act = 4 * rg < dk && 16 * cg < w;
     float cr[4][16];
 #pragma unroll
@@ -390,7 +396,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_big_kernel(BwdArgs a) {
             cr[e][b] = (act && a.C0) ? a.C0[(size_t)p * dk * dv + (size_t)(4 * rg + e) * dv + c0 + 16 * cg + b]
                                      : 0.0f;
     if (blk == 0)
-        for (int e = tid; e < dk; e += 256) ns[e] = a.n0 ? a.n0[(size_t)p * dk + e] : 0.0f;
+        for (int e = tid; e < dk; e += NTS) ns[e] = a.n0 ? a.n0[(size_t)p * dk + e] : 0.0f;
     float m = a.m0 ? a.m0[p] : 0.0f;
     for (int c = 0; c < nch; ++c) {
         const int t0 = c * L;
@@ -405,12 +411,12 @@ __global__ __launch_bounds__(256) void bwd_ckpt_big_kernel(BwdArgs a) {
                         f32x4{cr[e][b], cr[e][b + 1], cr[e][b + 2], cr[e][b + 3]};
         __syncthreads();  // ns of the previous chunk complete
         if (blk == 0) {
-            for (int e = tid; e < dk; e += 256) r[(size_t)dk * dv + e] = ns[e];
+            for (int e = tid; e < dk; e += NTS) r[(size_t)dk * dv + e] = ns[e];
             if (tid == 0) r[(size_t)dk * dv + dk] = m;
         }
         if (c + 1 == nch) break;  // the state after the last chunk is not needed
-        load_tile(Ks, LK, kg, dk, t0, T, tid, 256);
-        for (int e = tid; e < L * w; e += 256) {
+        load_tile(Ks, LK, kg, dk, t0, T, tid, NTS);
+        for (int e = tid; e < L * w; e += NTS) {
             const int j = e / w, t = t0 + j;
             Vs[j * BVB + e % w] = t < T ? to_f(vg[(size_t)t * dv + c0 + e % w]) : 0.0f;
         }
@@ -440,7 +446,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_big_kernel(BwdArgs a) {
             }
         }
         if (blk == 0)
-            for (int e = tid; e < dk; e += 256) {
+            for (int e = tid; e < dk; e += NTS) {
                 float acc = dec * ns[e];
                 for (int j = 0; j < L; ++j) acc = fmaf(wv[j], Ks[j * LK + e], acc);
                 ns[e] = acc;
@@ -641,10 +647,10 @@ __global__ __launch_bounds__(NTA) void bwd_a_kernel(BwdArgs a) {
 // backwards over the chunks, G*'s [d_qk][BVB] block in registers (a 4 x 16
 // tile per thread, as in the checkpoint pass); block 0 also carries g*.
 template <typename IO>
-__global__ __launch_bounds__(NTB2) void bwd_b_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
     constexpr int LK = kBwdMaxDk + 4;
     __shared__ __attribute__((aligned(16))) float Qs[L * LK], As[L * BVB];
-    __shared__ float gs[kBwdMaxDk], sq[L], sqb[L], red[NTB2];
+    __shared__ float gs[kBwdMaxDk], sq[L], sqb[L], red[NTS];
     __shared__ float decs;
     const int blk = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T;
@@ -653,14 +659,14 @@ __global__ __launch_bounds__(NTB2) void bwd_b_kernel(BwdArgs a) {
     const int nch = (int)lay.nch;
     float *base = a.ckpt + (size_t)p * lay.total;
     const IO *qg = static_cast<const IO *>(a.q) + (size_t)p * T * dk;
-    const int rg = tid >> 2, cg = tid & 3;
+    const int rg = tid / CG, cg = tid % CG;
     const bool act = 4 * rg < dk && 16 * cg < w;
     float gr[4][16];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int b = 0; b < 16; ++b) gr[e][b] = 0.0f;
-    for (int e = tid; e < dk; e += NTB2) gs[e] = 0.0f;
+    for (int e = tid; e < dk; e += NTS) gs[e] = 0.0f;
     for (int c = nch - 1; c >= 0; --c) {
         const int t0 = c * L;
         float *Gw = base + lay.off_g + (size_t)c * lay.grec;
@@ -676,9 +682,9 @@ __global__ __launch_bounds__(NTB2) void bwd_b_kernel(BwdArgs a) {
                         f32x4{gr[e][b], gr[e][b + 1], gr[e][b + 2], gr[e][b + 3]};
         __syncthreads();  // gs of the previous step complete
         if (blk == 0)
-            for (int e = tid; e < dk; e += NTB2) Gw[(size_t)dk * dv + e] = gs[e];
-        load_tile(Qs, LK, qg, dk, t0, T, tid, NTB2);
-        for (int e = tid; e < L * w; e += NTB2) As[(e / w) * BVB + e % w] = Aw[(e / w) * dv + c0 + e % w];
+            for (int e = tid; e < dk; e += NTS) Gw[(size_t)dk * dv + e] = gs[e];
+        load_tile(Qs, LK, qg, dk, t0, T, tid, NTS);
+        for (int e = tid; e < L * w; e += NTS) As[(e / w) * BVB + e % w] = Aw[(e / w) * dv + c0 + e % w];
         if (tid < L) {
             sq[tid] = Sw[tid];                    // sv_i
             sqb[tid] = Sw[tid] * Sw[2 * L + tid];  // sv_i beta_i
@@ -706,7 +712,7 @@ __global__ __launch_bounds__(NTB2) void bwd_b_kernel(BwdArgs a) {
             }
         }
         if (blk == 0)
-            for (int e = tid; e < dk; e += NTB2) {
+            for (int e = tid; e < dk; e += NTS) {
                 float acc = dec * gs[e];
                 for (int i = 0; i < L; ++i) acc = fmaf(sqb[i], Qs[i * LK + e], acc);
                 gs[e] = acc;
@@ -725,10 +731,10 @@ __global__ __launch_bounds__(NTB2) void bwd_b_kernel(BwdArgs a) {
                 if (a.C0) part = fmaf(gr[e][b], a.C0[x], part);
             }
     if (blk == 0 && a.gn0)
-        for (int e = tid; e < dk; e += NTB2) a.gn0[(size_t)p * dk + e] = gs[e];
+        for (int e = tid; e < dk; e += NTS) a.gn0[(size_t)p * dk + e] = gs[e];
     red[tid] = part;
     __syncthreads();
-    for (int s2 = NTB2 / 2; s2 > 0; s2 >>= 1) {
+    for (int s2 = NTS / 2; s2 > 0; s2 >>= 1) {
         if (tid < s2) red[tid] += red[tid + s2];
         __syncthreads();
     }
@@ -981,12 +987,12 @@ __global__ __launch_bounds__(64) void bwd_d_kernel(BwdArgs a) {
 template <typename IO>
 hipError_t launch_bwd_big(const BwdArgs &a, hipStream_t s) {
     const int nch = (a.T + L - 1) / L, nb = (a.dv + BVB - 1) / BVB;
-    hipLaunchKernelGGL(bwd_ckpt_big_kernel<IO>, dim3(nb, a.BH), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_ckpt_big_kernel<IO>, dim3(nb, a.BH), dim3(NTS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_a_kernel<IO>, dim3(nch, a.BH), dim3(NTA), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_b_kernel<IO>, dim3(nb, a.BH), dim3(NTB2), 0, s, a);
+    hipLaunchKernelGGL(bwd_b_kernel<IO>, dim3(nb, a.BH), dim3(NTS), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_c_kernel<IO>, dim3(nch, a.BH), dim3(NTA), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -98,7 +98,7 @@ __host__ __device__ inline size_t bwd_rec_floats(int dk, int dv) {
 // every section starts 16-byte aligned.  Per chunk c: the state at its start
 // (C', n', m), the rows a_i = dh sigmoid(o~)/den, the matrices P and P~, the
 // scalars (sv, w, beta; dec), the carried gradients entering it (G*, g*) and
-// the sum over its tokens of q.dq - k.dk; then one dm0 partial per block of 64
+// the sum over its tokens of q.dq - k.dk; then one dm0 partial per block of
 // value columns and the checkpoint pass's K, V tiles.
 struct BwdBigLayout {
     size_t nch, rec, grec;
