@@ -227,12 +227,11 @@ mlstm_status_t mlstm_step(const void *q, const void *k, const void *v,
  *            bytes; contents on entry are irrelevant.
  *
  * Gradients are float32 for either io dtype.  Supported heads: d_qk <= 256
- * and d_v <= 512, multiples of 16 (both <= 64: one compute unit per
- * sequence; larger: the chunks' local terms in parallel and the carried
- * gradient scanned by blocks of value columns, with the per-chunk states,
- * rows and carried gradients kept in the workspace, about
- * T/32 * (2 d_qk d_v + 32 d_v) floats per sequence).  Larger heads return
- * MLSTM_ERR_UNSUPPORTED.
+ * and d_v <= 512, multiples of 16: the chunks' local terms are computed in
+ * parallel and the carried gradient is scanned by blocks of value columns,
+ * with the per-chunk states, rows and carried gradients kept in the
+ * workspace, about T/32 * (2 d_qk d_v + 32 d_v) floats per sequence.
+ * Larger heads return MLSTM_ERR_UNSUPPORTED.
  * Errors as for mlstm_fwd_chunkwise; every output must overlap no input, no
  * other output and no workspace (MLSTM_ERR_ALIAS).
  */

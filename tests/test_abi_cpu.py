@@ -262,18 +262,16 @@ def bws(*args):
 
 
 def test_bwd_workspace_query(lib):
-    s, n = bws(2, 3, 70, 64, 48, 32, B.F32)
-    # the state (C', n', m) at every 32-token chunk start of every pair
-    assert s == OK and n == 6 * 3 * (64 * 48 + 64 + 1) * 4
-    # heads above 64, per pair and chunk: the state record (padded to 4
-    # floats), the rows a [32][dv], P and P~ [2][32][32], four scalars per
-    # token, the carried-gradient record (padded); then the chunk totals
+    # per pair and chunk: the state record (C', n', m; padded to 4 floats),
+    # the rows a [32][dv], P and P~ [2][32][32], four scalars per token, the
+    # carried-gradient record (G*, g*; padded); then the chunk totals
     # (padded), 64 dm0 partials and the checkpoint pass's K, V tiles
-    s, n = bws(2, 3, 70, 128, 64, 32, B.F32)
     up4 = lambda x: (x + 3) // 4 * 4
-    nch, rec, grec = 3, up4(128 * 64 + 128 + 1), up4(128 * 64 + 128)
-    per_pair = nch * (rec + 32 * 64 + 2 * 32 * 32 + 4 * 32 + grec) + up4(nch) + 64 + 32 * (128 + 64)
-    assert s == OK and n == 6 * per_pair * 4
+    for dk, dv in ((64, 48), (128, 64)):
+        s, n = bws(2, 3, 70, dk, dv, 32, B.F32)
+        nch, rec, grec = 3, up4(dk * dv + dk + 1), up4(dk * dv + dk)
+        per_pair = nch * (rec + 32 * dv + 2 * 32 * 32 + 4 * 32 + grec) + up4(nch) + 64 + 32 * (dk + dv)
+        assert s == OK and n == 6 * per_pair * 4, (dk, dv)
     assert bws(2, 3, 70, 256, 512, 32, B.BF16)[0] == OK
     assert bws(2, 3, 70, 272, 64, 32, B.F32)[0] == UNSUP     # d_qk above 256
     assert bws(2, 3, 70, 64, 528, 32, B.BF16)[0] == UNSUP    # d_v above 512

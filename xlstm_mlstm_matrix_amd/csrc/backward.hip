@@ -27,21 +27,19 @@
 // with w_j = e^{u_j - r_{L-1}}; after the first chunk G* and g* are the
 // gradients of the initial state (C0, n0) and dm0 = <dC0, C0> + dn0 . n0.
 //
-// For d_qk, d_v <= 64, two launches: the first runs the forward state
-// recurrence per pair and stores the state (C', n', m) at every chunk start
-// in the workspace; the second walks the chunks backwards, one workgroup per
-// pair with its tiles, the chunk-start state and G* in LDS (float32
-// throughout).  Larger heads (d_qk <= 256, d_v <= 512) split the same work
-// into chunk-parallel passes and column-block scans (see the section on heads
-// above 64 below).
+// Five launches (d_qk <= 256, d_v <= 512): a checkpoint pass stores the
+// state (C', n', m) at every chunk start, and chunk-parallel passes and
+// column-block scans take the gradients from there (the section "the passes"
+// below).  A single workgroup per pair walking the chunks backwards leaves
+// the chip idle at small batch and cannot hold heads above 64 in LDS; the
+// passes have B*H*(T/L) workgroups in their chunk-parallel launches.
 #include "common.hpp"
 
 namespace mlstm {
 
 namespace {
 
-constexpr int L = kBwdChunk, D = kBwdMaxDim, NTH = 256;
-constexpr int LD = D + 4;  // padded row length of the backward kernel's tiles (floats, 16-byte rows)
+constexpr int L = kBwdChunk;
 
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ float hsum(f32x4 x) { return (x[0] + x[1]) + (x[2] + x[3]); }
@@ -87,260 +85,16 @@ __device__ void chunk_gates(const float *ig, const float *fg, int t0, int T, flo
     }
 }
 
-template <typename IO>
-__global__ __launch_bounds__(NTH) void bwd_ckpt_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(16))) float Cs[D * D], Kt[L * D], Vt[L * D];
-    __shared__ float ns[D], wv[L], gb[L], gu[L], gr[L], last[2];
-    const int p = blockIdx.x, tid = threadIdx.x;
-    const int dk = a.dk, dv = a.dv, T = a.T;
-    const int nch = (T + L - 1) / L;
-    const size_t rec = (size_t)dk * dv + dk + 1;
-    const IO *kg = static_cast<const IO *>(a.k) + (size_t)p * T * dk;
-    const IO *vg = static_cast<const IO *>(a.v) + (size_t)p * T * dv;
-    const float *igp = a.ig + (size_t)p * T, *fgp = a.fg + (size_t)p * T;
-
-    for (int e = tid; e < dk * dv; e += NTH) Cs[e] = a.C0 ? a.C0[(size_t)p * dk * dv + e] : 0.0f;
-    for (int e = tid; e < dk; e += NTH) ns[e] = a.n0 ? a.n0[(size_t)p * dk + e] : 0.0f;
-    float m = a.m0 ? a.m0[p] : 0.0f;
-    __syncthreads();
-    float *ck = a.ckpt + (size_t)p * nch * rec;
-    for (int c = 0; c < nch; ++c) {
-        const int t0 = c * L;
-        float *r = ck + (size_t)c * rec;
-        for (int e = tid; e < dk * dv; e += NTH) r[e] = Cs[e];
-        for (int e = tid; e < dk; e += NTH) r[(size_t)dk * dv + e] = ns[e];
-        if (tid == 0) r[(size_t)dk * dv + dk] = m;
-        for (int e = tid; e < L * dk; e += NTH) {
-            const int t = t0 + e / dk;
-            Kt[e] = t < T ? to_f(kg[(size_t)t * dk + e % dk]) : 0.0f;
-        }
-        for (int e = tid; e < L * dv; e += NTH) {
-            const int t = t0 + e / dv;
-            Vt[e] = t < T ? to_f(vg[(size_t)t * dv + e % dv]) : 0.0f;
-        }
-        if (tid < 64) chunk_gates(igp, fgp, t0, T, m, gb, gu, gr, last);
-        __syncthreads();
-        const float b_last = last[0], r_last = last[1];
-        const float dec = exp_e(m - r_last);
-        if (tid < L) wv[tid] = exp_e(gu[tid] - r_last);
-        __syncthreads();
-        for (int e = tid; e < dk * dv / 4; e += NTH) {
-            const int row = (4 * e) / dv, col = (4 * e) % dv;
-            f32x4 acc = dec * ld4(&Cs[4 * e]);
-#pragma unroll 4
-            for (int j = 0; j < L; ++j) acc += (wv[j] * Kt[j * dk + row]) * ld4(&Vt[j * dv + col]);
-            *reinterpret_cast<f32x4 *>(&Cs[4 * e]) = acc;
-        }
-        for (int e = tid; e < dk; e += NTH) {
-            float acc = dec * ns[e];
-            for (int j = 0; j < L; ++j) acc = fmaf(wv[j], Kt[j * dk + e], acc);
-            ns[e] = acc;
-        }
-        m = b_last + r_last;
-        __syncthreads();
-    }
-}
-
-template <typename IO>
-__global__ __launch_bounds__(NTH) void bwd_kernel(BwdArgs a) {
-    // rows padded to LD floats: column walks (lanes on consecutive rows) then
-    // fall on consecutive banks
-    __shared__ __attribute__((aligned(16))) float Q[L * LD], K[L * LD], V[L * LD], SG[L * LD], DH[L * LD],
-        NUM[L * LD], A[L * LD], DQ[L * LD], DK[L * LD];
-    __shared__ __attribute__((aligned(16))) float Cc[D * LD], Gs[D * LD], P[L * L], PT[L * L];
-    __shared__ float nc[D], gs[D], gb[L], gu[L], gr[L], sv[L], fl[L], wv[L], dd[L], den[L], beta[L];
-    __shared__ float last[2], carry, red[NTH];
-    const int p = blockIdx.x, tid = threadIdx.x;
-    const int dk = a.dk, dv = a.dv, T = a.T;
-    const int nch = (T + L - 1) / L;
-    const size_t rec = (size_t)dk * dv + dk + 1;
-    const size_t oqk = (size_t)p * T * dk, ov = (size_t)p * T * dv, og1 = (size_t)p * T;
-    const IO *qg = static_cast<const IO *>(a.q) + oqk;
-    const IO *kg = static_cast<const IO *>(a.k) + oqk;
-    const IO *vg = static_cast<const IO *>(a.v) + ov;
-    const IO *ogp = static_cast<const IO *>(a.o) + ov;
-    const IO *dhg = static_cast<const IO *>(a.dh) + ov;
-
-    for (int e = tid; e < D * LD; e += NTH) Gs[e] = 0.0f;
-    for (int e = tid; e < dk; e += NTH) gs[e] = 0.0f;
-    if (tid == 0) carry = 0.0f;
-    __syncthreads();
-    for (int c = nch - 1; c >= 0; --c) {
-        const int t0 = c * L;
-        const float *ck = a.ckpt + ((size_t)p * nch + c) * rec;
-        for (int e = tid; e < dk * dv; e += NTH) Cc[(e / dv) * LD + e % dv] = ck[e];
-        for (int e = tid; e < dk; e += NTH) nc[e] = ck[(size_t)dk * dv + e];
-        const float m_prev = ck[(size_t)dk * dv + dk];
-        for (int e = tid; e < L * dk; e += NTH) {
-            const int i = e / dk, t = t0 + i;
-            const size_t g = (size_t)t * dk + e % dk;
-            Q[i * LD + e % dk] = t < T ? to_f(qg[g]) : 0.0f;
-            K[i * LD + e % dk] = t < T ? to_f(kg[g]) : 0.0f;
-        }
-        for (int e = tid; e < L * dv; e += NTH) {
-            const int i = e / dv, t = t0 + i, x = i * LD + e % dv;
-            const size_t g = (size_t)t * dv + e % dv;
-            V[x] = t < T ? to_f(vg[g]) : 0.0f;
-            SG[x] = t < T ? sigmoid(to_f(ogp[g])) : 0.0f;
-            DH[x] = t < T ? to_f(dhg[g]) : 0.0f;
-        }
-        if (tid < 64) chunk_gates(a.ig + og1, a.fg + og1, t0, T, m_prev, gb, gu, gr, last);
-        __syncthreads();
-        const float r_last = last[1];
-        const float dec = exp_e(m_prev - r_last);
-        if (tid < L) {
-            sv[tid] = exp_e(m_prev - gr[tid]);
-            fl[tid] = exp_e(-(gb[tid] + gr[tid]));
-            wv[tid] = exp_e(gu[tid] - r_last);
-        }
-        // P_ij = (q_i.k_j) e^{u_j - r_i}, causal, rows of real tokens only
-        for (int e = tid; e < L * L; e += NTH) {
-            const int i = e / L, j = e % L;
-            float s = 0.0f;
-            if (j <= i && t0 + i < T) s = dot(&Q[i * LD], &K[j * LD], dk) * exp_e(gu[j] - gr[i]);
-            P[e] = s;
-        }
-        __syncthreads();
-        // forward read-out and denominator, recomputed
-        for (int e = tid; e < L * dv / 4; e += NTH) {
-            const int i = (4 * e) / dv, b = (4 * e) % dv;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int r = 0; r < dk; ++r) acc += Q[i * LD + r] * ld4(&Cc[r * LD + b]);
-            acc *= sv[i];
-            for (int j = 0; j <= i; ++j) acc += P[i * L + j] * ld4(&V[j * LD + b]);
-            *reinterpret_cast<f32x4 *>(&NUM[i * LD + b]) = acc;
-        }
-        if (tid < L) {
-            const int i = tid;
-            float acc = 0.0f;
-            for (int r = 0; r < dk; ++r) acc = fmaf(nc[r], Q[i * LD + r], acc);
-            acc *= sv[i];
-            for (int j = 0; j <= i; ++j) acc += P[i * L + j];
-            dd[i] = acc;
-            den[i] = fmaxf(fabsf(acc), fl[i]);
-        }
-        __syncthreads();
-        // a = dh sigmoid(o~) / den, and the output-gate gradient
-        for (int e = tid; e < L * dv; e += NTH) {
-            const int i = e / dv, x = i * LD + e % dv;
-            const float sg = SG[x];
-            A[x] = DH[x] * sg / den[i];
-            const int t = t0 + i;
-            if (t < T) a.go[ov + (size_t)t * dv + e % dv] = DH[x] * NUM[x] / den[i] * sg * (1.0f - sg);
-        }
-        __syncthreads();
-        if (tid < L) {
-            const int i = tid;
-            const float an = dot(&A[i * LD], &NUM[i * LD], dv);
-            beta[i] = fabsf(dd[i]) > fl[i] ? (dd[i] > 0.0f ? -an : an) / den[i] : 0.0f;
-        }
-        __syncthreads();
-        // P~_ij = (a_i.v_j + beta_i) e^{u_j - r_i}
-        for (int e = tid; e < L * L; e += NTH) {
-            const int i = e / L, j = e % L;
-            float s = 0.0f;
-            if (j <= i && t0 + i < T) s = (dot(&A[i * LD], &V[j * LD], dv) + beta[i]) * exp_e(gu[j] - gr[i]);
-            PT[e] = s;
-        }
-        __syncthreads();
-        for (int e = tid; e < L * dk; e += NTH) {
-            const int i = e / dk, r = e % dk;
-            float acc = sv[i] * fmaf(nc[r], beta[i], dot(&Cc[r * LD], &A[i * LD], dv));
-            for (int j = 0; j <= i; ++j) acc = fmaf(PT[i * L + j], K[j * LD + r], acc);
-            DQ[i * LD + r] = acc;
-            const int t = t0 + i;
-            if (t < T) a.gq[oqk + (size_t)t * dk + r] = acc;
-        }
-        for (int e = tid; e < L * dk; e += NTH) {
-            const int j = e / dk, r = e % dk;
-            float acc = 0.0f;
-            for (int i = j; i < L; ++i) acc = fmaf(PT[i * L + j], Q[i * LD + r], acc);
-            acc = fmaf(wv[j], gs[r] + dot(&Gs[r * LD], &V[j * LD], dv), acc);
-            DK[j * LD + r] = acc;
-            const int t = t0 + j;
-            if (t < T) a.gk[oqk + (size_t)t * dk + r] = acc;
-        }
-        for (int e = tid; e < L * dv / 4; e += NTH) {
-            const int j = (4 * e) / dv, b = (4 * e) % dv;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, gk = {0.f, 0.f, 0.f, 0.f};
-            for (int i = j; i < L; ++i) acc += P[i * L + j] * ld4(&A[i * LD + b]);
-#pragma unroll 4
-            for (int r = 0; r < dk; ++r) gk += K[j * LD + r] * ld4(&Gs[r * LD + b]);
-            acc += wv[j] * gk;
-            const int t = t0 + j;
-            if (t < T) *reinterpret_cast<f32x4 *>(&a.gv[ov + (size_t)t * dv + b]) = acc;
-        }
-        __syncthreads();
-        // gate gradients: di = k.dk; df = reverse cumsum of q.dq - k.dk
-        if (tid < 64) {
-            const int j = tid, t = t0 + j;
-            const bool ok = j < L && t < T;
-            float di = 0.0f, x = 0.0f;
-            if (ok) {
-                di = dot(&K[j * LD], &DK[j * LD], dk);
-                x = dot(&Q[j * LD], &DQ[j * LD], dk) - di;
-            }
-            float y = x;  // sum over lanes >= j
-            for (int o = 1; o < 64; o <<= 1) {
-                const float z = __shfl_down(y, o, 64);
-                if (j + o < 64) y += z;
-            }
-            const float cin = carry;
-            if (ok) {
-                a.gi[og1 + t] = di;
-                a.gf[og1 + t] = y + cin;
-            }
-            const float tot = __shfl(y, 0, 64);
-            if (j == 0) carry = cin + tot;
-        }
-        // carried gradients for the chunk before (every read of G*, g* is past
-        // the barrier above)
-        for (int e = tid; e < dk * dv / 4; e += NTH) {
-            const int r = (4 * e) / dv, b = (4 * e) % dv;
-            f32x4 acc = dec * ld4(&Gs[r * LD + b]);
-#pragma unroll 4
-            for (int i = 0; i < L; ++i) acc += (sv[i] * Q[i * LD + r]) * ld4(&A[i * LD + b]);
-            *reinterpret_cast<f32x4 *>(&Gs[r * LD + b]) = acc;
-        }
-        for (int e = tid; e < dk; e += NTH) {
-            float acc = dec * gs[e];
-            for (int i = 0; i < L; ++i) acc = fmaf(sv[i] * beta[i], Q[i * LD + e], acc);
-            gs[e] = acc;
-        }
-        __syncthreads();
-    }
-    // gradients of the initial state
-    float part = 0.0f;
-    for (int e = tid; e < dk * dv; e += NTH) {
-        const float gx = Gs[(e / dv) * LD + e % dv];
-        if (a.gC0) a.gC0[(size_t)p * dk * dv + e] = gx;
-        if (a.C0) part = fmaf(gx, a.C0[(size_t)p * dk * dv + e], part);
-    }
-    for (int e = tid; e < dk; e += NTH) {
-        if (a.gn0) a.gn0[(size_t)p * dk + e] = gs[e];
-        if (a.n0) part = fmaf(gs[e], a.n0[(size_t)p * dk + e], part);
-    }
-    red[tid] = part;
-    __syncthreads();
-    for (int w = NTH / 2; w > 0; w >>= 1) {
-        if (tid < w) red[tid] += red[tid + w];
-        __syncthreads();
-    }
-    if (tid == 0 && a.gm0) a.gm0[p] = red[0];
-}
-
-// ---- heads above 64 (d_qk <= 256, d_v <= 512).  The pair's state is too
-// large for one compute unit, and only the carried gradient G* is sequential
-// over chunks: everything else of a chunk follows from its checkpointed
-// state.  So, after the checkpoint pass:
+// ---- the passes.  Only the carried gradient G* is sequential over chunks:
+// everything else of a chunk follows from its checkpointed state.  So, after
+// the checkpoint pass:
 //   A (pair, chunk): P, the read-out, a, beta, P~ and do~            -> workspace
 //   B (pair, BVB value columns): the reverse scan of G*, g* over the chunks,
 //     storing the value entering every chunk; dC0, dn0 and dm0 partials
 //   C (pair, chunk): dq, dk, dv, di~ and the in-chunk part of df~
 //   D (pair): df~'s carry across chunks and dm0
 // Tiles live in LDS in float32; the state, a, G* come from the workspace
-// through the caches.  Workspace layout: bwd_big_layout.
+// through the caches.  Workspace layout: bwd_layout.
 
 #ifndef BWD_BVB
 #define BWD_BVB 128
@@ -365,20 +119,20 @@ __device__ __forceinline__ f32x4 ld4_io(const IO *p) {
     return f32x4{to_f(p[0]), to_f(p[1]), to_f(p[2]), to_f(p[3])};
 }
 
-// Checkpoint pass for large heads: one workgroup per (block of BVB value
+// Checkpoint pass: one workgroup per (block of BVB value
 // columns, pair).  The state recurrence is separable by value column, so each
 // workgroup carries its [d_qk][BVB] block of C' in registers (a 4 x 16 tile
 // per thread) and writes it to the record of every chunk start; block 0 also
 // carries n' and writes m (every block computes the same gates).
 template <typename IO>
-__global__ __launch_bounds__(NTS) void bwd_ckpt_big_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTS) void bwd_ckpt_kernel(BwdArgs a) {
     constexpr int LK = kBwdMaxDk + 4;
     __shared__ __attribute__((aligned(16))) float Ks[L * LK], Vs[L * BVB];
     __shared__ float ns[kBwdMaxDk], wv[L], gb[L], gu[L], gr[L], last[2];
     const int blk = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T;
     const int c0 = blk * BVB, w = min(BVB, dv - c0);
-    const BwdBigLayout lay = bwd_big_layout(T, dk, dv);
+    const BwdLayout lay = bwd_layout(T, dk, dv);
     const int nch = (int)lay.nch;
     const size_t rec = lay.rec;
     float *base = a.ckpt + (size_t)p * lay.total;
@@ -469,7 +223,7 @@ __global__ __launch_bounds__(NTA) void bwd_a_kernel(BwdArgs a) {
     __shared__ float gb[L], gu[L], gr[L], sv[L], fl[L], dd[L], den[L], beta[L], last[2];
     const int c = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T, t0 = c * L;
-    const BwdBigLayout lay = bwd_big_layout(T, dk, dv);
+    const BwdLayout lay = bwd_layout(T, dk, dv);
     float *base = a.ckpt + (size_t)p * lay.total;
     const float *Cc = base + (size_t)c * lay.rec;  // C' rows of dv floats, then n', m
     const float *ncg = Cc + (size_t)dk * dv;
@@ -655,7 +409,7 @@ __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
     const int blk = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T;
     const int c0 = blk * BVB, w = min(BVB, dv - c0);  // this block's columns [c0, c0 + w)
-    const BwdBigLayout lay = bwd_big_layout(T, dk, dv);
+    const BwdLayout lay = bwd_layout(T, dk, dv);
     const int nch = (int)lay.nch;
     float *base = a.ckpt + (size_t)p * lay.total;
     const IO *qg = static_cast<const IO *>(a.q) + (size_t)p * T * dk;
@@ -758,7 +512,7 @@ __global__ __launch_bounds__(NTA) void bwd_c_kernel(BwdArgs a) {
     __shared__ float pq[L * NRGM], pk[L * NRGM];
     const int c = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T, t0 = c * L;
-    const BwdBigLayout lay = bwd_big_layout(T, dk, dv);
+    const BwdLayout lay = bwd_layout(T, dk, dv);
     float *base = a.ckpt + (size_t)p * lay.total;
     const float *Cc = base + (size_t)c * lay.rec;
     const float *ncg = Cc + (size_t)dk * dv;
@@ -960,7 +714,7 @@ __global__ __launch_bounds__(NTA) void bwd_c_kernel(BwdArgs a) {
 __global__ __launch_bounds__(64) void bwd_d_kernel(BwdArgs a) {
     const int p = blockIdx.x, lane = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T;
-    const BwdBigLayout lay = bwd_big_layout(T, dk, dv);
+    const BwdLayout lay = bwd_layout(T, dk, dv);
     const int nch = (int)lay.nch;
     const float *base = a.ckpt + (size_t)p * lay.total;
     const size_t og1 = (size_t)p * T;
@@ -985,9 +739,9 @@ __global__ __launch_bounds__(64) void bwd_d_kernel(BwdArgs a) {
 }
 
 template <typename IO>
-hipError_t launch_bwd_big(const BwdArgs &a, hipStream_t s) {
+hipError_t launch_passes(const BwdArgs &a, hipStream_t s) {
     const int nch = (a.T + L - 1) / L, nb = (a.dv + BVB - 1) / BVB;
-    hipLaunchKernelGGL(bwd_ckpt_big_kernel<IO>, dim3(nb, a.BH), dim3(NTS), 0, s, a);
+    hipLaunchKernelGGL(bwd_ckpt_kernel<IO>, dim3(nb, a.BH), dim3(NTS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_a_kernel<IO>, dim3(nch, a.BH), dim3(NTA), 0, s, a);
@@ -1003,20 +757,7 @@ hipError_t launch_bwd_big(const BwdArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs &a, int io_bf16, hipStream_t s) {
-    if (bwd_big(a.dk, a.dv)) return io_bf16 ? launch_bwd_big<bf16>(a, s) : launch_bwd_big<float>(a, s);
-    dim3 grid(a.BH), block(NTH);
-    if (io_bf16) {
-        hipLaunchKernelGGL(bwd_ckpt_kernel<bf16>, grid, block, 0, s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(bwd_kernel<bf16>, grid, block, 0, s, a);
-    } else {
-        hipLaunchKernelGGL(bwd_ckpt_kernel<float>, grid, block, 0, s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(bwd_kernel<float>, grid, block, 0, s, a);
-    }
-    return hipGetLastError();
+    return io_bf16 ? launch_passes<bf16>(a, s) : launch_passes<float>(a, s);
 }
 
 }  // namespace mlstm

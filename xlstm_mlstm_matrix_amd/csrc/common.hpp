@@ -82,33 +82,24 @@ struct BwdArgs {
     int BH, T, dk, dv;
 };
 
-// Tokens per chunk and largest head dimensions of the backward kernels, and
-// the floats one pair needs in the backward's workspace.
+// Tokens per chunk and largest head dimensions of the backward kernels.
 constexpr int kBwdChunk = 32;
-constexpr int kBwdMaxDim = 64;          // both head dims up to this: tiles and state in LDS
-constexpr int kBwdMaxDk = 256, kBwdMaxDv = 512;  // larger heads: tiles and state in global scratch
-__host__ __device__ inline bool bwd_big(int dk, int dv) { return dk > kBwdMaxDim || dv > kBwdMaxDim; }
-// floats of one checkpoint record (C', n', m); padded to 16 bytes for large heads,
-// whose kernels read its rows with 16-byte loads
-__host__ __device__ inline size_t bwd_rec_floats(int dk, int dv) {
-    const size_t r = (size_t)dk * dv + dk + 1;
-    return bwd_big(dk, dv) ? (r + 3) / 4 * 4 : r;
-}
-// Workspace of one pair for heads above 64, in floats from the pair's base;
-// every section starts 16-byte aligned.  Per chunk c: the state at its start
-// (C', n', m), the rows a_i = dh sigmoid(o~)/den, the matrices P and P~, the
-// scalars (sv, w, beta; dec), the carried gradients entering it (G*, g*) and
-// the sum over its tokens of q.dq - k.dk; then one dm0 partial per block of
-// value columns and the checkpoint pass's K, V tiles.
-struct BwdBigLayout {
+constexpr int kBwdMaxDk = 256, kBwdMaxDv = 512;
+// Workspace of one pair, in floats from the pair's base; every section starts
+// 16-byte aligned.  Per chunk c: the state at its start (C', n', m; padded so
+// that its rows are read with 16-byte loads), the rows a_i = dh sigmoid(o~)/den,
+// the matrices P and P~, the scalars (sv, w, beta; dec), the carried gradients
+// entering it (G*, g*) and the sum over its tokens of q.dq - k.dk; then one
+// dm0 partial per block of value columns and the checkpoint pass's K, V tiles.
+struct BwdLayout {
     size_t nch, rec, grec;
     size_t off_a, off_p, off_s, off_g, off_x, off_m, off_tile, total;
 };
-__host__ __device__ inline BwdBigLayout bwd_big_layout(int T, int dk, int dv) {
+__host__ __device__ inline BwdLayout bwd_layout(int T, int dk, int dv) {
     const size_t L = kBwdChunk;
-    BwdBigLayout o;
+    BwdLayout o;
     o.nch = ((size_t)T + L - 1) / L;
-    o.rec = bwd_rec_floats(dk, dv);
+    o.rec = ((size_t)dk * dv + dk + 1 + 3) / 4 * 4;
     o.grec = ((size_t)dk * dv + dk + 3) / 4 * 4;
     o.off_a = o.nch * o.rec;
     o.off_p = o.off_a + o.nch * L * dv;
@@ -120,10 +111,7 @@ __host__ __device__ inline BwdBigLayout bwd_big_layout(int T, int dk, int dv) {
     o.total = o.off_tile + L * ((size_t)dk + dv);
     return o;
 }
-__host__ __device__ inline size_t bwd_ckpt_floats(int T, int dk, int dv) {
-    if (bwd_big(dk, dv)) return bwd_big_layout(T, dk, dv).total;
-    return (size_t)((T + kBwdChunk - 1) / kBwdChunk) * bwd_rec_floats(dk, dv);
-}
+__host__ __device__ inline size_t bwd_ckpt_floats(int T, int dk, int dv) { return bwd_layout(T, dk, dv).total; }
 
 // Launchers (defined in the .hip files).  Return hipSuccess or the launch error.
 hipError_t launch_step(const StepArgs &a, int io_bf16, hipStream_t s);
