@@ -51,18 +51,14 @@ __device__ __forceinline__ float dot(const float *x, const float *y, int n) {
     return hsum(acc);
 }
 
-// In-chunk gate quantities of tokens t0 .. t0 + L - 1 for the stabilizer
-// m_before, by one wavefront (lane j = token j; tokens past T act as i~ =
-// -inf, f~ = 0, which leaves every running quantity unchanged):
-// gb = cumsum f~, gu = i~ - gb, gr = max(m_before, prefix max gu); last =
-// (gb, gr) of the chunk's last token.
-__device__ void chunk_gates(const float *ig, const float *fg, int t0, int T, float m_before, float *gb,
-                            float *gu, float *gr, float *last) {
+// In-chunk gate quantities of one chunk for the stabilizer m_before, by one
+// wavefront (lane j = token j, given its f~ and i~; tokens past T and lanes
+// past L act as i~ = -inf, f~ = 0, which leaves every running quantity
+// unchanged): gb = cumsum f~, gu = i~ - gb, gr = max(m_before, prefix max
+// gu); last = (gb, gr) of the chunk's last token.  Returns the lane's (u, r).
+__device__ void gate_scan(float b, float i, float m_before, float *gb, float *gu, float *gr, float *last,
+                          float *u_out, float *r_out) {
     const int lane = threadIdx.x & 63;
-    const int t = t0 + lane;
-    const bool ok = lane < L && t < T;
-    float b = ok ? fg[t] : 0.0f;
-    const float i = ok ? ig[t] : -INFINITY;
     for (int o = 1; o < 64; o <<= 1) {
         const float y = __shfl_up(b, o, 64);
         if (lane >= o) b += y;
@@ -83,6 +79,18 @@ __device__ void chunk_gates(const float *ig, const float *fg, int t0, int T, flo
         last[0] = b;
         last[1] = r;
     }
+    *u_out = u;
+    *r_out = r;
+}
+
+// gate_scan of tokens t0 .. t0 + L - 1, loading their gates
+__device__ void chunk_gates(const float *ig, const float *fg, int t0, int T, float m_before, float *gb,
+                            float *gu, float *gr, float *last) {
+    const int lane = threadIdx.x & 63;
+    const int t = t0 + lane;
+    const bool ok = lane < L && t < T;
+    float u, r;
+    gate_scan(ok ? fg[t] : 0.0f, ok ? ig[t] : -INFINITY, m_before, gb, gu, gr, last, &u, &r);
 }
 
 // ---- the passes.  Only the carried gradient G* is sequential over chunks:
@@ -119,15 +127,98 @@ __device__ __forceinline__ f32x4 ld4_io(const IO *p) {
     return f32x4{to_f(p[0]), to_f(p[1]), to_f(p[2]), to_f(p[3])};
 }
 
-// Checkpoint pass: one workgroup per (block of BVB value
-// columns, pair).  The state recurrence is separable by value column, so each
-// workgroup carries its [d_qk][BVB] block of C' in registers (a 4 x 16 tile
-// per thread) and writes it to the record of every chunk start; block 0 also
-// carries n' and writes m (every block computes the same gates).
+// Barrier for the two scans.  Within them only LDS is shared between the
+// wavefronts (their global stores are read by later launches), so this waits
+// for this wavefront's LDS operations and not for the outstanding global
+// loads of the next chunk, unlike __syncthreads(), whose fence waits for
+// every memory access.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Buffer descriptor over nbytes from p (32-bit data format, default cache
+// policy).  Loads at offsets past nbytes return zero without touching memory.
+constexpr int kBufFlags = 0x00020000;
+constexpr unsigned kFar = 0x80000000u;  // an offset past every buffer here (nbytes <= 2^31)
+template <typename E>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const E *p, size_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<E *>(p), 0, (int)nbytes, kBufFlags);
+}
+
+// Four consecutive elements, loaded in one instruction and converted later.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <typename E> struct Quad;
+template <> struct Quad<float> {
+    typedef f32x4 raw;
+    static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    }
+    static __device__ __forceinline__ f32x4 cvt(raw x) { return x; }
+};
+template <> struct Quad<bf16> {
+    typedef bf16x4 raw;
+    static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    }
+    static __device__ __forceinline__ f32x4 cvt(raw x) {
+        return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    }
+};
+
+// Rows t0 .. t0 + L - 1, columns [c0, c0 + w) of a row-major tensor with ld
+// elements per row, staged through registers in groups of four: fetch()
+// issues the loads of one chunk, put() converts them to float32 and writes
+// them to an [L][ldd] LDS tile.  Rows past the descriptor's end (tokens past
+// T) read as zero; groups past the tile (NQ * NT may exceed L * w / 4) load
+// nothing and are not written.  w and c0 are multiples of 4.
+template <typename E, int NQ, int NT>
+struct TileFetch {
+    typename Quad<E>::raw r[NQ];
+    __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, int ld, int c0, int w, int t0, int tid) {
+        const int g4 = w >> 2;
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+            const int q = tid + u * NT, i = q / g4;
+            const unsigned e = (unsigned)(t0 + i) * (unsigned)ld + (unsigned)(c0 + 4 * (q - i * g4));
+            r[u] = Quad<E>::load(rs, i < L ? e * (unsigned)sizeof(E) : kFar);
+        }
+    }
+    // dst holds L * ldd floats and one spare group after them, which takes
+    // the surplus groups (no branch: a store skipped on some lanes would
+    // leave its loads unwaited on that path, and the compiler's merged wait
+    // counts would then also wait for the stores issued after them)
+    __device__ __forceinline__ void put(float *dst, int ldd, int w, int tid) const {
+        const int g4 = w >> 2;
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+            const int q = tid + u * NT, i = q / g4;
+            *reinterpret_cast<f32x4 *>(&dst[i < L ? i * ldd + 4 * (q - i * g4) : L * ldd]) = Quad<E>::cvt(r[u]);
+        }
+    }
+};
+
+// 16- and 4-byte buffer accesses of float32 data (stores past the
+// descriptor's end are dropped, loads there return zero)
+__device__ __forceinline__ f32x4 buf_ld4(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buf_st4(f32x4 x, __amdgpu_buffer_rsrc_t r, unsigned off) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_st1(float x, __amdgpu_buffer_rsrc_t r, unsigned off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, (int)off, 0, 0);
+}
+
+// Checkpoint pass: one workgroup per (block of BVB value columns, pair).  The
+// state recurrence is separable by value column, so each workgroup carries
+// its [d_qk][BVB] block of C' in registers (a 4 x 16 tile per thread) and
+// writes it to the record of every chunk start; block 0 also carries n' and
+// writes m (every block computes the same gates).  The K and V tiles and the
+// gates of the next chunk load while the current chunk computes.
 template <typename IO>
 __global__ __launch_bounds__(NTS) void bwd_ckpt_kernel(BwdArgs a) {
     constexpr int LK = kBwdMaxDk + 4;
-    __shared__ __attribute__((aligned(16))) float Ks[L * LK], Vs[L * BVB];
+    __shared__ __attribute__((aligned(16))) float Ks[L * LK + 4], Vs[L * BVB + 4];
     __shared__ float ns[kBwdMaxDk], wv[L], gb[L], gu[L], gr[L], last[2];
     const int blk = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T;
@@ -139,47 +230,75 @@ __global__ __launch_bounds__(NTS) void bwd_ckpt_kernel(BwdArgs a) {
     const IO *kg = static_cast<const IO *>(a.k) + (size_t)p * T * dk;
     const IO *vg = static_cast<const IO *>(a.v) + (size_t)p * T * dv;
     const float *igp = a.ig + (size_t)p * T, *fgp = a.fg + (size_t)p * T;
-    // this thread's tile: rows 4*rg .. +3, block columns 16*cg .. +15
+    const __amdgpu_buffer_rsrc_t kr = rsrc(kg, (size_t)T * dk * sizeof(IO));
+    const __amdgpu_buffer_rsrc_t vr = rsrc(vg, (size_t)T * dv * sizeof(IO));
+    TileFetch<IO, L * kBwdMaxDk / 4 / NTS, NTS> kf;
+    TileFetch<IO, L * BVB / 4 / NTS, NTS> vf;
+    // every lane loads the gates of token t0 + lane % 64 (clamped into the
+    // sequence), and every wavefront runs the same scan of them
+    const int lane = tid & 63;
+    float fi, ff;
+    auto fetch = [&](int t0) {
+        kf.fetch(kr, dk, 0, dk, t0, tid);
+        vf.fetch(vr, dv, c0, w, t0, tid);
+        const int t = min(t0 + lane, T - 1);
+        fi = igp[t];
+        ff = fgp[t];
+    };
+    fetch(0);
+    // this thread's tile: rows 4*rg .. +3, block columns 16*cg .. +15; toff
+    // is its byte offset in a [d_qk][d_v] record, past every record when the
+    // tile lies outside the block (its stores are dropped)
     const int rg = tid / CG, cg = tid % CG;
     const bool act = 4 * rg < dk && 16 * cg < w;
+    const unsigned toff = act ? (unsigned)((4 * rg * dv + c0 + 16 * cg) * 4) : kFar;
+    // n' (block 0, threads below d_qk) and m (thread d_qk) follow C' in the record
+    const unsigned noff = (blk == 0 && tid <= dk) ? (unsigned)((dk * dv + tid) * 4) : kFar;
     float cr[4][16];
+    {
+        const __amdgpu_buffer_rsrc_t c0r =
+            a.C0 ? rsrc(a.C0 + (size_t)p * dk * dv, (size_t)dk * dv * 4) : rsrc(a.ckpt, 0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int b = 0; b < 16; ++b)
-            cr[e][b] = (act && a.C0) ? a.C0[(size_t)p * dk * dv + (size_t)(4 * rg + e) * dv + c0 + 16 * cg + b]
-                                     : 0.0f;
+            for (int b = 0; b < 16; b += 4) {
+                const f32x4 x = buf_ld4(c0r, toff + (unsigned)((e * dv + b) * 4));
+#pragma unroll
+                for (int y = 0; y < 4; ++y) cr[e][b + y] = x[y];
+            }
+    }
     if (blk == 0)
         for (int e = tid; e < dk; e += NTS) ns[e] = a.n0 ? a.n0[(size_t)p * dk + e] : 0.0f;
     float m = a.m0 ? a.m0[p] : 0.0f;
     for (int c = 0; c < nch; ++c) {
         const int t0 = c * L;
-        float *r = base + (size_t)c * rec;
-        // the state at this chunk's start
-        if (act)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int b = 0; b < 16; b += 4)
-                    *reinterpret_cast<f32x4 *>(&r[(size_t)(4 * rg + e) * dv + c0 + 16 * cg + b]) =
-                        f32x4{cr[e][b], cr[e][b + 1], cr[e][b + 2], cr[e][b + 3]};
-        __syncthreads();  // ns of the previous chunk complete
-        if (blk == 0) {
-            for (int e = tid; e < dk; e += NTS) r[(size_t)dk * dv + e] = ns[e];
-            if (tid == 0) r[(size_t)dk * dv + dk] = m;
+        // this chunk's tiles and gates into LDS first: they wait only for the
+        // loads issued a chunk ago, not for the record stores below (the
+        // tiles of the last chunk are not used)
+        kf.put(Ks, LK, dk, tid);
+        vf.put(Vs, BVB, w, tid);
+        {
+            const bool ok = lane < L && t0 + lane < T;
+            float u, rr;
+            gate_scan(ok ? ff : 0.0f, ok ? fi : -INFINITY, m, gb, gu, gr, last, &u, &rr);
+            const float r_last = __shfl(rr, L - 1, 64);
+            if (lane < L) wv[lane] = exp_e(u - r_last);
         }
+        // the state at this chunk's start (each thread reads and writes only
+        // its own entries of ns; the other reads are discarded)
+        const __amdgpu_buffer_rsrc_t rs = rsrc(base + (size_t)c * rec, rec * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int b = 0; b < 16; b += 4)
+                buf_st4(f32x4{cr[e][b], cr[e][b + 1], cr[e][b + 2], cr[e][b + 3]}, rs,
+                        toff + (unsigned)((e * dv + b) * 4));
+        buf_st1(tid < dk ? ns[tid < dk ? tid : 0] : m, rs, noff);
         if (c + 1 == nch) break;  // the state after the last chunk is not needed
-        load_tile(Ks, LK, kg, dk, t0, T, tid, NTS);
-        for (int e = tid; e < L * w; e += NTS) {
-            const int j = e / w, t = t0 + j;
-            Vs[j * BVB + e % w] = t < T ? to_f(vg[(size_t)t * dv + c0 + e % w]) : 0.0f;
-        }
-        if (tid < 64) chunk_gates(igp, fgp, t0, T, m, gb, gu, gr, last);
-        __syncthreads();
+        fetch(t0 + L);
+        lds_barrier();
         const float b_last = last[0], r_last = last[1];
         const float dec = exp_e(m - r_last);
-        if (tid < L) wv[tid] = exp_e(gu[tid] - r_last);
-        __syncthreads();
         if (act) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -206,7 +325,7 @@ __global__ __launch_bounds__(NTS) void bwd_ckpt_kernel(BwdArgs a) {
                 ns[e] = acc;
             }
         m = b_last + r_last;
-        __syncthreads();  // the tiles are rewritten next chunk
+        lds_barrier();  // the tiles are rewritten next chunk
     }
 }
 
@@ -403,9 +522,8 @@ __global__ __launch_bounds__(NTA) void bwd_a_kernel(BwdArgs a) {
 template <typename IO>
 __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
     constexpr int LK = kBwdMaxDk + 4;
-    __shared__ __attribute__((aligned(16))) float Qs[L * LK], As[L * BVB];
-    __shared__ float gs[kBwdMaxDk], sq[L], sqb[L], red[NTS];
-    __shared__ float decs;
+    __shared__ __attribute__((aligned(16))) float Qs[L * LK + 4], As[L * BVB + 4];
+    __shared__ float gs[kBwdMaxDk], sq[L], sqb[L], dcv[L], red[NTS];
     const int blk = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T;
     const int c0 = blk * BVB, w = min(BVB, dv - c0);  // this block's columns [c0, c0 + w)
@@ -413,8 +531,30 @@ __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
     const int nch = (int)lay.nch;
     float *base = a.ckpt + (size_t)p * lay.total;
     const IO *qg = static_cast<const IO *>(a.q) + (size_t)p * T * dk;
+    const __amdgpu_buffer_rsrc_t qr = rsrc(qg, (size_t)T * dk * sizeof(IO));
+    // the next chunk's Q tile, a rows and scalars load while the current
+    // chunk computes; lane l of every wavefront takes token l's sv and beta
+    // and slot l of the chunk's decay row (only slot 0 holds the decay; the
+    // others are unused workspace)
+    TileFetch<IO, L * kBwdMaxDk / 4 / NTS, NTS> qf;
+    TileFetch<float, L * BVB / 4 / NTS, NTS> af;
+    const int l = tid & (L - 1);
+    float s_sv, s_beta, s_dec;
+    auto fetch = [&](int c) {
+        const float *Sw = base + lay.off_s + (size_t)c * 4 * L;
+        qf.fetch(qr, dk, 0, dk, c * L, tid);
+        af.fetch(rsrc(base + lay.off_a + (size_t)c * L * dv, (size_t)L * dv * 4), dv, c0, w, 0, tid);
+        s_sv = Sw[l];
+        s_beta = Sw[2 * L + l];
+        s_dec = Sw[3 * L + l];
+    };
+    fetch(nch - 1);
+    // this thread's tile and its byte offset in a [d_qk][d_v] record (past
+    // every record when the tile lies outside the block: stores dropped)
     const int rg = tid / CG, cg = tid % CG;
     const bool act = 4 * rg < dk && 16 * cg < w;
+    const unsigned toff = act ? (unsigned)((4 * rg * dv + c0 + 16 * cg) * 4) : kFar;
+    const unsigned goff = (blk == 0 && tid < dk) ? (unsigned)((dk * dv + tid) * 4) : kFar;  // g*
     float gr[4][16];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -422,30 +562,26 @@ __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
         for (int b = 0; b < 16; ++b) gr[e][b] = 0.0f;
     for (int e = tid; e < dk; e += NTS) gs[e] = 0.0f;
     for (int c = nch - 1; c >= 0; --c) {
-        const int t0 = c * L;
-        float *Gw = base + lay.off_g + (size_t)c * lay.grec;
-        const float *Sw = base + lay.off_s + (size_t)c * 4 * L;
-        const float *Aw = base + lay.off_a + (size_t)c * L * dv;
-        // the carried gradients entering chunk c
-        if (act)
+        // this chunk's tiles and scalars into LDS first: they wait only for
+        // the loads issued a chunk ago, not for the record stores below
+        qf.put(Qs, LK, dk, tid);
+        af.put(As, BVB, w, tid);
+        sq[l] = s_sv;             // sv_i
+        sqb[l] = s_sv * s_beta;   // sv_i beta_i
+        dcv[l] = s_dec;
+        // the carried gradients entering chunk c (each thread reads and
+        // writes only its own entries of gs; the other reads are discarded)
+        const __amdgpu_buffer_rsrc_t gsd = rsrc(base + lay.off_g + (size_t)c * lay.grec, lay.grec * 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-                for (int b = 0; b < 16; b += 4)
-                    *reinterpret_cast<f32x4 *>(&Gw[(size_t)(4 * rg + e) * dv + c0 + 16 * cg + b]) =
-                        f32x4{gr[e][b], gr[e][b + 1], gr[e][b + 2], gr[e][b + 3]};
-        __syncthreads();  // gs of the previous step complete
-        if (blk == 0)
-            for (int e = tid; e < dk; e += NTS) Gw[(size_t)dk * dv + e] = gs[e];
-        load_tile(Qs, LK, qg, dk, t0, T, tid, NTS);
-        for (int e = tid; e < L * w; e += NTS) As[(e / w) * BVB + e % w] = Aw[(e / w) * dv + c0 + e % w];
-        if (tid < L) {
-            sq[tid] = Sw[tid];                    // sv_i
-            sqb[tid] = Sw[tid] * Sw[2 * L + tid];  // sv_i beta_i
-        }
-        if (tid == 0) decs = Sw[3 * L];
-        __syncthreads();
-        const float dec = decs;
+            for (int b = 0; b < 16; b += 4)
+                buf_st4(f32x4{gr[e][b], gr[e][b + 1], gr[e][b + 2], gr[e][b + 3]}, gsd,
+                        toff + (unsigned)((e * dv + b) * 4));
+        buf_st1(gs[tid < dk ? tid : 0], gsd, goff);
+        fetch(max(c - 1, 0));
+        lds_barrier();
+        const float dec = dcv[0];
         if (act) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -471,19 +607,27 @@ __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
                 for (int i = 0; i < L; ++i) acc = fmaf(sqb[i], Qs[i * LK + e], acc);
                 gs[e] = acc;
             }
-        __syncthreads();
+        lds_barrier();  // the tiles are rewritten next chunk
     }
-    // G*, g* after the first chunk: the initial state's gradients
+    // G*, g* after the first chunk: the initial state's gradients, and this
+    // block's part of <dC0, C0>
     float part = 0.0f;
-    if (act)
+    {
+        const size_t pb = (size_t)p * dk * dv, nb = (size_t)dk * dv * 4;
+        const __amdgpu_buffer_rsrc_t c0r = a.C0 ? rsrc(a.C0 + pb, nb) : rsrc(a.ckpt, 0);
+        const __amdgpu_buffer_rsrc_t g0r = a.gC0 ? rsrc(a.gC0 + pb, nb) : rsrc(a.ckpt, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int b = 0; b < 16; ++b) {
-                const size_t x = (size_t)p * dk * dv + (size_t)(4 * rg + e) * dv + c0 + 16 * cg + b;
-                if (a.gC0) a.gC0[x] = gr[e][b];
-                if (a.C0) part = fmaf(gr[e][b], a.C0[x], part);
+            for (int b = 0; b < 16; b += 4) {
+                const unsigned off = toff + (unsigned)((e * dv + b) * 4);
+                const f32x4 g{gr[e][b], gr[e][b + 1], gr[e][b + 2], gr[e][b + 3]};
+                buf_st4(g, g0r, off);
+                const f32x4 cv = buf_ld4(c0r, off);
+#pragma unroll
+                for (int y = 0; y < 4; ++y) part = fmaf(g[y], cv[y], part);
             }
+    }
     if (blk == 0 && a.gn0)
         for (int e = tid; e < dk; e += NTS) a.gn0[(size_t)p * dk + e] = gs[e];
     red[tid] = part;
