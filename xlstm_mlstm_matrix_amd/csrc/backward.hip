@@ -639,21 +639,53 @@ __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
     if (tid == 0) base[lay.off_m + blk] = red[0];
 }
 
-// Pass C: one workgroup per (chunk, pair).  Its contractions with the state
-// are small GEMMs staged through LDS in steps of BK: C' a and G* v (outputs
-// [token][d_qk], contraction over the value columns) share one loop, the
-// state and token tiles stored step-major so that a wavefront reads one
-// contiguous row of the state tile while the token values are broadcast;
-// dv's G*^T k and P^T a (outputs [token][value column]) loop over rows of G*
-// and of a.  Each thread owns 4 x 4 outputs of the first pair and 4 x 8 of
-// dv.  q.dq and k.dk are summed on the fly into per-row partials.
+// v_mfma_f32_16x16x4_f32: D[16][16] += A[16][4] B[4][16], float32 products
+// and sums.  Lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and
+// holds D[4 (l / 16) + v][l % 16] in element v.
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Pass C's dv part: four steps of rows of G* (steps sc .. sc + 3, rows
+// 4s + g, sc = min(s0, ns - 4)) into gr4, and their MFMAs against the K tile
+// (on = 0 makes a group contribute nothing).
+__device__ __forceinline__ void dv_gload(f32x4 (&gr4)[4], __amdgpu_buffer_rsrc_t r, unsigned off,
+                                         unsigned rstep, int s0, int ns) {
+    const int sc = min(s0, ns - 4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) gr4[u] = buf_ld4(r, off + (unsigned)(sc + u) * rstep);
+}
+template <int LK>
+__device__ __forceinline__ void dv_gstep(f32x4 (&x)[2][4], const f32x4 (&gr4)[4], const float *K, int l16, int g,
+                                         int s0, float on) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = 4 * (s0 + u) + g;
+        const float k0 = on * K[l16 * LK + r], k1 = on * K[(16 + l16) * LK + r];
+#pragma unroll
+        for (int xx = 0; xx < 4; ++xx) {
+            x[0][xx] = mfma4(k0, gr4[u][xx], x[0][xx]);
+            x[1][xx] = mfma4(k1, gr4[u][xx], x[1][xx]);
+        }
+    }
+}
+
+// Pass C: one workgroup per (chunk, pair); its contractions run on the
+// matrix cores in float32 (16 x 16 output tiles, one per wavefront at a time).
+//   dq, dk by 16 rows of d_qk: C' a and G* v contract over the value columns,
+//     which each lane reads four at a time straight from the records (the
+//     k index of successive MFMAs is permuted alike in both operands), then
+//     are scaled per token, and the in-chunk P~ K and P~^T Q are added
+//     through the same accumulators;
+//   dv by 16 value columns: G*^T k over the rows of G*, scaled per token,
+//     plus P^T a.
+// q.dq and k.dk are summed per (token, 16 rows) into partials for the gates.
 template <typename IO>
 __global__ __launch_bounds__(NTA) void bwd_c_kernel(BwdArgs a) {
-    constexpr int LK = kBwdMaxDk + 4, BK = 16, SB = kBwdMaxDk * BK, NRGM = kBwdMaxDk / 4;
+    constexpr int LK = kBwdMaxDk + 4, LP = L + 1, NRTM = kBwdMaxDk / 16, NW = NTA / 64;
     __shared__ __attribute__((aligned(16))) float Q[L * LK], K[L * LK];
-    __shared__ __attribute__((aligned(16))) float stage[2 * SB + 2 * L * BK];
-    __shared__ float P[L * L], PT[L * L], sv[L], wv[L], beta[L], gsv[kBwdMaxDk];
-    __shared__ float pq[L * NRGM], pk[L * NRGM];
+    __shared__ float P[L * LP], PT[L * LP], sv[L], wv[L], beta[L];
+    __shared__ float pq[L * NRTM], pk[L * NRTM];
     const int c = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T, t0 = c * L;
     const BwdLayout lay = bwd_layout(T, dk, dv);
@@ -665,167 +697,193 @@ __global__ __launch_bounds__(NTA) void bwd_c_kernel(BwdArgs a) {
     const float *Sw = base + lay.off_s + (size_t)c * 4 * L;
     const float *Gw = base + lay.off_g + (size_t)c * lay.grec;  // G* entering chunk c, then g*
     const size_t oqk = (size_t)p * T * dk, ov = (size_t)p * T * dv, og1 = (size_t)p * T;
-    const IO *vg = static_cast<const IO *>(a.v) + ov;
 
     load_tile(Q, LK, static_cast<const IO *>(a.q) + oqk, dk, t0, T, tid, NTA);
     load_tile(K, LK, static_cast<const IO *>(a.k) + oqk, dk, t0, T, tid, NTA);
     for (int e = tid; e < L * L; e += NTA) {
-        P[e] = Pw[e];
-        PT[e] = Pw[L * L + e];
+        P[(e / L) * LP + e % L] = Pw[e];
+        PT[(e / L) * LP + e % L] = Pw[L * L + e];
     }
-    for (int e = tid; e < dk; e += NTA) gsv[e] = Gw[(size_t)dk * dv + e];
     if (tid < L) {
         sv[tid] = Sw[tid];
         wv[tid] = Sw[L + tid];
         beta[tid] = Sw[2 * L + tid];
     }
+    __syncthreads();
 
-    // ---- dq and dk: thread (ig, rg) owns token rows 4ig .. +3 and rows 4rg .. +3 of d_qk
-    const int NRG = dk / 4;
-    const int ig = tid / NRG, rg = tid % NRG;
-    const bool act1 = ig < L / 4;
-    float aq[4][4], ak[4][4];
+    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    const __amdgpu_buffer_rsrc_t vr = rsrc(static_cast<const IO *>(a.v) + ov, (size_t)T * dv * sizeof(IO));
+    // outputs through descriptors ending at token T: rows past it are dropped
+    const __amdgpu_buffer_rsrc_t oq = rsrc(a.gq + oqk, (size_t)T * dk * 4);
+    const __amdgpu_buffer_rsrc_t ok_ = rsrc(a.gk + oqk, (size_t)T * dk * 4);
+    const __amdgpu_buffer_rsrc_t ovr = rsrc(a.gv + ov, (size_t)T * dv * 4);
+
+    // ---- dq and dk: rows [r0, r0 + 16) of d_qk for all L tokens
+    const int NRT = dk / 16;
+    for (int rt = wave; rt < NRT; rt += NW) {
+        const int r0 = 16 * rt;
+        f32x4 xq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, xk[2] = {xq[0], xq[0]};
+        // lane (l16, g) reads C'[r0 + l16][b0 + 4g .. +3] and G* likewise, and
+        // a_i, v_i of tokens i = l16 and 16 + l16 at the same columns, all
+        // through buffer loads (the compiler keeps those where they are
+        // issued, a block pair ahead of their use; it moved plain loads down
+        // to their uses)
+        const __amdgpu_buffer_rsrc_t cr = rsrc(Cc, (size_t)dk * dv * 4), grs = rsrc(Gw, (size_t)dk * dv * 4);
+        const __amdgpu_buffer_rsrc_t ar = rsrc(Aw, (size_t)L * dv * 4);
+        const unsigned so = (unsigned)(((r0 + l16) * dv + 4 * g) * 4), ao = (unsigned)((l16 * dv + 4 * g) * 4);
+        const unsigned astep = (unsigned)(16 * dv * 4);
+        const unsigned vo = (unsigned)(((t0 + l16) * dv + 4 * g) * (int)sizeof(IO));
+        const unsigned vstep = (unsigned)(16 * dv * (int)sizeof(IO));
+        // (v stays in its I/O type until used: a conversion before the
+        // scheduling barrier below would wait for the load)
+        struct Blk { f32x4 c, g, a0, a1; typename Quad<IO>::raw v0, v1; };
+        auto fetch = [&](int b0) {
+            Blk x;
+            const unsigned fb = (unsigned)(b0 * 4), eb = (unsigned)(b0 * (int)sizeof(IO));
+            x.c = buf_ld4(cr, so + fb);
+            x.g = buf_ld4(grs, so + fb);
+            x.a0 = buf_ld4(ar, ao + fb);
+            x.a1 = buf_ld4(ar, ao + astep + fb);
+            x.v0 = Quad<IO>::load(vr, vo + eb);
+            x.v1 = Quad<IO>::load(vr, vo + vstep + eb);
+            return x;
+        };
+        auto step = [&](const Blk &x, float on) {
+            const f32x4 v0 = Quad<IO>::cvt(x.v0), v1 = Quad<IO>::cvt(x.v1);
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+            for (int s = 0; s < 4; ++s) {
+                xq[0] = mfma4(on * x.a0[s], x.c[s], xq[0]);
+                xq[1] = mfma4(on * x.a1[s], x.c[s], xq[1]);
+                xk[0] = mfma4(on * v0[s], x.g[s], xk[0]);
+                xk[1] = mfma4(on * v1[s], x.g[s], xk[1]);
+            }
+        };
+        // blocks of 16 value columns alternate between two register sets, each
+        // reloaded right after its MFMAs are issued (so the other set's MFMAs
+        // cover its loads, and no loop-carried copy waits for a load); an odd
+        // last block reads a valid block again and is multiplied by zero
+        const int last = dv - 16;
+        Blk xa = fetch(0);
+        __builtin_amdgcn_sched_barrier(0);  // all of set A's loads before set B's
+        Blk xb = fetch(min(16, last));
+        __builtin_amdgcn_sched_barrier(0);
+        for (int b0 = 0; b0 < dv; b0 += 32) {
+            step(xa, 1.0f);
+            xa = fetch(min(b0 + 32, last));
+            __builtin_amdgcn_sched_barrier(0);
+            step(xb, b0 + 16 < dv ? 1.0f : 0.0f);
+            xb = fetch(min(b0 + 48, last));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // scale per token: dq_i = sv_i (C' a_i + n' beta_i), dk_i = w_i (G* v_i + g*)
+        const float nr = ncg[r0 + l16], gr_ = Gw[(size_t)dk * dv + r0 + l16];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) aq[x][e] = ak[x][e] = 0.0f;
-    float *Ct = stage, *Gt = stage + SB, *At = stage + 2 * SB, *Vt = At + L * BK;
-    for (int b0 = 0; b0 < dv; b0 += BK) {
-        __syncthreads();  // (first pass: the tiles above; then: the previous step's reads)
-        // Ct[k][r] = C'[r][b0 + k], Gt likewise: each row of the state gives BK
-        // consecutive floats, stored transposed
-        for (int e = tid; e < dk * (BK / 4); e += NTA) {
-            const int r = e / (BK / 4), k4 = e % (BK / 4);
-            const f32x4 cv = ld4(&Cc[(size_t)r * dv + b0 + 4 * k4]);
-            const f32x4 gv = ld4(&Gw[(size_t)r * dv + b0 + 4 * k4]);
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                Ct[(4 * k4 + x) * dk + r] = cv[x];
-                Gt[(4 * k4 + x) * dk + r] = gv[x];
+            for (int v = 0; v < 4; ++v) {
+                const int i = 16 * tt + 4 * g + v;
+                xq[tt][v] = sv[i] * fmaf(nr, beta[i], xq[tt][v]);
+                xk[tt][v] = wv[i] * (xk[tt][v] + gr_);
+            }
+        // + sum_j P~_ij k_j and + sum_i2 P~_i2,i q_i2 (zero outside j <= i)
+#pragma unroll
+        for (int s = 0; s < L / 4; ++s) {
+            const int j = 4 * s + g;
+            const float kb = K[j * LK + r0 + l16], qb = Q[j * LK + r0 + l16];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                xq[tt] = mfma4(PT[(16 * tt + l16) * LP + j], kb, xq[tt]);
+                xk[tt] = mfma4(PT[j * LP + 16 * tt + l16], qb, xk[tt]);
             }
         }
-        // At[k][i] = a_i[b0 + k], Vt[k][j] = v_j[b0 + k] (zero past T)
-        for (int e = tid; e < L * BK; e += NTA) {
-            const int i = e / BK, k = e % BK, t = t0 + i;
-            At[k * L + i] = Aw[i * dv + b0 + k];
-            Vt[k * L + i] = t < T ? to_f(vg[(size_t)t * dv + b0 + k]) : 0.0f;
-        }
-        __syncthreads();
-        if (act1) {
-#pragma unroll 4
-            for (int k = 0; k < BK; ++k) {
-                const f32x4 c4 = ld4(&Ct[k * dk + 4 * rg]);
-                const f32x4 g4 = ld4(&Gt[k * dk + 4 * rg]);
-                const f32x4 a4 = ld4(&At[k * L + 4 * ig]);
-                const f32x4 v4 = ld4(&Vt[k * L + 4 * ig]);
+        // outputs, and q.dq, k.dk over these 16 rows per token
 #pragma unroll
-                for (int x = 0; x < 4; ++x)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        aq[x][e] = fmaf(a4[x], c4[e], aq[x][e]);
-                        ak[x][e] = fmaf(v4[x], g4[e], ak[x][e]);
-                    }
-            }
-        }
-    }
-    if (act1) {
+            for (int v = 0; v < 4; ++v) {
+                const int i = 16 * tt + 4 * g + v, r = r0 + l16;
+                const unsigned off = (unsigned)(((t0 + i) * dk + r) * 4);
+                buf_st1(xq[tt][v], oq, off);
+                buf_st1(xk[tt][v], ok_, off);
+                float sq = Q[i * LK + r] * xq[tt][v], sk = K[i * LK + r] * xk[tt][v];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int i = 4 * ig + x, t = t0 + i;
-            float sq = 0.0f, sk = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * rg + e;
-                float q_ = sv[i] * fmaf(ncg[r], beta[i], aq[x][e]);
-                for (int j = 0; j <= i; ++j) q_ = fmaf(PT[i * L + j], K[j * LK + r], q_);
-                float k_ = 0.0f;
-                for (int i2 = i; i2 < L; ++i2) k_ = fmaf(PT[i2 * L + i], Q[i2 * LK + r], k_);
-                k_ = fmaf(wv[i], ak[x][e] + gsv[r], k_);
-                if (t < T) {
-                    a.gq[oqk + (size_t)t * dk + r] = q_;
-                    a.gk[oqk + (size_t)t * dk + r] = k_;
+                for (int o = 1; o < 16; o <<= 1) {
+                    sq += __shfl_xor(sq, o, 64);
+                    sk += __shfl_xor(sk, o, 64);
                 }
-                sq = fmaf(Q[i * LK + r], q_, sq);
-                sk = fmaf(K[i * LK + r], k_, sk);
+                if (l16 == 0) {
+                    pq[i * NRTM + rt] = sq;
+                    pk[i * NRTM + rt] = sk;
+                }
             }
-            pq[i * NRGM + rg] = sq;
-            pk[i * NRGM + rg] = sk;
-        }
     }
 
-    // ---- dv: thread (jg, bg) owns token rows 4jg .. +3 and value columns 8bg .. +7
-    const int NBG = dv / 8;
-    const int jg = tid / NBG, bg = tid % NBG;
-    const bool act2 = jg < L / 4;
-    float acc[4][8];
+    // ---- dv: value columns [b0, b0 + 64) for all L tokens.  Lane (l16, g)
+    // reads four consecutive columns b0 + 4 l16 .. +3 of a row of G* (or of
+    // a), one for each of four MFMA tiles: tile x takes column b0 + 4n + x as
+    // its column n, so each lane's outputs of a token are again four
+    // consecutive columns.  Lanes past d_v load zeros and store nothing.  The
+    // wavefronts take these units in reverse order, so that those without
+    // d_qk rows start first.
+    const int NBU = (dv + 63) / 64, NS = dk / 4;  // NS: steps of 4 rows of G*, a multiple of 4
+    for (int bu = NW - 1 - wave; bu < NBU; bu += NW) {
+        const int b0 = 64 * bu;
+        const __amdgpu_buffer_rsrc_t gsr = rsrc(Gw, (size_t)dk * dv * 4), asr = rsrc(Aw, (size_t)L * dv * 4);
+        const bool colok = b0 + 4 * l16 < dv;
+        const unsigned go = colok ? (unsigned)((g * dv + b0 + 4 * l16) * 4) : kFar;
+        const unsigned rstep = (unsigned)(4 * dv * 4);  // four rows
+        f32x4 x[2][4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int y = 0; y < 8; ++y) acc[x][y] = 0.0f;
-    float *Rt = stage;  // [BK][dv] rows of G*, then of a
-    // w_j sum_r k_j[r] G*[r][b]
-    for (int r0 = 0; r0 < dk; r0 += BK) {
-        __syncthreads();
-        for (int e = tid; e < BK * dv / 4; e += NTA) {
-            const int k = (4 * e) / dv, b = (4 * e) % dv;
-            *reinterpret_cast<f32x4 *>(&Rt[k * dv + b]) = ld4(&Gw[(size_t)(r0 + k) * dv + b]);
+            for (int xx = 0; xx < 4; ++xx) x[tt][xx] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // w_j sum_r k_j[r] G*[r][b] over steps s (rows 4s + g), in groups of
+        // four steps alternating between two register sets, each reloaded
+        // right after use; a group past the last one reloads a valid group
+        // and its K operand is zero
+        f32x4 ga[4], gb[4];
+        dv_gload(ga, gsr, go, rstep, 0, NS);
+        __builtin_amdgcn_sched_barrier(0);
+        dv_gload(gb, gsr, go, rstep, 4, NS);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int s0 = 0; s0 < NS; s0 += 8) {
+            dv_gstep<LK>(x, ga, K, l16, g, s0, 1.0f);
+            dv_gload(ga, gsr, go, rstep, s0 + 8, NS);
+            __builtin_amdgcn_sched_barrier(0);
+            dv_gstep<LK>(x, gb, K, l16, g, min(s0 + 4, NS - 4), s0 + 4 < NS ? 1.0f : 0.0f);
+            dv_gload(gb, gsr, go, rstep, s0 + 12, NS);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();
-        if (act2) {
-#pragma unroll 4
-            for (int k = 0; k < BK; ++k) {
-                const f32x4 g0 = ld4(&Rt[k * dv + 8 * bg]), g1 = ld4(&Rt[k * dv + 8 * bg + 4]);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const float kv = K[(4 * jg + x) * LK + r0 + k];
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                    for (int y = 0; y < 4; ++y) {
-                        acc[x][y] = fmaf(kv, g0[y], acc[x][y]);
-                        acc[x][4 + y] = fmaf(kv, g1[y], acc[x][4 + y]);
-                    }
-                }
+            for (int v = 0; v < 4; ++v) {
+                const float wj = wv[16 * tt + 4 * g + v];
+#pragma unroll
+                for (int xx = 0; xx < 4; ++xx) x[tt][xx][v] *= wj;
+            }
+        // + sum_{i >= j} P_ij a_i[b]  (steps over tokens i = 4s + g)
+        const unsigned ao2 = colok ? (unsigned)((g * dv + b0 + 4 * l16) * 4) : kFar;
+#pragma unroll
+        for (int s = 0; s < L / 4; ++s) {
+            const f32x4 av = buf_ld4(asr, ao2 + (unsigned)s * rstep);
+            const int i = 4 * s + g;
+            const float p0 = P[i * LP + l16], p1 = P[i * LP + 16 + l16];
+#pragma unroll
+            for (int xx = 0; xx < 4; ++xx) {
+                x[0][xx] = mfma4(p0, av[xx], x[0][xx]);
+                x[1][xx] = mfma4(p1, av[xx], x[1][xx]);
             }
         }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = t0 + 16 * tt + 4 * g + v;
+                buf_st4(f32x4{x[tt][0][v], x[tt][1][v], x[tt][2][v], x[tt][3][v]}, ovr,
+                        colok ? (unsigned)((t * dv + b0 + 4 * l16) * 4) : kFar);
+            }
     }
-    if (act2)
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int y = 0; y < 8; ++y) acc[x][y] *= wv[4 * jg + x];
-    // + sum_{i >= j} P_ij a_i[b]
-    for (int i0 = 0; i0 < L; i0 += BK) {
-        __syncthreads();
-        for (int e = tid; e < BK * dv / 4; e += NTA) {
-            const int k = (4 * e) / dv, b = (4 * e) % dv;
-            *reinterpret_cast<f32x4 *>(&Rt[k * dv + b]) = ld4(&Aw[(size_t)(i0 + k) * dv + b]);
-        }
-        __syncthreads();
-        if (act2) {
-#pragma unroll 4
-            for (int k = 0; k < BK; ++k) {
-                const f32x4 a0 = ld4(&Rt[k * dv + 8 * bg]), a1 = ld4(&Rt[k * dv + 8 * bg + 4]);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const float pv = P[(i0 + k) * L + 4 * jg + x];  // zero unless i >= j
-#pragma unroll
-                    for (int y = 0; y < 4; ++y) {
-                        acc[x][y] = fmaf(pv, a0[y], acc[x][y]);
-                        acc[x][4 + y] = fmaf(pv, a1[y], acc[x][4 + y]);
-                    }
-                }
-            }
-        }
-    }
-    if (act2)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int t = t0 + 4 * jg + x;
-            if (t < T) {
-                float *o = a.gv + ov + (size_t)t * dv + 8 * bg;
-                *reinterpret_cast<f32x4 *>(o) = f32x4{acc[x][0], acc[x][1], acc[x][2], acc[x][3]};
-                *reinterpret_cast<f32x4 *>(o + 4) = f32x4{acc[x][4], acc[x][5], acc[x][6], acc[x][7]};
-            }
-        }
     __syncthreads();  // the row partials of q.dq and k.dk complete
     // gate gradients: di = k.dk; the in-chunk part of df (reverse cumsum of
     // q.dq - k.dk) and the chunk's total, for the carry of pass D
@@ -835,9 +893,9 @@ __global__ __launch_bounds__(NTA) void bwd_c_kernel(BwdArgs a) {
         float di = 0.0f, x = 0.0f;
         if (ok) {
             float sq = 0.0f;
-            for (int r = 0; r < NRG; ++r) {
-                di += pk[j * NRGM + r];
-                sq += pq[j * NRGM + r];
+            for (int r = 0; r < NRT; ++r) {
+                di += pk[j * NRTM + r];
+                sq += pq[j * NRTM + r];
             }
             x = sq - di;
         }
