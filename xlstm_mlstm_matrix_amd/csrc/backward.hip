@@ -209,6 +209,13 @@ __device__ __forceinline__ void buf_st1(float x, __amdgpu_buffer_rsrc_t r, unsig
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, (int)off, 0, 0);
 }
 
+// v_mfma_f32_16x16x4_f32: D[16][16] += A[16][4] B[4][16], float32 products
+// and sums.  Lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and
+// holds D[4 (l / 16) + v][l % 16] in element v.
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // Checkpoint pass: one workgroup per (block of BVB value columns, pair).  The
 // state recurrence is separable by value column, so each workgroup carries
 // its [d_qk][BVB] block of C' in registers (a 4 x 16 tile per thread) and
@@ -246,26 +253,45 @@ __global__ __launch_bounds__(NTS) void bwd_ckpt_kernel(BwdArgs a) {
         ff = fgp[t];
     };
     fetch(0);
-    // this thread's tile: rows 4*rg .. +3, block columns 16*cg .. +15; toff
-    // is its byte offset in a [d_qk][d_v] record, past every record when the
-    // tile lies outside the block (its stores are dropped)
-    const int rg = tid / CG, cg = tid % CG;
-    const bool act = 4 * rg < dk && 16 * cg < w;
-    const unsigned toff = act ? (unsigned)((4 * rg * dv + c0 + 16 * cg) * 4) : kFar;
+    // The block of C' is held as MFMA accumulators: wavefront w owns row
+    // tiles w and w + 8 (16 rows each) and two quads of 64 columns; in a
+    // quad, lane (l16, g) holds the four consecutive columns 4 l16 .. +3, one
+    // in each of four MFMA tiles (tile x takes quad column 4n + x as its
+    // column n), so that a lane's values of a row are one 16-byte group.
+    // sacc[a][q][x][v] = C'[16 (w + 8a) + 4g + v][c0 + 64q + 4 l16 + x].
+    // soff[a][q] is the byte offset of its row 4g in a [d_qk][d_v] record,
+    // past every record when the tile lies outside the block.
+    const int wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
+    f32x4 sacc[2][2][4];
+    unsigned soff[2][2];
+    bool arow[2], aq[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        arow[x] = 16 * (wave + 8 * x) < dk;
+        aq[x] = 64 * x < w;
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            soff[x][q] = (arow[x] && 64 * q + 4 * l16 < w)
+                             ? (unsigned)(((16 * (wave + 8 * x) + 4 * g) * dv + c0 + 64 * q + 4 * l16) * 4)
+                             : kFar;
     // n' (block 0, threads below d_qk) and m (thread d_qk) follow C' in the record
     const unsigned noff = (blk == 0 && tid <= dk) ? (unsigned)((dk * dv + tid) * 4) : kFar;
-    float cr[4][16];
     {
         const __amdgpu_buffer_rsrc_t c0r =
             a.C0 ? rsrc(a.C0 + (size_t)p * dk * dv, (size_t)dk * dv * 4) : rsrc(a.ckpt, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int b = 0; b < 16; b += 4) {
-                const f32x4 x = buf_ld4(c0r, toff + (unsigned)((e * dv + b) * 4));
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int y = 0; y < 4; ++y) cr[e][b + y] = x[y];
-            }
+                for (int v = 0; v < 4; ++v) {
+                    const f32x4 y = buf_ld4(c0r, soff[x][q] + (unsigned)(v * dv * 4));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sacc[x][q][e][v] = y[e];
+                }
     }
     if (blk == 0)
         for (int e = tid; e < dk; e += NTS) ns[e] = a.n0 ? a.n0[(size_t)p * dk + e] : 0.0f;
@@ -288,33 +314,42 @@ __global__ __launch_bounds__(NTS) void bwd_ckpt_kernel(BwdArgs a) {
         // its own entries of ns; the other reads are discarded)
         const __amdgpu_buffer_rsrc_t rs = rsrc(base + (size_t)c * rec, rec * 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int b = 0; b < 16; b += 4)
-                buf_st4(f32x4{cr[e][b], cr[e][b + 1], cr[e][b + 2], cr[e][b + 3]}, rs,
-                        toff + (unsigned)((e * dv + b) * 4));
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    buf_st4(f32x4{sacc[x][q][0][v], sacc[x][q][1][v], sacc[x][q][2][v], sacc[x][q][3][v]}, rs,
+                            soff[x][q] + (unsigned)(v * dv * 4));
         buf_st1(tid < dk ? ns[tid < dk ? tid : 0] : m, rs, noff);
         if (c + 1 == nch) break;  // the state after the last chunk is not needed
         fetch(t0 + L);
         lds_barrier();
         const float b_last = last[0], r_last = last[1];
         const float dec = exp_e(m - r_last);
-        if (act) {
+        // C' <- dec C' + sum_j (w_j k_j) v_j^T on the matrix cores (k index = token)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int b = 0; b < 16; ++b) cr[e][b] *= dec;
-            for (int j = 0; j < L; ++j) {
-                float kw[4];
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) kw[e] = wv[j] * Ks[j * LK + 4 * rg + e];
+                for (int e = 0; e < 4; ++e) sacc[x][q][e] *= dec;
 #pragma unroll
-                for (int b = 0; b < 16; b += 4) {
-                    const f32x4 vv = ld4(&Vs[j * BVB + 16 * cg + b]);
+        for (int s4 = 0; s4 < L / 4; ++s4) {
+            const int j = 4 * s4 + g;
+            const float wj = wv[j];
+            f32x4 vb[2];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
+            for (int q = 0; q < 2; ++q) vb[q] = ld4(&Vs[j * BVB + 64 * q + 4 * l16]);
 #pragma unroll
-                        for (int x = 0; x < 4; ++x) cr[e][b + x] = fmaf(kw[e], vv[x], cr[e][b + x]);
+            for (int x = 0; x < 2; ++x) {
+                if (!arow[x]) continue;  // uniform in the wavefront
+                const float ka = wj * Ks[j * LK + 16 * (wave + 8 * x) + l16];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    if (!aq[q]) continue;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sacc[x][q][e] = mfma4(ka, vb[q][e], sacc[x][q][e]);
                 }
             }
         }
@@ -549,17 +584,28 @@ __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
         s_dec = Sw[3 * L + l];
     };
     fetch(nch - 1);
-    // this thread's tile and its byte offset in a [d_qk][d_v] record (past
-    // every record when the tile lies outside the block: stores dropped)
-    const int rg = tid / CG, cg = tid % CG;
-    const bool act = 4 * rg < dk && 16 * cg < w;
-    const unsigned toff = act ? (unsigned)((4 * rg * dv + c0 + 16 * cg) * 4) : kFar;
+    // G*'s block as MFMA accumulators, laid out as C' in the checkpoint pass:
+    // gacc[a][q][x][v] = G*[16 (w + 8a) + 4g + v][c0 + 64q + 4 l16 + x]
+    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    f32x4 gacc[2][2][4];
+    unsigned soff[2][2];
+    bool arow[2], aq[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        arow[x] = 16 * (wave + 8 * x) < dk;
+        aq[x] = 64 * x < w;
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            soff[x][q] = (arow[x] && 64 * q + 4 * l16 < w)
+                             ? (unsigned)(((16 * (wave + 8 * x) + 4 * g) * dv + c0 + 64 * q + 4 * l16) * 4)
+                             : kFar;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gacc[x][q][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     const unsigned goff = (blk == 0 && tid < dk) ? (unsigned)((dk * dv + tid) * 4) : kFar;  // g*
-    float gr[4][16];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int b = 0; b < 16; ++b) gr[e][b] = 0.0f;
     for (int e = tid; e < dk; e += NTS) gs[e] = 0.0f;
     for (int c = nch - 1; c >= 0; --c) {
         // this chunk's tiles and scalars into LDS first: they wait only for
@@ -573,31 +619,40 @@ __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
         // writes only its own entries of gs; the other reads are discarded)
         const __amdgpu_buffer_rsrc_t gsd = rsrc(base + lay.off_g + (size_t)c * lay.grec, lay.grec * 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int b = 0; b < 16; b += 4)
-                buf_st4(f32x4{gr[e][b], gr[e][b + 1], gr[e][b + 2], gr[e][b + 3]}, gsd,
-                        toff + (unsigned)((e * dv + b) * 4));
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    buf_st4(f32x4{gacc[x][q][0][v], gacc[x][q][1][v], gacc[x][q][2][v], gacc[x][q][3][v]}, gsd,
+                            soff[x][q] + (unsigned)(v * dv * 4));
         buf_st1(gs[tid < dk ? tid : 0], gsd, goff);
         fetch(max(c - 1, 0));
         lds_barrier();
         const float dec = dcv[0];
-        if (act) {
+        // G* <- dec G* + sum_i (sv_i q_i) a_i^T on the matrix cores (k index = token)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int b = 0; b < 16; ++b) gr[e][b] *= dec;
-            for (int i = 0; i < L; ++i) {
-                float qa[4];
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) qa[e] = sq[i] * Qs[i * LK + 4 * rg + e];
+                for (int e = 0; e < 4; ++e) gacc[x][q][e] *= dec;
 #pragma unroll
-                for (int b = 0; b < 16; b += 4) {
-                    const f32x4 av = ld4(&As[i * BVB + 16 * cg + b]);
+        for (int s4 = 0; s4 < L / 4; ++s4) {
+            const int i = 4 * s4 + g;
+            const float si = sq[i];
+            f32x4 ab[2];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
+            for (int q = 0; q < 2; ++q) ab[q] = ld4(&As[i * BVB + 64 * q + 4 * l16]);
 #pragma unroll
-                        for (int x = 0; x < 4; ++x) gr[e][b + x] = fmaf(qa[e], av[x], gr[e][b + x]);
+            for (int x = 0; x < 2; ++x) {
+                if (!arow[x]) continue;  // uniform in the wavefront
+                const float qa = si * Qs[i * LK + 16 * (wave + 8 * x) + l16];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    if (!aq[q]) continue;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) gacc[x][q][e] = mfma4(qa, ab[q][e], gacc[x][q][e]);
                 }
             }
         }
@@ -617,16 +672,18 @@ __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
         const __amdgpu_buffer_rsrc_t c0r = a.C0 ? rsrc(a.C0 + pb, nb) : rsrc(a.ckpt, 0);
         const __amdgpu_buffer_rsrc_t g0r = a.gC0 ? rsrc(a.gC0 + pb, nb) : rsrc(a.ckpt, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int b = 0; b < 16; b += 4) {
-                const unsigned off = toff + (unsigned)((e * dv + b) * 4);
-                const f32x4 g{gr[e][b], gr[e][b + 1], gr[e][b + 2], gr[e][b + 3]};
-                buf_st4(g, g0r, off);
-                const f32x4 cv = buf_ld4(c0r, off);
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int y = 0; y < 4; ++y) part = fmaf(g[y], cv[y], part);
-            }
+                for (int v = 0; v < 4; ++v) {
+                    const unsigned off = soff[x][q] + (unsigned)(v * dv * 4);
+                    const f32x4 gv{gacc[x][q][0][v], gacc[x][q][1][v], gacc[x][q][2][v], gacc[x][q][3][v]};
+                    buf_st4(gv, g0r, off);
+                    const f32x4 cv = buf_ld4(c0r, off);
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) part = fmaf(gv[y], cv[y], part);
+                }
     }
     if (blk == 0 && a.gn0)
         for (int e = tid; e < dk; e += NTS) a.gn0[(size_t)p * dk + e] = gs[e];
@@ -637,13 +694,6 @@ __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
         __syncthreads();
     }
     if (tid == 0) base[lay.off_m + blk] = red[0];
-}
-
-// v_mfma_f32_16x16x4_f32: D[16][16] += A[16][4] B[4][16], float32 products
-// and sums.  Lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and
-// holds D[4 (l / 16) + v][l % 16] in element v.
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 // Pass C's dv part: four steps of rows of G* (steps sc .. sc + 3, rows
