@@ -216,6 +216,31 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Products [L tokens] x [rows of a record] x [64 value columns] (passes A and
+// C): four steps of record rows (steps sc .. sc + 3, rows 4s + g, sc =
+// min(s0, ns - 4)) into gr4, and their MFMAs against a token tile in LDS
+// (on = 0 makes a group contribute nothing).
+__device__ __forceinline__ void dv_gload(f32x4 (&gr4)[4], __amdgpu_buffer_rsrc_t r, unsigned off,
+                                         unsigned rstep, int s0, int ns) {
+    const int sc = min(s0, ns - 4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) gr4[u] = buf_ld4(r, off + (unsigned)(sc + u) * rstep);
+}
+template <int LK>
+__device__ __forceinline__ void dv_gstep(f32x4 (&x)[2][4], const f32x4 (&gr4)[4], const float *K, int l16, int g,
+                                         int s0, float on) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = 4 * (s0 + u) + g;
+        const float k0 = on * K[l16 * LK + r], k1 = on * K[(16 + l16) * LK + r];
+#pragma unroll
+        for (int xx = 0; xx < 4; ++xx) {
+            x[0][xx] = mfma4(k0, gr4[u][xx], x[0][xx]);
+            x[1][xx] = mfma4(k1, gr4[u][xx], x[1][xx]);
+        }
+    }
+}
+
 // Checkpoint pass: one workgroup per (block of BVB value columns, pair).  The
 // state recurrence is separable by value column, so each workgroup carries
 // its [d_qk][BVB] block of C' in registers (a 4 x 16 tile per thread) and
@@ -364,16 +389,18 @@ __global__ __launch_bounds__(NTS) void bwd_ckpt_kernel(BwdArgs a) {
     }
 }
 
-// Pass A: one workgroup per (chunk, pair).  The read-out's contractions (Q C'
-// and the causal P V, outputs [token][value column]) run as GEMMs staged
-// through LDS in steps of BK rows, each thread owning 4 x 8 outputs; a and do~
-// follow in registers, and P~'s a.v products are a staged [L][L] product over
-// the value columns.
+// Pass A: one workgroup per (chunk, pair).  P (the decayed causal q.k) and
+// the denominators in float32 on the vector units; then on the matrix cores:
+// the read-out num = sv (Q C') + P V by units of 64 value columns (C' rows
+// read as 16-byte groups of four columns, one per MFMA tile, as in pass C's
+// dv part), a and do~ from it in registers, and the a.v products of P~ as
+// 2 x 2 tiles of [L][L], split over 16-column blocks across the wavefronts
+// and summed through LDS.
 template <typename IO>
 __global__ __launch_bounds__(NTA) void bwd_a_kernel(BwdArgs a) {
-    constexpr int LK = kBwdMaxDk + 4, BK = 16, NBGM = kBwdMaxDv / 8;
-    __shared__ __attribute__((aligned(16))) float Q[L * LK], K[L * LK], stage[BK * kBwdMaxDv];
-    __shared__ float P[L * L], part[L * NBGM];
+    constexpr int LK = kBwdMaxDk + 4, LP = L + 1, NW = NTA / 64, NUM = kBwdMaxDv / 64;
+    __shared__ __attribute__((aligned(16))) float Q[L * LK], K[L * LK];  // K's space later holds partial sums
+    __shared__ float P[L * LP], part[L * NUM];
     __shared__ float gb[L], gu[L], gr[L], sv[L], fl[L], dd[L], den[L], beta[L], last[2];
     const int c = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T, t0 = c * L;
@@ -386,9 +413,10 @@ __global__ __launch_bounds__(NTA) void bwd_a_kernel(BwdArgs a) {
     float *Pw = base + lay.off_p + (size_t)c * 2 * L * L;
     float *Sw = base + lay.off_s + (size_t)c * 4 * L;
     const size_t oqk = (size_t)p * T * dk, ov = (size_t)p * T * dv, og1 = (size_t)p * T;
-    const IO *vg = static_cast<const IO *>(a.v) + ov;
-    const IO *ogp = static_cast<const IO *>(a.o) + ov;
-    const IO *dhg = static_cast<const IO *>(a.dh) + ov;
+    const size_t ioN = (size_t)T * dv * sizeof(IO);
+    const __amdgpu_buffer_rsrc_t vr = rsrc(static_cast<const IO *>(a.v) + ov, ioN);
+    const __amdgpu_buffer_rsrc_t orr = rsrc(static_cast<const IO *>(a.o) + ov, ioN);
+    const __amdgpu_buffer_rsrc_t dhr = rsrc(static_cast<const IO *>(a.dh) + ov, ioN);
 
     load_tile(Q, LK, static_cast<const IO *>(a.q) + oqk, dk, t0, T, tid, NTA);
     load_tile(K, LK, static_cast<const IO *>(a.k) + oqk, dk, t0, T, tid, NTA);
@@ -403,7 +431,7 @@ __global__ __launch_bounds__(NTA) void bwd_a_kernel(BwdArgs a) {
         const int i = e / L, j = e % L;
         float s = 0.0f;
         if (j <= i && t0 + i < T) s = dot(&Q[i * LK], &K[j * LK], dk) * exp_e(gu[j] - gr[i]);
-        P[e] = s;
+        P[i * LP + j] = s;
     }
     __syncthreads();
     if (tid < L) {
@@ -411,143 +439,157 @@ __global__ __launch_bounds__(NTA) void bwd_a_kernel(BwdArgs a) {
         float acc = 0.0f;
         for (int r = 0; r < dk; ++r) acc = fmaf(ncg[r], Q[i * LK + r], acc);
         acc *= sv[i];
-        for (int j = 0; j <= i; ++j) acc += P[i * L + j];
+        for (int j = 0; j <= i; ++j) acc += P[i * LP + j];
         dd[i] = acc;
         den[i] = fmaxf(fabsf(acc), fl[i]);
     }
+    __syncthreads();
 
-    // ---- the read-out num: thread (ig, bg) owns token rows 4ig .. +3 and value columns 8bg .. +7
-    const int NBG = dv / 8;
-    const int ig = tid / NBG, bg = tid % NBG;
-    const bool act = ig < L / 4;
-    float acc[4][8];
+    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    // ---- num, a, do~: value columns [b0, b0 + 64); x[tt][xx][v] holds token
+    // 16 tt + 4g + v, column b0 + 4 l16 + xx
+    const int NU = (dv + 63) / 64, NS = dk / 4;
+    for (int bu = wave; bu < NU; bu += NW) {
+        const int b0 = 64 * bu;
+        const bool colok = b0 + 4 * l16 < dv;
+        const __amdgpu_buffer_rsrc_t cr = rsrc(Cc, (size_t)dk * dv * 4);
+        const __amdgpu_buffer_rsrc_t aw = rsrc(Aw, (size_t)L * dv * 4);
+        const __amdgpu_buffer_rsrc_t gor = rsrc(a.go + ov, (size_t)T * dv * 4);
+        const unsigned co = colok ? (unsigned)((g * dv + b0 + 4 * l16) * 4) : kFar;
+        const unsigned rstep = (unsigned)(4 * dv * 4);
+        f32x4 x[2][4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int y = 0; y < 8; ++y) acc[x][y] = 0.0f;
-    // sum_r q_i[r] C'[r][b]
-    for (int r0 = 0; r0 < dk; r0 += BK) {
-        __syncthreads();
-        for (int e = tid; e < BK * dv / 4; e += NTA) {
-            const int k = (4 * e) / dv, b = (4 * e) % dv;
-            *reinterpret_cast<f32x4 *>(&stage[k * dv + b]) = ld4(&Cc[(size_t)(r0 + k) * dv + b]);
+            for (int xx = 0; xx < 4; ++xx) x[tt][xx] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // sum_r q_i[r] C'[r][b]
+        f32x4 ga[4], gb4[4];
+        dv_gload(ga, cr, co, rstep, 0, NS);
+        __builtin_amdgcn_sched_barrier(0);
+        dv_gload(gb4, cr, co, rstep, 4, NS);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int s0 = 0; s0 < NS; s0 += 8) {
+            dv_gstep<LK>(x, ga, Q, l16, g, s0, 1.0f);
+            dv_gload(ga, cr, co, rstep, s0 + 8, NS);
+            __builtin_amdgcn_sched_barrier(0);
+            dv_gstep<LK>(x, gb4, Q, l16, g, min(s0 + 4, NS - 4), s0 + 4 < NS ? 1.0f : 0.0f);
+            dv_gload(gb4, cr, co, rstep, s0 + 12, NS);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();
-        if (act) {
-#pragma unroll 4
-            for (int k = 0; k < BK; ++k) {
-                const f32x4 c0v = ld4(&stage[k * dv + 8 * bg]), c1v = ld4(&stage[k * dv + 8 * bg + 4]);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const float qv = Q[(4 * ig + x) * LK + r0 + k];
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                    for (int y = 0; y < 4; ++y) {
-                        acc[x][y] = fmaf(qv, c0v[y], acc[x][y]);
-                        acc[x][4 + y] = fmaf(qv, c1v[y], acc[x][4 + y]);
-                    }
-                }
+            for (int v = 0; v < 4; ++v) {
+                const float si = sv[16 * tt + 4 * g + v];
+#pragma unroll
+                for (int xx = 0; xx < 4; ++xx) x[tt][xx][v] *= si;
+            }
+        // + sum_{j <= i} P_ij v_j[b] (P zero above the diagonal; v zero past T)
+#pragma unroll
+        for (int s = 0; s < L / 4; ++s) {
+            const int j = 4 * s + g;
+            const f32x4 vb = Quad<IO>::cvt(
+                Quad<IO>::load(vr, colok ? (unsigned)(((t0 + j) * dv + b0 + 4 * l16) * (int)sizeof(IO)) : kFar));
+            const float p0 = P[l16 * LP + j], p1 = P[(16 + l16) * LP + j];
+#pragma unroll
+            for (int xx = 0; xx < 4; ++xx) {
+                x[0][xx] = mfma4(p0, vb[xx], x[0][xx]);
+                x[1][xx] = mfma4(p1, vb[xx], x[1][xx]);
             }
         }
-    }
-    if (act)
+        // a = dh sigmoid(o~) / den (to the workspace; zero past T, where dh
+        // reads as zero), do~ (rows past T dropped), and a.num over these
+        // columns per token
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int y = 0; y < 8; ++y) acc[x][y] *= sv[4 * ig + x];
-    // + sum_{j <= i} P_ij v_j[b]
-    for (int j0 = 0; j0 < L; j0 += BK) {
-        __syncthreads();
-        for (int e = tid; e < BK * dv / 4; e += NTA) {
-            const int k = (4 * e) / dv, b = (4 * e) % dv, t = t0 + j0 + k;
-            *reinterpret_cast<f32x4 *>(&stage[k * dv + b]) =
-                t < T ? ld4_io(vg + (size_t)t * dv + b) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        __syncthreads();
-        if (act) {
-#pragma unroll 4
-            for (int k = 0; k < BK; ++k) {
-                const f32x4 v0 = ld4(&stage[k * dv + 8 * bg]), v1 = ld4(&stage[k * dv + 8 * bg + 4]);
+            for (int v = 0; v < 4; ++v) {
+                const int i = 16 * tt + 4 * g + v, t = t0 + i;
+                const unsigned eo = colok ? (unsigned)((t * dv + b0 + 4 * l16) * (int)sizeof(IO)) : kFar;
+                const f32x4 dh = Quad<IO>::cvt(Quad<IO>::load(dhr, eo));
+                const f32x4 og = Quad<IO>::cvt(Quad<IO>::load(orr, eo));
+                const float rd = 1.0f / den[i];
+                f32x4 av, go;
+                float an = 0.0f;
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const float pv = P[(4 * ig + x) * L + j0 + k];  // zero unless j <= i
-#pragma unroll
-                    for (int y = 0; y < 4; ++y) {
-                        acc[x][y] = fmaf(pv, v0[y], acc[x][y]);
-                        acc[x][4 + y] = fmaf(pv, v1[y], acc[x][4 + y]);
-                    }
+                for (int xx = 0; xx < 4; ++xx) {
+                    const float sg = sigmoid(og[xx]), num = x[tt][xx][v];
+                    av[xx] = dh[xx] * sg * rd;
+                    go[xx] = dh[xx] * num * rd * sg * (1.0f - sg);
+                    an = fmaf(av[xx], num, an);
                 }
+                buf_st4(go, gor, colok ? (unsigned)((t * dv + b0 + 4 * l16) * 4) : kFar);
+                buf_st4(av, aw, colok ? (unsigned)((i * dv + b0 + 4 * l16) * 4) : kFar);
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) an += __shfl_xor(an, o, 64);
+                if (l16 == 0) part[i * NUM + bu] = an;
             }
-        }
-    }
-    // a = dh sigmoid(o~) / den and do~ in registers; a to the workspace; row
-    // partials of a.num for beta
-    if (act) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int i = 4 * ig + x, t = t0 + i;
-            float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, go[8];
-            if (t < T) {
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const f32x4 dh = ld4_io(dhg + (size_t)t * dv + 8 * bg + 4 * h2);
-                    const f32x4 og = ld4_io(ogp + (size_t)t * dv + 8 * bg + 4 * h2);
-#pragma unroll
-                    for (int y = 0; y < 4; ++y) {
-                        const float sg = sigmoid(og[y]);
-                        av[4 * h2 + y] = dh[y] * sg / den[i];
-                        go[4 * h2 + y] = dh[y] * acc[x][4 * h2 + y] / den[i] * sg * (1.0f - sg);
-                    }
-                }
-                float *o = a.go + ov + (size_t)t * dv + 8 * bg;
-                *reinterpret_cast<f32x4 *>(o) = f32x4{go[0], go[1], go[2], go[3]};
-                *reinterpret_cast<f32x4 *>(o + 4) = f32x4{go[4], go[5], go[6], go[7]};
-            }
-            *reinterpret_cast<f32x4 *>(&Aw[i * dv + 8 * bg]) = f32x4{av[0], av[1], av[2], av[3]};
-            *reinterpret_cast<f32x4 *>(&Aw[i * dv + 8 * bg + 4]) = f32x4{av[4], av[5], av[6], av[7]};
-            float an = 0.0f;
-#pragma unroll
-            for (int y = 0; y < 8; ++y) an = fmaf(av[y], acc[x][y], an);
-            part[i * NBGM + bg] = an;
-        }
     }
     __syncthreads();  // a rows in the workspace and the row partials visible
     if (tid < L) {
         const int i = tid;
         float an = 0.0f;
-        for (int b = 0; b < NBG; ++b) an += part[i * NBGM + b];
+        for (int b = 0; b < NU; ++b) an += part[i * NUM + b];
         beta[i] = fabsf(dd[i]) > fl[i] ? (dd[i] > 0.0f ? -an : an) / den[i] : 0.0f;
         Sw[i] = sv[i];
         Sw[L + i] = exp_e(gu[i] - r_last);
         Sw[2 * L + i] = beta[i];
         if (i == 0) Sw[3 * L] = exp_e(m_prev - r_last);
     }
-    // ---- P~_ij = (a_i.v_j + beta_i) e^{u_j - r_i}: thread (i, jq) owns j = 2jq, 2jq + 1
-    const int pi = tid >> 4, pj = 2 * (tid & 15);
-    float pa0 = 0.0f, pa1 = 0.0f;
-    float *At = stage, *Vt = stage + BK * L;
-    for (int b0 = 0; b0 < dv; b0 += BK) {
-        __syncthreads();
-        for (int e = tid; e < L * BK; e += NTA) {
-            const int i = e / BK, k = e % BK, t = t0 + i;
-            At[k * L + i] = Aw[i * dv + b0 + k];
-            Vt[k * L + i] = t < T ? to_f(vg[(size_t)t * dv + b0 + k]) : 0.0f;
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int k = 0; k < BK; ++k) {
-            const float av = At[k * L + pi];
-            pa0 = fmaf(av, Vt[k * L + pj], pa0);
-            pa1 = fmaf(av, Vt[k * L + pj + 1], pa1);
-        }
-    }
-    // P and P~ to the workspace (beta is in LDS since the barriers above)
+    // ---- a.v for P~: tile (ti, tj) of [L][L]; this wavefront takes the
+    // 16-column blocks wave, wave + 8, ... (up to four; blocks past d_v load
+    // zeros).  pt[ti][tj][v] = sum over its blocks of a_i . v_j, i = 16 ti +
+    // 4g + v, j = 16 tj + l16.
     {
-        const int i = pi;
-        const bool row = t0 + i < T;
-        Pw[i * L + pj] = P[i * L + pj];
-        Pw[i * L + pj + 1] = P[i * L + pj + 1];
-        Pw[L * L + i * L + pj] = (pj <= i && row) ? (pa0 + beta[i]) * exp_e(gu[pj] - gr[i]) : 0.0f;
-        Pw[L * L + i * L + pj + 1] = (pj + 1 <= i && row) ? (pa1 + beta[i]) * exp_e(gu[pj + 1] - gr[i]) : 0.0f;
+        const int NB16 = dv / 16;
+        const __amdgpu_buffer_rsrc_t ar = rsrc(Aw, (size_t)L * dv * 4);
+        f32x4 a4[4][2];
+        typename Quad<IO>::raw v4[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int kb = wave + NW * u;
+            const bool ok = kb < NB16;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                a4[u][h] = buf_ld4(ar, ok ? (unsigned)(((16 * h + l16) * dv + 16 * kb + 4 * g) * 4) : kFar);
+                v4[u][h] = Quad<IO>::load(
+                    vr, ok ? (unsigned)(((t0 + 16 * h + l16) * dv + 16 * kb + 4 * g) * (int)sizeof(IO)) : kFar);
+            }
+        }
+        f32x4 pt[2][2];
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < 2; ++tj) pt[ti][tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 vb0 = Quad<IO>::cvt(v4[u][0]), vb1 = Quad<IO>::cvt(v4[u][1]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti) {
+                    pt[ti][0] = mfma4(a4[u][ti][s], vb0[s], pt[ti][0]);
+                    pt[ti][1] = mfma4(a4[u][ti][s], vb1[s], pt[ti][1]);
+                }
+        }
+        float *red = K;  // [NW][L][L] partial sums (K is no longer read)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    red[(wave * L + 16 * ti + 4 * g + v) * L + 16 * tj + l16] = pt[ti][tj][v];
+    }
+    __syncthreads();
+    // P~_ij = (a_i.v_j + beta_i) e^{u_j - r_i}, and P, to the workspace
+    for (int e = tid; e < L * L; e += NTA) {
+        const int i = e / L, j = e % L;
+        float pa = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) pa += K[w2 * L * L + e];
+        Pw[e] = P[i * LP + j];
+        Pw[L * L + e] = (j <= i && t0 + i < T) ? (pa + beta[i]) * exp_e(gu[j] - gr[i]) : 0.0f;
     }
 }
 
@@ -694,30 +736,6 @@ __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
         __syncthreads();
     }
     if (tid == 0) base[lay.off_m + blk] = red[0];
-}
-
-// Pass C's dv part: four steps of rows of G* (steps sc .. sc + 3, rows
-// 4s + g, sc = min(s0, ns - 4)) into gr4, and their MFMAs against the K tile
-// (on = 0 makes a group contribute nothing).
-__device__ __forceinline__ void dv_gload(f32x4 (&gr4)[4], __amdgpu_buffer_rsrc_t r, unsigned off,
-                                         unsigned rstep, int s0, int ns) {
-    const int sc = min(s0, ns - 4);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) gr4[u] = buf_ld4(r, off + (unsigned)(sc + u) * rstep);
-}
-template <int LK>
-__device__ __forceinline__ void dv_gstep(f32x4 (&x)[2][4], const f32x4 (&gr4)[4], const float *K, int l16, int g,
-                                         int s0, float on) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int r = 4 * (s0 + u) + g;
-        const float k0 = on * K[l16 * LK + r], k1 = on * K[(16 + l16) * LK + r];
-#pragma unroll
-        for (int xx = 0; xx < 4; ++xx) {
-            x[0][xx] = mfma4(k0, gr4[u][xx], x[0][xx]);
-            x[1][xx] = mfma4(k1, gr4[u][xx], x[1][xx]);
-        }
-    }
 }
 
 // Pass C: one workgroup per (chunk, pair); its contractions run on the
