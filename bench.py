@@ -410,7 +410,10 @@ def main():
                         "(checkpoint pass + chunk-parallel passes and column-block scans, 32-token chunks)",
             "ms_per_step": msb7, "tokens_per_s": wb7.B * wb7.T / msb7 * 1e3,
             "roofline": {"bound": "alu", "achieved": flb7 / msb7 / 1e9, "peak": PEAK_FP32_TFLOPS,
-                         "unit": "TFLOP/s", "frac": flb7 / msb7 / 1e9 / PEAK_FP32_TFLOPS, "traffic": None,
+                         "unit": "TFLOP/s", "frac": flb7 / msb7 / 1e9 / PEAK_FP32_TFLOPS,
+                         "traffic": traffic_record("backward_7b"),
+                         "traffic_note": "HBM bytes per call summed over bwd_ckpt/a/b/c_kernel<bf16> "
+                                         "(bwd_d_kernel moves a few KB)",
                          "kernel": BWD_KERNELS,
                          "algorithmic_flops_per_launch": flb7}}
 

@@ -44,6 +44,7 @@ KERNEL_FILES = {
     "prefill_7b": ["common.hpp", "prefill.hip", "prefill_ws.hpp", "prefill_bf16.hpp",
                    "prefill_kernel.hpp"],
     "decode": ["common.hpp", "step.hip"],
+    "backward_7b": ["common.hpp", "backward.hip"],
 }
 
 
