@@ -170,7 +170,8 @@ template <> struct Quad<bf16> {
 // issues the loads of one chunk, put() converts them to float32 and writes
 // them to an [L][ldd] LDS tile.  Rows past the descriptor's end (tokens past
 // T) read as zero; groups past the tile (NQ * NT may exceed L * w / 4) load
-// nothing and are not written.  w and c0 are multiples of 4.
+// nothing and are not written; whole rounds of NT groups past the tile are
+// skipped.  w and c0 are multiples of 4.
 template <typename E, int NQ, int NT>
 struct TileFetch {
     typename Quad<E>::raw r[NQ];
@@ -178,6 +179,7 @@ struct TileFetch {
         const int g4 = w >> 2;
 #pragma unroll
         for (int u = 0; u < NQ; ++u) {
+            if (u * NT >= L * g4) break;  // uniform: no group of this round lies in the tile
             const int q = tid + u * NT, i = q / g4;
             const unsigned e = (unsigned)(t0 + i) * (unsigned)ld + (unsigned)(c0 + 4 * (q - i * g4));
             r[u] = Quad<E>::load(rs, i < L ? e * (unsigned)sizeof(E) : kFar);
@@ -191,6 +193,7 @@ struct TileFetch {
         const int g4 = w >> 2;
 #pragma unroll
         for (int u = 0; u < NQ; ++u) {
+            if (u * NT >= L * g4) break;  // uniform, as in fetch
             const int q = tid + u * NT, i = q / g4;
             *reinterpret_cast<f32x4 *>(&dst[i < L ? i * ldd + 4 * (q - i * g4) : L * ldd]) = Quad<E>::cvt(r[u]);
         }
@@ -341,11 +344,13 @@ __global__ __launch_bounds__(NTS) void bwd_ckpt_kernel(BwdArgs a) {
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < 2; ++q) {
+                if (!arow[x] || !aq[q]) continue;  // uniform in the wavefront: the tile lies outside
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
                     buf_st4(f32x4{sacc[x][q][0][v], sacc[x][q][1][v], sacc[x][q][2][v], sacc[x][q][3][v]}, rs,
                             soff[x][q] + (unsigned)(v * dv * 4));
+            }
         buf_st1(tid < dk ? ns[tid < dk ? tid : 0] : m, rs, noff);
         if (c + 1 == nch) break;  // the state after the last chunk is not needed
         fetch(t0 + L);
@@ -663,11 +668,13 @@ __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < 2; ++q) {
+                if (!arow[x] || !aq[q]) continue;  // uniform in the wavefront: the tile lies outside
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
                     buf_st4(f32x4{gacc[x][q][0][v], gacc[x][q][1][v], gacc[x][q][2][v], gacc[x][q][3][v]}, gsd,
                             soff[x][q] + (unsigned)(v * dv * 4));
+            }
         buf_st1(gs[tid < dk ? tid : 0], gsd, goff);
         fetch(max(c - 1, 0));
         lds_barrier();
