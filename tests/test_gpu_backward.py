@@ -126,7 +126,11 @@ def test_matches_autograd_free_identities():
 
 
 @pytest.mark.parametrize("dk,dv,io", [(128, 64, "f32"), (64, 128, "f32"), (80, 96, "f32"),
-                                      (256, 512, "f32"), (256, 512, "bf16")])
+                                      (256, 512, "f32"), (256, 512, "bf16"),
+                                      # odd counts of 16-row tiles above 128 (the second row
+                                      # tile of a wavefront valid on some only) and a last
+                                      # value-column block of 16 of 128 columns
+                                      (240, 400, "f32"), (176, 144, "bf16")])
 def test_large_heads(dk, dv, io):
     """Heads above 64 (state and tiles in the workspace), with a random initial
     state and a ragged last chunk."""
