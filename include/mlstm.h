@@ -231,9 +231,9 @@ mlstm_status_t mlstm_step(const void *q, const void *k, const void *v,
  * parallel and the carried gradient is scanned by blocks of value columns,
  * with the per-chunk states, rows and carried gradients kept in the
  * workspace, about T/32 * (2 d_qk d_v + 32 d_v) floats per sequence.
- * Larger heads, and sequences with T * max(d_qk, d_v) >= 2^29 (one
- * sequence's q, k or v in float32 at 2 GiB or more), return
- * MLSTM_ERR_UNSUPPORTED.
+ * Larger heads, and sequences with (T + 32) * max(d_qk, d_v) >= 2^29
+ * (one sequence's q, k or v, or their gradients, at 2 GiB or more in float32),
+ * return MLSTM_ERR_UNSUPPORTED.
  * Errors as for mlstm_fwd_chunkwise; every output must overlap no input, no
  * other output and no workspace (MLSTM_ERR_ALIAS).
  */

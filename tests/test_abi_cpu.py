@@ -276,8 +276,8 @@ def test_bwd_workspace_query(lib):
     assert bws(2, 3, 70, 272, 64, 32, B.F32)[0] == UNSUP     # d_qk above 256
     assert bws(2, 3, 70, 64, 528, 32, B.BF16)[0] == UNSUP    # d_v above 512
     assert bws(2, 3, 70, 24, 64, 32, B.F32)[0] == UNSUP      # not a multiple of 16
-    assert bws(1, 1, (1 << 20) - 32, 256, 512, 32, B.BF16)[0] == OK
-    assert bws(1, 1, 1 << 20, 256, 512, 32, B.BF16)[0] == UNSUP   # T * 512 floats = 2 GiB
+    assert bws(1, 1, (1 << 20) - 64, 256, 512, 32, B.BF16)[0] == OK
+    assert bws(1, 1, (1 << 20) - 32, 256, 512, 32, B.BF16)[0] == UNSUP   # (T + 32) * 512 floats = 2 GiB
     assert bws(2, 3, 70, 64, 64, 48, B.F32)[0] == UNSUP      # chunk
     assert bws(2, 3, 0, 64, 64, 32, B.F32)[0] == SHAPE
     assert bws(2, 3, 70, 64, 64, 32, 5)[0] == UNSUP          # dtype

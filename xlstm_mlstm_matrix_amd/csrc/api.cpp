@@ -320,8 +320,9 @@ static mlstm_status_t bwd_check_dims(int B, int H, int T, int d_qk, int d_v, int
     if (!mul_ok((size_t)B, (size_t)H, &BH) || BH > (size_t)INT32_MAX) return MLSTM_ERR_SHAPE;
     if (!mul_ok(BH, (size_t)T, &n) || !mul_ok(n, (size_t)(d_qk > d_v ? d_qk : d_v), &n))
         return MLSTM_ERR_SHAPE;
-    // one sequence's q, k or v is read through 32-bit buffer offsets
-    if ((size_t)T * (size_t)(d_qk > d_v ? d_qk : d_v) * sizeof(float) >= ((size_t)1 << 31))
+    // one sequence's q, k, v and gradients are addressed through 32-bit
+    // offsets, up to a chunk past T
+    if ((size_t)(T + kBwdChunk) * (size_t)(d_qk > d_v ? d_qk : d_v) * sizeof(float) >= ((size_t)1 << 31))
         return MLSTM_ERR_UNSUPPORTED;
     if (!mul_ok(BH, bwd_ckpt_floats(T, d_qk, d_v), &n) || !mul_ok(n, sizeof(float), bytes))
         return MLSTM_ERR_SHAPE;
