@@ -995,11 +995,26 @@ __global__ __launch_bounds__(64) void bwd_d_kernel(BwdArgs a) {
     const int nch = (int)lay.nch;
     const float *base = a.ckpt + (size_t)p * lay.total;
     const size_t og1 = (size_t)p * T;
-    float carry = 0.0f;
-    for (int c = nch - 1; c >= 0; --c) {
-        const int t = c * L + lane;
-        if (lane < L && t < T) a.gf[og1 + t] += carry;
-        carry += base[lay.off_x + c];
+    // groups of 64 chunks from the end: lane j takes chunk c0 + j; its carry
+    // is the sum of the totals of every later chunk (an exclusive suffix sum,
+    // within the group by a wavefront scan, plus the later groups' running
+    // sum), which it then adds to the df~ of its chunk's tokens
+    float running = 0.0f;
+    for (int c0 = (nch - 1) / 64 * 64; c0 >= 0; c0 -= 64) {
+        const int c = c0 + lane;
+        const float x = c < nch ? base[lay.off_x + c] : 0.0f;
+        float y = x;  // sum over lanes >= this one
+        for (int o = 1; o < 64; o <<= 1) {
+            const float z = __shfl_down(y, o, 64);
+            if (lane + o < 64) y += z;
+        }
+        const float carry = running + (y - x);
+        running += __shfl(y, 0, 64);
+        if (c < nch) {
+            float *gf = a.gf + og1 + (size_t)c * L;
+            const int n = min(L, T - c * L);
+            for (int i = 0; i < n; ++i) gf[i] += carry;
+        }
     }
     if (a.gm0) {
         float part = 0.0f;
