@@ -107,9 +107,11 @@ __device__ void chunk_gates(const float *ig, const float *fg, int t0, int T, flo
 #ifndef BWD_BVB
 #define BWD_BVB 128
 #endif
-// value columns per workgroup of the two scans (128 measured fastest: 64 and
-// 32 re-read the K or Q tile more often, 256 halves the workgroups), and their
-// threads (a 4 x 16 tile of the block per thread, rows up to 256)
+// value columns per workgroup of the two scans (128 measured fastest when the
+// scans ran on the vector units: 64 and 32 re-read the K or Q tile more
+// often, 256 halves the workgroups), and their threads (eight wavefronts, each
+// holding two 16-row tiles of the block by two 64-column quads as MFMA
+// accumulators; rows up to 256)
 constexpr int NTA = 512, BVB = BWD_BVB, CG = BVB / 16, NTS = 64 * CG;
 
 // load rows t0 .. t0 + L - 1 of a [T, d] input as float32 into a [L][ld] tile
@@ -246,10 +248,11 @@ __device__ __forceinline__ void dv_gstep(f32x4 (&x)[2][4], const f32x4 (&gr4)[4]
 
 // Checkpoint pass: one workgroup per (block of BVB value columns, pair).  The
 // state recurrence is separable by value column, so each workgroup carries
-// its [d_qk][BVB] block of C' in registers (a 4 x 16 tile per thread) and
-// writes it to the record of every chunk start; block 0 also carries n' and
-// writes m (every block computes the same gates).  The K and V tiles and the
-// gates of the next chunk load while the current chunk computes.
+// its [d_qk][BVB] block of C' in registers (as MFMA accumulators, laid out
+// below) and writes it to the record of every chunk start; block 0 also
+// carries n' and writes m (every block computes the same gates).  The K and V
+// tiles and the gates of the next chunk load while the current chunk
+// computes.
 template <typename IO>
 __global__ __launch_bounds__(NTS) void bwd_ckpt_kernel(BwdArgs a) {
     constexpr int LK = kBwdMaxDk + 4;
@@ -599,8 +602,8 @@ __global__ __launch_bounds__(NTA) void bwd_a_kernel(BwdArgs a) {
 }
 
 // Pass B: one workgroup per (block of BVB value columns, pair): G* and g*
-// backwards over the chunks, G*'s [d_qk][BVB] block in registers (a 4 x 16
-// tile per thread, as in the checkpoint pass); block 0 also carries g*.
+// backwards over the chunks, G*'s [d_qk][BVB] block in registers (as MFMA
+// accumulators, laid out as in the checkpoint pass); block 0 also carries g*.
 template <typename IO>
 __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
     constexpr int LK = kBwdMaxDk + 4;
@@ -752,8 +755,9 @@ __global__ __launch_bounds__(NTS) void bwd_b_kernel(BwdArgs a) {
 //     k index of successive MFMAs is permuted alike in both operands), then
 //     are scaled per token, and the in-chunk P~ K and P~^T Q are added
 //     through the same accumulators;
-//   dv by 16 value columns: G*^T k over the rows of G*, scaled per token,
-//     plus P^T a.
+//   dv by 64 value columns: G*^T k over the rows of G* (a lane reads four
+//     consecutive columns of a row, one for each of four MFMA tiles), scaled
+//     per token, plus P^T a.
 // q.dq and k.dk are summed per (token, 16 rows) into partials for the gates.
 template <typename IO>
 __global__ __launch_bounds__(NTA) void bwd_c_kernel(BwdArgs a) {
