@@ -140,6 +140,16 @@ def test_large_heads(dk, dv, io):
     compare(out, ref[:len(out)], io, f"large heads {dk}x{dv} {io}", state_grad=io == "f32")
 
 
+@pytest.mark.parametrize("T", [1, 32, 33])
+def test_large_heads_chunk_edges(T):
+    """Heads above 64 at one token, exactly one chunk and one token past it
+    (the scans' single-chunk and one-token-chunk cases)."""
+    w, d, dh = case("small_f32", pairs=[(0, 1), (1, 0)], T=T, d_qk=128, d_v=192, io="f32")
+    out = run_gpu(d, dh, True)
+    ref = run_oracle(d, dh)
+    compare(out, ref[:len(out)], "f32", f"large heads T={T}", state_grad=True)
+
+
 def test_7b_heads_bf16():
     """The 7B layer's heads and distributions (bf16, d_qk 256, d_v 512) over
     200 tokens of two pairs, from the zero state."""
