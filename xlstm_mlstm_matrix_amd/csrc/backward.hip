@@ -83,6 +83,26 @@ __device__ void gate_scan(float b, float i, float m_before, float *gb, float *gu
     *r_out = r;
 }
 
+// The part of gate_scan that does not depend on the stabilizer: lane j's
+// cumsum b of f~, u = i~ - b and the prefix max pm of u over lanes <= j.
+__device__ __forceinline__ void gate_prefix(float f, float i, float *b_out, float *u_out, float *pm_out) {
+    const int lane = threadIdx.x & 63;
+    float b = f;
+    for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(b, o, 64);
+        if (lane >= o) b += y;
+    }
+    const float u = i - b;
+    float pm = u;
+    for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(pm, o, 64);
+        if (lane >= o) pm = fmaxf(pm, y);
+    }
+    *b_out = b;
+    *u_out = u;
+    *pm_out = pm;
+}
+
 // gate_scan of tokens t0 .. t0 + L - 1, loading their gates
 __device__ void chunk_gates(const float *ig, const float *fg, int t0, int T, float m_before, float *gb,
                             float *gu, float *gr, float *last) {
@@ -257,7 +277,7 @@ template <typename IO>
 __global__ __launch_bounds__(NTS) void bwd_ckpt_kernel(BwdArgs a) {
     constexpr int LK = kBwdMaxDk + 4;
     __shared__ __attribute__((aligned(16))) float Ks[L * LK + 4], Vs[L * BVB + 4];
-    __shared__ float ns[kBwdMaxDk], wv[L], gb[L], gu[L], gr[L], last[2];
+    __shared__ float ns[kBwdMaxDk], wv[L], last[2];
     const int blk = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
     const int dk = a.dk, dv = a.dv, T = a.T;
     const int c0 = blk * BVB, w = min(BVB, dv - c0);
@@ -272,18 +292,33 @@ __global__ __launch_bounds__(NTS) void bwd_ckpt_kernel(BwdArgs a) {
     const __amdgpu_buffer_rsrc_t vr = rsrc(vg, (size_t)T * dv * sizeof(IO));
     TileFetch<IO, L * kBwdMaxDk / 4 / NTS, NTS> kf;
     TileFetch<IO, L * BVB / 4 / NTS, NTS> vf;
-    // every lane loads the gates of token t0 + lane % 64 (clamped into the
-    // sequence), and every wavefront runs the same scan of them
-    const int lane = tid & 63;
-    float fi, ff;
     auto fetch = [&](int t0) {
         kf.fetch(kr, dk, 0, dk, t0, tid);
         vf.fetch(vr, dv, c0, w, t0, tid);
-        const int t = min(t0 + lane, T - 1);
-        fi = igp[t];
-        ff = fgp[t];
     };
     fetch(0);
+    // The gates: every lane loads those of token t0 + lane % 64 (clamped into
+    // the sequence) two chunks ahead, into (ni, nf).  They are scanned a chunk
+    // ahead into (sb, su, sp) (gate_prefix), and the scan is finished with the
+    // stabilizer when the chunk starts; only last[] and wv[] are read by the
+    // other wavefronts.  When the last wavefront holds no state tiles (d_qk up
+    // to 112) it alone does this, while the others run the chunk's MFMAs;
+    // otherwise every wavefront does (one would delay the chunk).
+    const int lane = tid & 63;
+    const bool gwave = 16 * (NTS / 64 - 1) >= dk ? (tid >> 6) == NTS / 64 - 1 : true;
+    float ni, nf, sb = 0.0f, su = 0.0f, sp = 0.0f;
+    auto gload = [&](int t0) {
+        const int t = min(t0 + lane, T - 1);
+        ni = igp[t];
+        nf = fgp[t];
+    };
+    auto gscan = [&](int t0) {
+        const bool ok = lane < L && t0 + lane < T;
+        gate_prefix(ok ? nf : 0.0f, ok ? ni : -INFINITY, &sb, &su, &sp);
+    };
+    gload(0);
+    if (gwave) gscan(0);
+    gload(L);
     // The block of C' is held as MFMA accumulators: wavefront w owns row
     // tiles w and w + 8 (16 rows each) and two quads of 64 columns; in a
     // quad, lane (l16, g) holds the four consecutive columns 4 l16 .. +3, one
@@ -334,12 +369,14 @@ __global__ __launch_bounds__(NTS) void bwd_ckpt_kernel(BwdArgs a) {
         // tiles of the last chunk are not used)
         kf.put(Ks, LK, dk, tid);
         vf.put(Vs, BVB, w, tid);
-        {
-            const bool ok = lane < L && t0 + lane < T;
-            float u, rr;
-            gate_scan(ok ? ff : 0.0f, ok ? fi : -INFINITY, m, gb, gu, gr, last, &u, &rr);
-            const float r_last = __shfl(rr, L - 1, 64);
-            if (lane < L) wv[lane] = exp_e(u - r_last);
+        if (gwave) {  // this chunk's gates: r = max(m, prefix max u)
+            const float r = fmaxf(m, sp);
+            const float r_last = __shfl(r, L - 1, 64);
+            if (lane < L) wv[lane] = exp_e(su - r_last);
+            if (lane == L - 1) {
+                last[0] = sb;
+                last[1] = r;
+            }
         }
         // the state at this chunk's start (each thread reads and writes only
         // its own entries of ns; the other reads are discarded)
@@ -360,6 +397,8 @@ __global__ __launch_bounds__(NTS) void bwd_ckpt_kernel(BwdArgs a) {
         lds_barrier();
         const float b_last = last[0], r_last = last[1];
         const float dec = exp_e(m - r_last);
+        if (gwave) gscan(t0 + L);  // the next chunk's gates, off the chain
+        gload(t0 + 2 * L);
         // C' <- dec C' + sum_j (w_j k_j) v_j^T on the matrix cores (k index = token)
 #pragma unroll
         for (int x = 0; x < 2; ++x)
