@@ -13,13 +13,18 @@ roofline, and the float64 oracle timed on the host cores over a bounded
 sample (`cpu_baseline`).
 
 Kernel times come from HIP events recorded on the stream the library
-launches on (torch's current stream).  The default warmup (200 untimed
-steps, about 0.1 s of work) lets the GPU clock settle after the seconds of
-host-side input generation; with 3 warmup steps the first timed steps still
-run at a lower clock (about 25% slower on the 7B-layer prefill).  Rooflines use algorithmic work:
+launches on (torch's current stream), one before every timed step and one
+after the last: `ms_per_step` is the whole span over the K steps divided by
+K (the mean), `ms_per_step_median` the median of the per-step spans.  Before
+the warmup steps, whatever --warmup is, the prefill step runs untimed for a
+fixed stretch of GPU time (--settle-ms, default 300 ms), so that the clock
+has left the low state it sits in after the seconds of host-side input
+generation: without it the first timed steps ran about 25% slower on the
+7B-layer prefill.  Rooflines use algorithmic work:
   prefill flops per token-head  (L+1)(d_qk+d_v) + 4 d_qk d_v + 4 d_qk
   prefill bytes per token-head  2(2 d_qk + 2 d_v) + 2 d_v + 8   (bf16 q,k,v,o~ in, h out, f32 gates)
-  decode bytes per pair-step    8(d_qk d_v + d_qk + 1) + 2(2 d_qk + 2 d_v) + 8
+  decode bytes per pair-step    8(d_qk d_v + d_qk + 1) + 2(2 d_qk + 2 d_v) + 2 d_v + 8
+                                (state read + written, bf16 q,k,v,o~ in, h out, f32 gates)
 against MI355X peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8 TB/s.
 """
 from __future__ import annotations
@@ -38,6 +43,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_FP32_TFLOPS = 157.3  # fp32 vector peak of the chip (the unpacked FMA rate is half of it)
 BWD_KERNELS = "bwd_ckpt_kernel + bwd_a_kernel + bwd_b_kernel + bwd_c_kernel + bwd_d_kernel"
 METRIC = "mLSTM prefill tokens/s + %MFMA peak; decode step state GB/s + %HBM peak"
+PREFILL_KERNEL = "mlstm_ws_kernel<256> (role-split chunkwise forward, one launch per step)"
 CPU_THREADS_MAX = 16  # host cores that go with one GPU
 
 
@@ -45,8 +51,11 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def prefill_work(w):
-    L, dk, dv = w.chunk, w.d_qk, w.d_v
+def prefill_work(w, L=None):
+    """Algorithmic flops and bytes of one prefill call; flops are counted at
+    chunk L (the workload's chunk unless given)."""
+    L = w.chunk if L is None else L
+    dk, dv = w.d_qk, w.d_v
     th = w.B * w.H * w.T
     flops = th * ((L + 1) * (dk + dv) + 4 * dk * dv + 4 * dk)
     io_bytes = th * (2 * (2 * dk + 2 * dv) + 2 * dv + 8)
@@ -55,10 +64,12 @@ def prefill_work(w):
 
 
 def decode_work(w):
+    """Bytes of one decode step: the state read and written (float32), and
+    q, k, v, o~ read, h written (bf16), the two float32 gates read."""
     dk, dv = w.d_qk, w.d_v
     pairs = w.B * w.H
     state = pairs * 8 * (dk * dv + dk + 1)
-    io = pairs * (2 * (2 * dk + 2 * dv) + 8)
+    io = pairs * (2 * (2 * dk + 2 * dv) + 2 * dv + 8)
     return state, state + io
 
 
@@ -74,6 +85,46 @@ def traffic_record(name):
     if rec.get("kernel_src_sha") != src_hash(name):
         return None
     return rec.get("bytes_per_launch")
+
+
+def time_steps(torch, run, steps):
+    """Run `run` exactly `steps` times back to back between two device
+    synchronisations, with a HIP event before every step and after the last
+    (events on the stream the library launches on).  Returns (mean, median)
+    milliseconds per step: the mean is the whole span over the steps, the
+    median that of the per-step spans."""
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i].record(st)
+        run()
+    ev[steps].record(st)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    total = ev[0].elapsed_time(ev[steps])
+    mid = steps // 2
+    median = per[mid] if steps % 2 else 0.5 * (per[mid - 1] + per[mid])
+    return total / steps, median
+
+
+def settle_clock(torch, run, settle_ms):
+    """Untimed phase of fixed duration before any warmup: runs the step until
+    `settle_ms` of GPU time has passed, so that the clock has left its idle
+    state whatever --warmup is.  Returns (milliseconds spent, steps run)."""
+    spent, n, batch = 0.0, 0, 1
+    while spent < settle_ms:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(torch.cuda.current_stream())
+        for _ in range(batch):
+            run()
+        b.record(torch.cuda.current_stream())
+        b.synchronize()
+        spent += a.elapsed_time(b)
+        n += batch
+        batch = min(batch * 2, 256)
+    return spent, n
 
 
 class Timer:
@@ -93,7 +144,7 @@ class Timer:
         self.ms = self.a.elapsed_time(self.b)
 
 
-def bench_prefill(torch, I, binding, name, steps, warmup, variant="auto"):
+def bench_prefill(torch, I, binding, name, steps, warmup, variant="auto", settle_ms=0.0):
     w = I.workload(name)
     t0 = time.time()
     d = I.gen_prefill(w, threads=16)
@@ -113,17 +164,19 @@ def bench_prefill(torch, I, binding, name, steps, warmup, variant="auto"):
         binding.fwd_chunkwise(*args, chunk=w.chunk, variant=variant, h=h, C_T=C, n_T=n, m_T=m,
                               workspace=ws)
 
+    settle = settle_clock(torch, run, settle_ms) if settle_ms > 0 else (0.0, 0)
     for _ in range(warmup):
         run()
-    with Timer(torch) as tm:
-        for _ in range(steps):
-            run()
-    ms = tm.ms / steps
+    ms, med = time_steps(torch, run, steps)
+    kc, _ = binding.schedule(w.B, w.H, w.T, w.d_qk, w.d_v, w.chunk, io, variant)
     flops, nbytes = prefill_work(w)
+    flops_kc, _ = prefill_work(w, L=kc)
     tokens = w.B * w.T
-    log(f"{name}: {ms:.3f} ms/step, {tokens / ms * 1e3:.3e} tokens/s, "
-        f"{flops / ms / 1e9:.1f} TFLOP/s, {nbytes / ms / 1e6:.0f} GB/s")
-    return w, ms, flops, nbytes, (g, h, C, n, m)
+    log(f"{name}: {ms:.4f} ms/step (median {med:.4f}; clock settled over {settle[0]:.0f} ms, "
+        f"{settle[1]} steps), {tokens / ms * 1e3:.3e} tokens/s, {flops / ms / 1e9:.1f} TFLOP/s, "
+        f"{nbytes / ms / 1e6:.0f} GB/s")
+    return dict(w=w, ms=ms, median_ms=med, flops=flops, flops_kernel_chunk=flops_kc, kernel_chunk=kc,
+                bytes=nbytes, settle_ms=settle[0], settle_steps=settle[1], keep=(g, h, C, n, m))
 
 
 def bench_decode(torch, I, binding, warmup_passes=1, nsteps=None):
@@ -158,10 +211,14 @@ def bench_decode(torch, I, binding, warmup_passes=1, nsteps=None):
     with Timer(torch) as tm:
         one_pass()
     ms = tm.ms / w.T
+    # a second pass with an event around every step: the per-step median
+    it = iter(range(w.T))
+    _, med = time_steps(torch, lambda: binding.step(*(steps[k][next(it)] for k in keys), C, n, m, h=h,
+                                                    C_out=C, n_out=n, m_out=m, workspace=ws), w.T)
     state_bytes, total_bytes = decode_work(w)
-    log(f"decode: {ms:.4f} ms/step, state {state_bytes / ms / 1e6:.0f} GB/s, "
+    log(f"decode: {ms:.4f} ms/step (median {med:.4f}), state {state_bytes / ms / 1e6:.0f} GB/s, "
         f"total {total_bytes / ms / 1e6:.0f} GB/s, {w.B / ms * 1e3:.3e} tokens/s")
-    return w, ms, state_bytes, total_bytes
+    return w, ms, med, state_bytes, total_bytes
 
 
 def backward_work(w, L=32):
@@ -271,8 +328,8 @@ def cpu_baseline(I, pairs_sample):
     import oracle
     w = I.workload("prefill_7b_bf16")
     d = I.gen_prefill(w, pairs=pairs_sample, threads=16)
-    cores = min(len(os.sched_getaffinity(0)), CPU_THREADS_MAX)
-    threads = min(cores, len(pairs_sample))
+    host_cores = len(os.sched_getaffinity(0))
+    threads = min(host_cores, CPU_THREADS_MAX, len(pairs_sample))
     orc = oracle.load()
     t0 = time.time()
     orc.forward(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"], threads=threads)
@@ -280,7 +337,8 @@ def cpu_baseline(I, pairs_sample):
     frac = len(pairs_sample) / (w.B * w.H)
     tokens_per_s = (w.B * w.T) * frac / dt   # the sample's share of the workload's tokens
     log(f"cpu oracle: {len(pairs_sample)} pairs x {w.T} tokens in {dt:.2f}s on {threads} threads")
-    return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "host_cores": host_cores,
+            "threads_cap": CPU_THREADS_MAX, "kind": "oracle",
             "sample": f"{len(pairs_sample)} of {w.B * w.H} (batch, head) pairs of the 7B-layer prefill "
                       f"workload, full T={w.T} each, float64 sequential recurrence, OpenMP over pairs; "
                       f"rate = sampled tokens x (pairs sampled / all pairs) / wall time "
@@ -293,6 +351,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed GPU time spent running the prefill step before its warmup, "
+                         "whatever --warmup is, so the timed steps run at the settled clock")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -329,15 +390,17 @@ def main():
         log("copy probe: 3 x 1 GiB streamed (neg)")
         del src, dst
 
-    rec = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1}
     if args.no_prefill:
         w = I.workload("prefill_7b_bf16")
-        ms = flops = nbytes = float("nan")
+        r = dict(w=w, ms=float("nan"), median_ms=float("nan"), flops=float("nan"),
+                 flops_kernel_chunk=float("nan"), kernel_chunk=w.chunk, bytes=float("nan"),
+                 settle_ms=0.0, settle_steps=0)
     else:
-        w, ms, flops, nbytes, _keep = bench_prefill(torch, I, binding, "prefill_7b_bf16", args.steps,
-                                                    args.warmup)
-        del _keep
+        r = bench_prefill(torch, I, binding, "prefill_7b_bf16", args.steps, args.warmup,
+                          settle_ms=args.settle_ms)
+        r.pop("keep")
         torch.cuda.empty_cache()
+    w, ms, flops, nbytes = r["w"], r["ms"], r["flops"], r["bytes"]
     tflops = flops / ms / 1e9
     gbs = nbytes / ms / 1e6
     kc, nseg = binding.schedule(w.B, w.H, w.T, w.d_qk, w.d_v, w.chunk, binding.BF16)
@@ -349,6 +412,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": r["median_ms"],
+        "clock_settle": {"ms": r["settle_ms"], "steps": r["settle_steps"]},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -360,34 +425,40 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": traffic_record("prefill_7b"),
-                     "kernel": "mlstm_ws_kernel<256> (role-split chunkwise forward, one launch per step)",
-                     "mfma": {"achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                              "frac": tflops / PEAK_BF16_TFLOPS},
+                     "mfma_achieved_tflops": tflops, "mfma_peak_tflops": PEAK_BF16_TFLOPS,
+                     "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+                     "kernel": PREFILL_KERNEL,
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes},
     }
 
     if not args.no_long:
         try:
-            wl, msl, fl, bl, _keep = bench_prefill(torch, I, binding, "prefill_long_bf16",
-                                                  max(3, args.steps // 4), max(1, args.warmup // 4))
-            del _keep
+            rl = bench_prefill(torch, I, binding, "prefill_long_bf16", max(3, args.steps // 4),
+                               max(1, args.warmup // 4), settle_ms=min(args.settle_ms, 100.0))
+            rl.pop("keep")
             torch.cuda.empty_cache()
+            wl, msl = rl["w"], rl["ms"]
             kcl, nsl = binding.schedule(wl.B, wl.H, wl.T, wl.d_qk, wl.d_v, wl.chunk, binding.BF16)
             rec["long_context"] = {
                 "workload": "prefill B=1 H=8 T=65536 d_qk=256 d_v=512 chunk=128 bf16 I/O fp32 state, "
                             "final state returned",
                 "kernel_chunk": kcl, "segments": nsl,
-                "ms_per_step": msl, "tokens_per_s": wl.B * wl.T / msl * 1e3,
-                "mfma_frac": fl / msl / 1e9 / PEAK_BF16_TFLOPS, "hbm_frac": bl / msl / 1e6 / PEAK_HBM_GBS}
+                "ms_per_step": msl, "ms_per_step_median": rl["median_ms"],
+                "tokens_per_s": wl.B * wl.T / msl * 1e3,
+                "mfma_frac": rl["flops"] / msl / 1e9 / PEAK_BF16_TFLOPS,
+                "mfma_frac_at_kernel_chunk": rl["flops_kernel_chunk"] / msl / 1e9 / PEAK_BF16_TFLOPS,
+                "flops_note": f"mfma_frac counts the intra-chunk flops at the requested chunk "
+                              f"({wl.chunk}); mfma_frac_at_kernel_chunk at the executed one ({kcl})",
+                "hbm_frac": rl["bytes"] / msl / 1e6 / PEAK_HBM_GBS}
         except Exception as e:  # reported, not hidden
             rec["long_context"] = {"error": str(e)}
             log(f"long context: {e}")
 
     if not args.no_decode:
-        wd, msd, sb, tb = bench_decode(torch, I, binding, nsteps=args.decode_steps or None)
+        wd, msd, medd, sb, tb = bench_decode(torch, I, binding, nsteps=args.decode_steps or None)
         rec["decode"] = {
             "workload": "decode B=256 H=8 d_qk=256 d_v=512, 1024 in-place mlstm_step calls, bf16 I/O fp32 state",
-            "ms_per_step": msd, "tokens_per_s": wd.B / msd * 1e3,
+            "ms_per_step": msd, "ms_per_step_median": medd, "tokens_per_s": wd.B / msd * 1e3,
             "state_GBs": sb / msd / 1e6,
             "roofline": {"bound": "hbm", "achieved": tb / msd / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": tb / msd / 1e6 / PEAK_HBM_GBS, "traffic": traffic_record("decode"),

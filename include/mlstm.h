@@ -283,8 +283,12 @@ mlstm_status_t mlstm_layer_fwd_workspace_size(int B, int T, int d_model, int H, 
  * one hipBLASLt handle per device on first use and keeps it, with the
  * algorithm chosen per GEMM shape, until the process ends.  Errors: as
  * mlstm_fwd_chunkwise, plus MLSTM_ERR_BLAS when a hipBLASLt call fails (the
- * projections enqueued before it may have run); inputs overlapping an output
- * or the workspace -> MLSTM_ERR_ALIAS.
+ * projections enqueued before it may have run).  Every check runs on the host
+ * before the first projection is enqueued: a state triple given in part ->
+ * MLSTM_ERR_STATE_ARGS; any pointer misaligned -> MLSTM_ERR_ALIGN; h, C_T,
+ * n_T, m_T and the workspace overlapping a layer input, each other, or an
+ * initial-state buffer -> MLSTM_ERR_ALIAS, except that C_T, n_T, m_T may
+ * coincide exactly with C0, n0, m0 (the state updated in place).
  */
 mlstm_status_t mlstm_layer_fwd(const void *x, const void *W_q, const void *W_k, const void *W_v,
                                const void *W_o, const void *W_i, const void *W_f,

@@ -45,15 +45,23 @@ static double sigmoid(double x) {
     return e / (1.0 + e);
 }
 
-/* one group of d cells over T tokens */
-static void run_group(const double *gx, const double *R, const double *c0, const double *n0,
-                      const double *m0, const double *h0, double *h, double *cT, double *nT,
-                      double *mT, double *hT, long T, long d) {
+/* one group of d cells over T tokens; returns 0, or -2 when out of memory */
+static int run_group(const double *gx, const double *R, const double *c0, const double *n0,
+                     const double *m0, const double *h0, double *h, double *cT, double *nT,
+                     double *mT, double *hT, long T, long d) {
     double *c = calloc((size_t)d, sizeof(double));
     double *n = calloc((size_t)d, sizeof(double));
     double *m = calloc((size_t)d, sizeof(double));
     double *hp = calloc((size_t)d, sizeof(double));     /* h_{t-1} */
     double *pre = malloc((size_t)(4 * d) * sizeof(double));
+    if (!c || !n || !m || !hp || !pre) {
+        free(c);
+        free(n);
+        free(m);
+        free(hp);
+        free(pre);
+        return -2;
+    }
     if (c0) {
         memcpy(c, c0, (size_t)d * sizeof(double));
         memcpy(n, n0, (size_t)d * sizeof(double));
@@ -95,25 +103,29 @@ static void run_group(const double *gx, const double *R, const double *c0, const
     free(m);
     free(hp);
     free(pre);
+    return 0;
 }
 
-/* Returns 0, or -1 on bad sizes.  The state arguments come in complete sets:
- * all of c0, n0, m0, h0 or none; all of cT, nT, mT, hT or none. */
+/* Returns 0, -1 on bad sizes, -2 when out of memory.  The state arguments
+ * come in complete sets: all of c0, n0, m0, h0 or none; all of cT, nT, mT,
+ * hT or none.  threads > 0 sets the number of threads of this call only
+ * (0: the OpenMP default); the process-wide setting is left alone. */
 int slstm_ref_forward(const double *gx, const double *R, const double *c0, const double *n0,
                       const double *m0, const double *h0, double *h, double *cT, double *nT,
                       double *mT, double *hT, long P, long T, long d, int threads) {
     if (P < 0 || T < 0 || d <= 0) return -1;
+    int fail = 0;
 #ifdef _OPENMP
-    if (threads > 0) omp_set_num_threads(threads);
-#pragma omp parallel for schedule(dynamic, 1)
+    if (threads <= 0) threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(threads) reduction(| : fail)
 #endif
     for (long p = 0; p < P; ++p) {
         const size_t sd = (size_t)p * d;
-        run_group(gx + (size_t)p * T * 4 * d, R + (size_t)p * 4 * d * d, c0 ? c0 + sd : NULL,
-                  n0 ? n0 + sd : NULL, m0 ? m0 + sd : NULL, h0 ? h0 + sd : NULL,
-                  h + (size_t)p * T * d, cT ? cT + sd : NULL, nT ? nT + sd : NULL,
-                  mT ? mT + sd : NULL, hT ? hT + sd : NULL, T, d);
+        fail |= run_group(gx + (size_t)p * T * 4 * d, R + (size_t)p * 4 * d * d, c0 ? c0 + sd : NULL,
+                          n0 ? n0 + sd : NULL, m0 ? m0 + sd : NULL, h0 ? h0 + sd : NULL,
+                          h + (size_t)p * T * d, cT ? cT + sd : NULL, nT ? nT + sd : NULL,
+                          mT ? mT + sd : NULL, hT ? hT + sd : NULL, T, d) != 0;
     }
     (void)threads;
-    return 0;
+    return fail ? -2 : 0;
 }

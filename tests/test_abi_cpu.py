@@ -405,6 +405,51 @@ def test_layer_validation(lib):
     assert call_layer(a) == ALIAS
 
 
+def with_layer_state(a, inplace=False):
+    fa = Fake()
+    fa.next = 1 << 44  # far from the addresses layer_args handed out
+    B_, T, D, H, dk, dv = a["dims"][:6]
+    P = H * B_
+    a.update(C0=fa(P * dk * dv * 4), n0=fa(P * dk * 4), m0=fa(P * 4))
+    if inplace:
+        a.update(CT=a["C0"], nT=a["n0"], mT=a["m0"])
+    else:
+        a.update(CT=fa(P * dk * dv * 4), nT=fa(P * dk * 4), mT=fa(P * 4))
+    return a
+
+
+def test_layer_validation_precedes_device_work(lib):
+    # The cell's own checks (state triples, alignment of the state and h,
+    # overlap of h / the final state / the workspace) run before the first
+    # projection is enqueued: each of these returns its validation status, not
+    # MLSTM_ERR_HIP from a device call.
+    for key in ("C0", "n0", "m0", "CT", "nT", "mT"):
+        a = with_layer_state(layer_args()); a[key] = None
+        assert call_layer(a) == STATE, key
+    for key in ("C0", "n0", "m0", "h", "CT", "nT", "mT"):
+        a = with_layer_state(layer_args()); a[key] += 4
+        assert call_layer(a) == 8, key   # MLSTM_ERR_ALIGN
+    a = layer_args(); a["h"] = a["ws"] + 256       # h inside the workspace
+    assert call_layer(a) == ALIAS
+    a = with_layer_state(layer_args()); a["CT"] = a["ws"]
+    assert call_layer(a) == ALIAS
+    a = with_layer_state(layer_args()); a["nT"] = a["h"]
+    assert call_layer(a) == ALIAS
+    a = with_layer_state(layer_args()); a["C0"] = a["ws"] + 1024   # read state inside the workspace
+    assert call_layer(a) == ALIAS
+    a = with_layer_state(layer_args()); a["h"] = a["C0"]
+    assert call_layer(a) == ALIAS
+    a = with_layer_state(layer_args()); a["CT"] = a["C0"] + 16     # partial overlap, not in place
+    assert call_layer(a) == ALIAS
+    a = with_layer_state(layer_args()); a["nT"] = a["C0"]          # another state buffer
+    assert call_layer(a) == ALIAS
+    # in place but with h overlapping the state: still rejected (an exact
+    # in-place call with valid buffers would reach device work, which these
+    # fake addresses must never do)
+    a = with_layer_state(layer_args(), inplace=True); a["h"] = a["m0"]
+    assert call_layer(a) == ALIAS
+
+
 # ---- sLSTM: host-side validation only
 
 def slstm_args(B_=2, H=3, T=50, d=32, io=B.BF16, state=True):

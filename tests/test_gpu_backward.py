@@ -157,6 +157,29 @@ def test_7b_heads_bf16():
     compare(run_gpu(d, dh, False), run_oracle(d, dh)[:6], "bf16", "7b heads", state_grad=False)
 
 
+@pytest.mark.parametrize("T,pairs", [(1024, [(0, 0), (7, 5)]), (2100, [(3, 6)])])
+def test_7b_heads_bf16_long(T, pairs):
+    """The 7B layer's heads (bf16, d_qk 256, d_v 512) over long sequences:
+    1024 tokens (32 chunks) of two pairs, and 2100 tokens of one pair, which
+    crosses the 64-chunk groups of the carried-gradient scan (the benchmark
+    runs 4096 tokens, 128 chunks)."""
+    w, d, dh = case("prefill_7b_bf16", pairs=pairs, T=T)
+    print(f"[case] backward 7b heads T={T} pairs={pairs}", flush=True)
+    out = run_gpu(d, dh, False)
+    compare(out, run_oracle(d, dh)[:6], "bf16", f"7b heads T={T}", state_grad=False)
+
+
+def test_long_sequence_f32_chunk_groups():
+    """Float32, d=64, 2200 tokens (69 chunks of 32) with an initial state:
+    the carried-gradient scan runs past its first 64-chunk group, with the
+    state gradients."""
+    w = I.workload("small_f32", T=2200)   # the workload's own T is 1024
+    d = I.gen_prefill(w, pairs=[(2, 1)])
+    dh = I.to_io_dtype(np.random.default_rng(4242 + 2200).normal(0.0, 1.0, (1, 2200, w.d_v)), w.io)
+    assert d["q"].shape[1] == 2200
+    compare(run_gpu(d, dh, True), run_oracle(d, dh), "f32", "f32 T=2200")
+
+
 def test_unsupported_head_dim_raises():
     w, d, dh = case("small_f32", pairs=[(0, 0)], T=40, d_qk=272, d_v=64)
     with pytest.raises(binding.MlstmError):

@@ -208,29 +208,65 @@ def test_linear_attention_special_case():
     assert float(m.abs().max()) == 0.0
 
 
-@pytest.mark.parametrize("variant", ["fused", "segscan"])
-def test_7b_full_size_sampled(variant):
-    """The whole 7B-layer-shaped workload (B=8 H=8 T=4096 d_qk=256 d_v=512
-    chunk=64 bf16) in one launch; the oracle checks three sampled pairs
-    element by element, and every pair's final stabilizer is checked against
-    its closed form from the gates."""
+@pytest.fixture(scope="module")
+def prefill_7b():
+    """The 7B-layer-shaped workload (B=8 H=8 T=4096 d_qk=256 d_v=512, bf16)
+    and its oracle result over every pair."""
     w = I.workload("prefill_7b_bf16")
+    print("[case] 7b full size: inputs + oracle (64 pairs x 4096 tokens)", flush=True)
+    d = I.gen_prefill(w, threads=16)
+    ref = PT.run_oracle(d, threads=16)
+    return w, d, ref
+
+
+@pytest.mark.parametrize("variant", ["fused", "segscan"])
+def test_7b_full_size(prefill_7b, variant):
+    """The whole 7B-layer-shaped workload (chunk=64) in one call, in the
+    launch configuration the benchmark times (fused) and as a segment scan:
+    h of every token and the final (C, n, m) of every pair against the
+    oracle; every pair's final stabilizer also against its closed form."""
+    w, d, ref = prefill_7b
     print(f"[case] 7b full size, variant={variant}", flush=True)
-    d = I.gen_prefill(w)
     g = PT.cuda(d)
     shp = lambda t: t.reshape(w.B, w.H, *t.shape[1:])
     h, (C, n, m) = binding.fwd_chunkwise(*[shp(g[k]) for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")],
                                          chunk=w.chunk, variant=variant)
     torch.cuda.synchronize()
-    assert torch.isfinite(h).all() and torch.isfinite(C).all()
+    del g
     m_ref = PT.m_closed_form(d["i_pre"].double().numpy(), d["f_pre"].double().numpy())
     assert np.max(np.abs(PT.to_np(m).reshape(-1) - m_ref)) <= PT.TOL_M["bf16"]
-    sample = [(0, 0), (3, 5), (7, 7)]
-    idx = [b * w.H + hh for b, hh in sample]
-    sub = {k: (v[idx] if v is not None else None) for k, v in d.items()}
-    ref = PT.run_oracle(sub)
+    flat = lambda t: t.reshape(w.B * w.H, *t.shape[2:])
+    PT.compare_fwd((flat(h), flat(C), flat(n), flat(m)), ref, "bf16", f"7b full size {variant}, all 64 pairs")
+
+
+@pytest.mark.parametrize("variant", ["fused", "segscan"])
+def test_inplace_7b_heads_many_workgroups(variant):
+    """In place (C_T == C0, n_T == n0, m_T == m0) at the 7B heads with 4
+    value-column tiles per pair and 72 pairs (288 workgroups, more than the
+    compute units): the tiles that read n0/m0 while another one writes n_T/m_T
+    give bitwise the result of separate output buffers."""
+    w = I.workload("prefill_7b_bf16", B=9)
+    T = 200
+    d = PT.cuda(I.gen_prefill(w, T=T, threads=16))
+    wd = I.workload("decode_bf16")
+    C0, n0, m0 = (x.cuda().reshape(-1, *x.shape[2:])[: w.B * w.H] for x in I.gen_decode_state(wd, B=w.B + 1))
+    shp = lambda t: t.reshape(w.B, w.H, *t.shape[1:])
+    args = [shp(d[k]) for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")]
+    st = [shp(C0), shp(n0), shp(m0)]
+    h1, (C1, n1, m1) = binding.fwd_chunkwise(*args, *st, chunk=64, variant=variant)
+    Ci, ni, mi = (x.clone() for x in st)
+    h2, _ = binding.fwd_chunkwise(*args, Ci, ni, mi, chunk=64, variant=variant, C_T=Ci, n_T=ni, m_T=mi)
+    torch.cuda.synchronize()
+    for a, b, what in ((h1, h2, "h"), (C1, Ci, "C"), (n1, ni, "n"), (m1, mi, "m")):
+        assert torch.equal(a, b), (variant, what)
+    # and against the oracle on two pairs, one of them past the first 64
+    idx = [5, 70]
+    sub = {k: (v.reshape(w.B * w.H, *v.shape[2:])[idx].cpu() if v is not None else None)
+           for k, v in zip(("q", "k", "v", "i_pre", "f_pre", "o_pre"), args)}
+    sub.update(C0=C0[idx].cpu(), n0=n0[idx].cpu(), m0=m0[idx].cpu())
     flat = lambda t: t.reshape(w.B * w.H, *t.shape[2:])[idx]
-    PT.compare_fwd((flat(h), flat(C), flat(n), flat(m)), ref, "bf16", f"7b full, sampled pairs {sample}")
+    PT.compare_fwd((flat(h2), flat(Ci), flat(ni), flat(mi)), PT.run_oracle(sub), "bf16",
+                   f"in place 7b heads {variant}")
 
 
 @pytest.fixture(scope="module")

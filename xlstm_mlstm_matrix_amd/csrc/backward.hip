@@ -124,15 +124,12 @@ __device__ void chunk_gates(const float *ig, const float *fg, int t0, int T, flo
 // Tiles live in LDS in float32; the state, a, G* come from the workspace
 // through the caches.  Workspace layout: bwd_layout.
 
-#ifndef BWD_BVB
-#define BWD_BVB 128
-#endif
 // value columns per workgroup of the two scans (128 measured fastest when the
 // scans ran on the vector units: 64 and 32 re-read the K or Q tile more
 // often, 256 halves the workgroups), and their threads (eight wavefronts, each
 // holding two 16-row tiles of the block by two 64-column quads as MFMA
 // accumulators; rows up to 256)
-constexpr int NTA = 512, BVB = BWD_BVB, CG = BVB / 16, NTS = 64 * CG;
+constexpr int NTA = 512, BVB = 128, CG = BVB / 16, NTS = 64 * CG;
 
 // load rows t0 .. t0 + L - 1 of a [T, d] input as float32 into a [L][ld] tile
 // (zero past T)

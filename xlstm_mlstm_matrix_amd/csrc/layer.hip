@@ -204,11 +204,15 @@ mlstm_status_t mlstm_layer_fwd(const void *x, const void *W_q, const void *W_k, 
     LayerPlan p;
     mlstm_status_t st = layer_plan(B, T, d_model, H, d_qk, d_v, chunk, io, &p);
     if (st != MLSTM_OK) return st;
-    if (!all_aligned({x, W_q, W_k, W_v, W_o, W_i, W_f, b_q, b_k, b_v, b_o, b_i, b_f, workspace}))
+    // Every check of the cell call at the end runs here as well, before the
+    // first GEMM is enqueued: a rejected call enqueues nothing.
+    const int in0 = (C0 != nullptr) + (n0 != nullptr) + (m0 != nullptr);
+    const int out0 = (C_T != nullptr) + (n_T != nullptr) + (m_T != nullptr);
+    if ((in0 != 0 && in0 != 3) || (out0 != 0 && out0 != 3)) return MLSTM_ERR_STATE_ARGS;
+    if (!all_aligned({x, W_q, W_k, W_v, W_o, W_i, W_f, b_q, b_k, b_v, b_o, b_i, b_f, C0, n0, m0, h, C_T,
+                      n_T, m_T, workspace}))
         return MLSTM_ERR_ALIGN;
     if (!workspace || workspace_bytes < p.total) return MLSTM_ERR_WORKSPACE;
-    // the layer's own inputs must not overlap its outputs or the workspace;
-    // the cell call below checks the state and h against everything it sees
     const size_t es = p.es, D = (size_t)d_model;
     const Range ins[] = {rng(x, p.BT * D * es),           rng(W_q, (size_t)H * d_qk * D * es),
                          rng(W_k, (size_t)H * d_qk * D * es), rng(W_v, (size_t)H * d_v * D * es),
@@ -218,11 +222,26 @@ mlstm_status_t mlstm_layer_fwd(const void *x, const void *W_q, const void *W_k, 
                          rng(b_o, (size_t)H * d_v * 4),       rng(b_i, (size_t)H * 4),
                          rng(b_f, (size_t)H * 4)};
     const size_t nC = (size_t)H * B * d_qk * d_v, nn = (size_t)H * B * d_qk, nm = (size_t)H * B;
+    const Range st_in[] = {rng(C0, nC * 4), rng(n0, nn * 4), rng(m0, nm * 4)};
+    // written: h, the final state and the workspace
     const Range outs[] = {rng(h, p.nv * es), rng(C_T, nC * 4), rng(n_T, nn * 4), rng(m_T, nm * 4),
                           rng(workspace, p.total)};
-    for (const Range &i : ins)
-        for (const Range &o : outs)
+    constexpr int NO = sizeof(outs) / sizeof(outs[0]);
+    for (const Range &o : outs) {
+        for (const Range &i : ins)
             if (overlaps(i, o)) return MLSTM_ERR_ALIAS;
+    }
+    // each written buffer overlaps no other one; a final-state buffer may
+    // coincide exactly with its own initial-state buffer (in place) and
+    // overlaps no other initial-state buffer
+    for (int o = 0; o < NO; ++o) {
+        for (int o2 = o + 1; o2 < NO; ++o2)
+            if (overlaps(outs[o], outs[o2])) return MLSTM_ERR_ALIAS;
+        for (int i = 0; i < 3; ++i) {
+            const bool allowed = o == i + 1 && same(outs[o], st_in[i]);
+            if (overlaps(outs[o], st_in[i]) && !allowed) return MLSTM_ERR_ALIAS;
+        }
+    }
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return MLSTM_ERR_HIP;
