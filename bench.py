@@ -213,8 +213,12 @@ def bench_decode(torch, I, binding, warmup_passes=1, nsteps=None):
     ms = tm.ms / w.T
     # a second pass with an event around every step: the per-step median
     it = iter(range(w.T))
-    _, med = time_steps(torch, lambda: binding.step(*(steps[k][next(it)] for k in keys), C, n, m, h=h,
-                                                    C_out=C, n_out=n, m_out=m, workspace=ws), w.T)
+
+    def one_step():
+        t = next(it)
+        binding.step(*(steps[k][t] for k in keys), C, n, m, h=h, C_out=C, n_out=n, m_out=m, workspace=ws)
+
+    _, med = time_steps(torch, one_step, w.T)
     state_bytes, total_bytes = decode_work(w)
     log(f"decode: {ms:.4f} ms/step (median {med:.4f}), state {state_bytes / ms / 1e6:.0f} GB/s, "
         f"total {total_bytes / ms / 1e6:.0f} GB/s, {w.B / ms * 1e3:.3e} tokens/s")
