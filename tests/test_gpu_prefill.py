@@ -27,7 +27,7 @@ def test_small_f32():
     PT.compare_fwd(PT.run_gpu_fwd(d, w.chunk), PT.run_oracle(d), "f32", "small_f32")
 
 
-@pytest.mark.parametrize("T", [1, 15, 61, 64, 65, 200, 512])
+@pytest.mark.parametrize("T", [1, 15, 31, 32, 33, 61, 64, 65, 127, 128, 129, 200, 512])
 def test_7b_shapes_ragged(T):
     """d_qk=256, d_v=512 bf16 at lengths that end mid-chunk or inside one chunk."""
     w, d = case("prefill_7b_bf16", pairs=[(0, 0), (5, 3)], T=T)
