@@ -31,7 +31,9 @@
  *    caller owns every buffer; the library allocates nothing, keeps no state
  *    between calls and never synchronizes: work is enqueued on `stream`
  *    (a hipStream_t; NULL = the null stream) and the call returns at once.
- *    (Exception: mlstm_layer_fwd keeps a hipBLASLt handle per device.)
+ *    (Exceptions: mlstm_layer_fwd keeps a hipBLASLt handle per device, and
+ *    mlstm_step_noalloc works in a fixed scratch array that each device
+ *    holds for the life of the process.)
  *  - q, k, v, o_pre and h have the I/O dtype `io` (float32 or bfloat16);
  *    i_pre, f_pre and the state (C, n, m) are always float32.
  *  - Every pointer, workspace included, must be 16-byte aligned (the kernels
@@ -74,8 +76,12 @@ typedef enum {
     MLSTM_ERR_ALIAS = 6,       /* buffers overlap in a way the call does not allow */
     MLSTM_ERR_HIP = 7,         /* the HIP runtime reported an error */
     MLSTM_ERR_ALIGN = 8,       /* a pointer is not 16-byte aligned */
-    MLSTM_ERR_BLAS = 9         /* a hipBLASLt call failed (layer projections) */
+    MLSTM_ERR_BLAS = 9,        /* a hipBLASLt call failed (layer projections) */
+    MLSTM_ERR_SCRATCH = 10     /* the shape needs more than mlstm_step_noalloc's fixed scratch */
 } mlstm_status_t;
+
+/* Bytes of the fixed per-device scratch array of mlstm_step_noalloc. */
+#define MLSTM_STEP_NOALLOC_MAX_BYTES ((size_t)32 << 20)
 
 /* Kernel strategy of the chunkwise forward (the result is the same up to
  * rounding; only the schedule differs). */
@@ -201,6 +207,37 @@ mlstm_status_t mlstm_step(const void *q, const void *k, const void *v,
                           void *h, float *C_out, float *n_out, float *m_out,
                           int B, int H, int d_qk, int d_v, mlstm_dtype_t io,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * mlstm_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, checks, results and errors as mlstm_step given a
+ * workspace, except that the row split's workspace is a fixed scratch array
+ * inside the library, MLSTM_STEP_NOALLOC_MAX_BYTES per device, so the call
+ * allocates nothing (not even through another library).  The caller still
+ * passes every input and output.
+ *
+ *  - A shape whose workspace (mlstm_step_workspace_size) exceeds
+ *    MLSTM_STEP_NOALLOC_MAX_BYTES -> MLSTM_ERR_SCRATCH, nothing enqueued:
+ *    32 MiB holds the partial read-outs of 4064 cells at d_qk = 256,
+ *    d_v = 512 (B*H cells need B*H*4*(d_v+4)*4 bytes there).  A shape that
+ *    gains nothing from the split runs the one-workgroup kernel and uses
+ *    no scratch.
+ *  - The scratch belongs to the device of `stream` (the current device for
+ *    the null stream); its address there is looked up on the first call on
+ *    that device, with that device current (a failure -> MLSTM_ERR_HIP).
+ *  - Every call on one device shares that device's array and leaves its own
+ *    partial results in it; each call writes what it reads before reading
+ *    it, so no contents need clearing.  Calls that may run at the same time
+ *    on one device (different streams, or overlapping graphs) race: the
+ *    caller orders them.
+ */
+mlstm_status_t mlstm_step_noalloc(const void *q, const void *k, const void *v,
+                                  const float *i_pre, const float *f_pre, const void *o_pre,
+                                  const float *C_in, const float *n_in, const float *m_in,
+                                  void *h, float *C_out, float *n_out, float *m_out,
+                                  int B, int H, int d_qk, int d_v, mlstm_dtype_t io,
+                                  void *stream);
 
 /*
  * Gradients of a loss L with respect to every input of mlstm_fwd_chunkwise,

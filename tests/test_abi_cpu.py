@@ -37,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s+(mlstm_\w+)", out))
@@ -48,7 +48,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for s in range(10):
+    for s in range(11):
         assert B.status_string(s).startswith(B.STATUS[s])
     assert "unknown" in B.status_string(99)
     assert lib.mlstm_version().decode().startswith("mlstm-gfx950")
@@ -243,6 +243,35 @@ def test_step_workspace_validation(lib):
     assert call_step(a) == ALIAS
     a = step_args(**dims); a["ws"] = free(a) + 8; a["wsn"] = need
     assert call_step(a) == 8   # MLSTM_ERR_ALIGN
+
+
+def call_step_noalloc(a):
+    return B.lib().mlstm_step_noalloc(a["q"], a["k"], a["v"], a["i"], a["f"], a["o"], a["C"], a["n"],
+                                      a["m"], a["h"], a["Co"], a["no"], a["mo"], *a["dims"], None)
+
+
+def test_step_noalloc_validation(lib):
+    # the checks of mlstm_step, then the scratch limit, all before any HIP call
+    for key in ("q", "k", "v", "i", "f", "o", "h", "Co", "no", "mo"):
+        a = step_args(); a[key] = None
+        assert call_step_noalloc(a) == NULL, key
+    a = step_args(); a["dims"] = (0, 2, 64, 128, B.BF16)
+    assert call_step_noalloc(a) == SHAPE
+    a = step_args(); a["dims"] = (4, 2, 40, 128, B.BF16)
+    assert call_step_noalloc(a) == UNSUP
+    a = step_args(); a["n"] = None
+    assert call_step_noalloc(a) == STATE
+    a = step_args(); a["h"] = a["o"]
+    assert call_step_noalloc(a) == ALIAS
+    a = step_args(); a["q"] += 4
+    assert call_step_noalloc(a) == 8   # MLSTM_ERR_ALIGN
+    # the partials of 4064 cells of 256 x 512 fit in the 32 MiB scratch; of 4065 they do not
+    assert sws(4064, 1, 256, 512, B.BF16)[1] <= B.STEP_NOALLOC_MAX_BYTES < sws(4065, 1, 256, 512, B.BF16)[1]
+    a = step_args(B_=4065, H=1, dk=256, dv=512)
+    assert call_step_noalloc(a) == 10  # MLSTM_ERR_SCRATCH
+    a = step_args(B_=1000, H=5, dk=256, dv=512, state=False)
+    assert call_step_noalloc(a) == 10
+    assert "mlstm_step_noalloc" in B.status_string(10)
 
 
 def test_binding_refuses_cpu_tensors():

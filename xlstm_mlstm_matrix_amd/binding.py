@@ -18,7 +18,9 @@ F32, BF16 = 0, 1
 VARIANTS = {"auto": 0, "fused": 1, "segscan": 2}
 STATUS = {0: "MLSTM_OK", 1: "MLSTM_ERR_NULL", 2: "MLSTM_ERR_SHAPE", 3: "MLSTM_ERR_UNSUPPORTED",
           4: "MLSTM_ERR_STATE_ARGS", 5: "MLSTM_ERR_WORKSPACE", 6: "MLSTM_ERR_ALIAS",
-          7: "MLSTM_ERR_HIP", 8: "MLSTM_ERR_ALIGN", 9: "MLSTM_ERR_BLAS"}
+          7: "MLSTM_ERR_HIP", 8: "MLSTM_ERR_ALIGN", 9: "MLSTM_ERR_BLAS", 10: "MLSTM_ERR_SCRATCH"}
+# bytes of the fixed per-device scratch of mlstm_step_noalloc (MLSTM_STEP_NOALLOC_MAX_BYTES)
+STEP_NOALLOC_MAX_BYTES = 32 << 20
 
 # exported entry points and their C signatures (kept in step with include/mlstm.h)
 _vp, _fp, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
@@ -33,6 +35,7 @@ SIGNATURES = {
     "mlstm_fwd_chunkwise_variant": (_i, [_vp] * 13 + [_i] * 8 + [_vp, _sz, _vp]),
     "mlstm_step_workspace_size": (_i, [_i] * 5 + [ctypes.POINTER(_sz)]),
     "mlstm_step": (_i, [_vp] * 13 + [_i] * 5 + [_vp, _sz, _vp]),
+    "mlstm_step_noalloc": (_i, [_vp] * 13 + [_i] * 5 + [_vp]),
     "mlstm_bwd_chunkwise_workspace_size": (_i, [_i] * 7 + [ctypes.POINTER(_sz)]),
     "mlstm_bwd_chunkwise": (_i, [_vp] * 19 + [_i] * 7 + [_vp, _sz, _vp]),
     "mlstm_layer_fwd_workspace_size": (_i, [_i] * 8 + [ctypes.POINTER(_sz)]),
@@ -347,4 +350,37 @@ def step(q, k, v, i_pre, f_pre, o_pre, C=None, n=None, m=None, *, h=None, C_out=
         _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(o_pre),
         _ptr(C), _ptr(n), _ptr(m), _ptr(h), _ptr(C_out), _ptr(n_out), _ptr(m_out),
         B, H, dk, dv, _io(q), _ptr(workspace), ws_bytes, _stream(dev)))
+    return h, C_out, n_out, m_out
+
+
+def step_noalloc(q, k, v, i_pre, f_pre, o_pre, C=None, n=None, m=None, *, h=None, C_out=None,
+                 n_out=None, m_out=None, inplace: bool = True):
+    """``step`` through mlstm_step_noalloc: the row split's workspace is the
+    library's fixed per-device scratch (nothing is allocated by the library;
+    outputs not given are allocated here, by torch, before the call).  Same
+    arguments and result as ``step`` with ``split=True``."""
+    import torch
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    io_t = q.dtype
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("o_pre", o_pre)):
+        _req(t, name, io_t, dev)
+    for name, t in (("i_pre", i_pre), ("f_pre", f_pre), ("C", C), ("n", n), ("m", m)):
+        _req(t, name, torch.float32, dev)
+    if h is None:
+        h = torch.empty((B, H, dv), dtype=io_t, device=dev)
+    if C_out is None:
+        if inplace and C is not None:
+            C_out, n_out, m_out = C, n, m
+        else:
+            C_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+            n_out = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+            m_out = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _check(lib().mlstm_step_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(o_pre),
+        _ptr(C), _ptr(n), _ptr(m), _ptr(h), _ptr(C_out), _ptr(n_out), _ptr(m_out),
+        B, H, dk, dv, _io(q), _stream(dev)))
     return h, C_out, n_out, m_out

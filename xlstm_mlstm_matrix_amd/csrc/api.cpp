@@ -2,7 +2,9 @@
 //
 // Every check here runs on the host before any device work, so an invalid
 // call enqueues nothing and touches no device.  The library allocates
-// nothing and never synchronizes; launches go to the caller's stream.
+// nothing and never synchronizes; launches go to the caller's stream.  (The
+// one piece of device memory it owns is the fixed scratch array of
+// mlstm_step_noalloc, part of its code object, in step.hip.)
 #include "mlstm.h"
 
 #include <stdint.h>
@@ -25,7 +27,10 @@ const char *kStatus[] = {
     "MLSTM_ERR_HIP: the HIP runtime reported an error",
     "MLSTM_ERR_ALIGN: a pointer is not 16-byte aligned",
     "MLSTM_ERR_BLAS: a hipBLASLt call failed",
+    "MLSTM_ERR_SCRATCH: the shape needs more than the fixed per-device scratch of "
+    "mlstm_step_noalloc (MLSTM_STEP_NOALLOC_MAX_BYTES); use mlstm_step with a workspace",
 };
+static_assert(MLSTM_STEP_NOALLOC_MAX_BYTES == kStepScratchBytes, "scratch size out of step");
 
 constexpr int kMaxDk = 256, kMaxDv = 512;
 constexpr int kTargetWorkgroups = 256;  // one workgroup per compute unit of an MI355X
@@ -248,11 +253,19 @@ mlstm_status_t mlstm_step_workspace_size(int B, int H, int d_qk, int d_v, mlstm_
     return MLSTM_OK;
 }
 
-mlstm_status_t mlstm_step(const void *q, const void *k, const void *v, const float *i_pre,
-                          const float *f_pre, const void *o_pre, const float *C_in,
-                          const float *n_in, const float *m_in, void *h, float *C_out, float *n_out,
-                          float *m_out, int B, int H, int d_qk, int d_v, mlstm_dtype_t io,
-                          void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// mlstm_step and mlstm_step_noalloc: the same checks and launches; the second
+// takes the row split's workspace from the library's fixed per-device scratch
+// (after every host-side check, so an invalid call touches no device).
+mlstm_status_t step_call(const void *q, const void *k, const void *v, const float *i_pre,
+                         const float *f_pre, const void *o_pre, const float *C_in,
+                         const float *n_in, const float *m_in, void *h, float *C_out,
+                         float *n_out, float *m_out, int B, int H, int d_qk, int d_v,
+                         mlstm_dtype_t io, void *workspace, size_t workspace_bytes,
+                         bool fixed_scratch, void *stream) {
     if (!q || !k || !v || !i_pre || !f_pre || !o_pre || !h || !C_out || !n_out || !m_out)
         return MLSTM_ERR_NULL;
     if (B <= 0 || H <= 0 || d_qk <= 0 || d_v <= 0) return MLSTM_ERR_SHAPE;
@@ -292,6 +305,19 @@ mlstm_status_t mlstm_step(const void *q, const void *k, const void *v, const flo
     // with a workspace, large memories are split into row blocks (one
     // workgroup each); without one, one workgroup streams each pair
     const size_t need = step_workspace_bytes(BH, d_qk, d_v);
+    if (fixed_scratch) {
+        if (need > kStepScratchBytes) return MLSTM_ERR_SCRATCH;
+        workspace = nullptr;
+        if (need > 0) {
+            int dev = 0;
+            float *p = nullptr;
+            if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) != hipSuccess ||
+                step_scratch(dev, &p) != hipSuccess)
+                return MLSTM_ERR_HIP;
+            workspace = p;
+            workspace_bytes = kStepScratchBytes;
+        }
+    }
     if (workspace && need > 0) {
         if (workspace_bytes < need) return MLSTM_ERR_WORKSPACE;
         const Range rws = rng(workspace, need);
@@ -306,6 +332,28 @@ mlstm_status_t mlstm_step(const void *q, const void *k, const void *v, const flo
     }
     hipError_t e = launch_step(a, io == MLSTM_BF16, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MLSTM_OK : MLSTM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+mlstm_status_t mlstm_step(const void *q, const void *k, const void *v, const float *i_pre,
+                          const float *f_pre, const void *o_pre, const float *C_in,
+                          const float *n_in, const float *m_in, void *h, float *C_out, float *n_out,
+                          float *m_out, int B, int H, int d_qk, int d_v, mlstm_dtype_t io,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    return step_call(q, k, v, i_pre, f_pre, o_pre, C_in, n_in, m_in, h, C_out, n_out, m_out, B, H,
+                     d_qk, d_v, io, workspace, workspace_bytes, false, stream);
+}
+
+mlstm_status_t mlstm_step_noalloc(const void *q, const void *k, const void *v, const float *i_pre,
+                                  const float *f_pre, const void *o_pre, const float *C_in,
+                                  const float *n_in, const float *m_in, void *h, float *C_out,
+                                  float *n_out, float *m_out, int B, int H, int d_qk, int d_v,
+                                  mlstm_dtype_t io, void *stream) {
+    return step_call(q, k, v, i_pre, f_pre, o_pre, C_in, n_in, m_in, h, C_out, n_out, m_out, B, H,
+                     d_qk, d_v, io, nullptr, 0, true, stream);
 }
 
 // ---- backward

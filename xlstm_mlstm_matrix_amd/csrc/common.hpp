@@ -118,6 +118,10 @@ hipError_t launch_step(const StepArgs &a, int io_bf16, hipStream_t s);
 // rows per block of the step's row split and the workspace it needs (0: no split)
 int step_rows_per_block(int dk, int dv);
 size_t step_workspace_bytes(size_t BH, int dk, int dv);
+// size of the fixed per-device scratch of the no-allocation step, and its
+// address on device `dev` (looked up once per device, that device current)
+constexpr size_t kStepScratchBytes = (size_t)32 << 20;
+hipError_t step_scratch(int dev, float **out);
 hipError_t launch_fused(const FwdArgs &a, int io_bf16, int chunk, int state_only, hipStream_t s);
 hipError_t launch_seg_combine(const FwdArgs &a, float *ws, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs &a, int io_bf16, hipStream_t s);

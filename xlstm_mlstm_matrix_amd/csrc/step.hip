@@ -30,6 +30,8 @@
 //    overwritten only after every block has read it.  (Handing the sum to the
 //    last block through an atomic counter needs a device-scope release per
 //    block, which writes back the whole L2 on this chip: 15x slower.)
+#include <mutex>
+
 #include "common.hpp"
 
 namespace mlstm {
@@ -290,6 +292,43 @@ size_t step_workspace_bytes(size_t BH, int dk, int dv) {
     const int rows = step_rows_per_block(dk, dv);
     const size_t nb = ((size_t)dk + rows - 1) / rows;
     return nb < 2 ? 0 : BH * nb * (size_t)(dv + 4) * 4;
+}
+
+// Fixed scratch of the entry point that allocates nothing: the row split's
+// partial read-outs, in a file-scope array of the library's code object (each
+// device holds its own copy, at its own address, until the process ends).
+// Host code never passes the array's name to a kernel (on the host it is only
+// a stand-in for the symbol): it looks up each device's address once, with
+// that device current, and passes that.  Every call on one device shares the
+// array, so calls that may run at the same time on one device race.  The
+// partials are written in full before they are read, so nothing needs
+// clearing between calls.
+static __device__ __align__(256) float scratch[kStepScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t step_scratch(int dev, float **out) {
+    static std::mutex mu;
+    static float *addr[kMaxDevices] = {};
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (e == hipSuccess) e = back;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = static_cast<float *>(p);
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_step(const StepArgs &a, int io_bf16, hipStream_t s) {
