@@ -18,21 +18,22 @@
 //    columns [32 s, 32 s + 32) in registers (MFMA accumulator layout, float32,
 //    for the whole sequence).  Per chunk they compute the inter-chunk
 //    read-out C'^T Q^T (C' split into a bf16 high part and remainder, two
-//    MFMAs) and q.n' (MFMA with n' as a broadcast operand, token tile s) and
-//    hand them to the intra wavefronts through LDS, then update C' and n'
-//    with MFMAs.  They issue no memory instructions (a wavefront whose
-//    vector-memory queue is full stalls at issue);
+//    MFMAs) and hand it to the intra wavefronts through LDS, then update C'
+//    and n' with one straight run of MFMAs.  They issue no memory
+//    instructions (a wavefront whose vector-memory queue is full stalls at
+//    issue);
 //  * intra wavefronts (4..7): wavefront 4 + t owns token tile t (16 tokens)
 //    for all 128 columns: its causal S tiles (MFMA), P in registers (the S
 //    accumulator layout is, up to a permutation of the MFMA k index that the
-//    V^T fragment follows too, the B operand of V^T P^T), V^T P^T, the
-//    normaliser, the output gate and the bf16 h stores.  They copy the Q, K
-//    and V tiles.
+//    V^T fragment follows too, the B operand of V^T P^T), V^T P^T, q.n' (MFMA
+//    with n' as a broadcast operand), the normaliser, the output gate and
+//    the bf16 h stores.  They copy the Q, K and V tiles.
 // Two phases per chunk, separated by workgroup barriers:
-//   phase 1: state: read-out and q.n' of chunk c -> LDS
-//            intra: copy V(c), load o~, gates; S, P of chunk c; one of them
-//                   prepares the gate table of chunk c+1; copy K(c+1)
-//   phase 2: state: C', n' update with chunk c
+//   phase 1: state: read-out of chunk c -> LDS
+//            intra: copy V(c), load o~, gates; S, q.n', P of chunk c; one of
+//                   them prepares the gate table of chunk c+1; copy K(c+1)
+//   phase 2: state: C', n' update with chunk c (n' double buffered: the
+//                   intra wavefronts read the other one in phase 1)
 //            intra: copy Q(c+1); V^T P^T on top of the read-out, h of chunk c
 // No wavefront has a copy in flight when it uses a plain load (the compiler
 // counts loads and copies together and would wait for both); the barriers
@@ -54,8 +55,8 @@ struct WsCfg {
     static constexpr int QG = DKP / 8, VG = BV / 8;   // 16-byte granules per row
     static constexpr int GTF = 6 * L + 8;             // gate table floats (as Bf16Cfg)
     static constexpr size_t LDS_BYTES = 2 * (3 * (size_t)L * DKP + (size_t)L * BV) +
-                                        16 * (size_t)NT * NCT * 64 + 4 * (2 * (size_t)GTF + DKP) +
-                                        2 * 2 * (size_t)DKP;
+                                        16 * (size_t)NT * NCT * 64 + 4 * (2 * (size_t)GTF + 2 * (size_t)DKP) +
+                                        2 * 2 * 2 * (size_t)DKP;
     static_assert(NT == NW - NSW, "one token tile per intra wavefront");
     static_assert(NAT % 4 == 0, "n' tiles spread over the state wavefronts");
     static_assert(QG >= 8, "swizzle needs 8 granules per row");
@@ -84,6 +85,11 @@ __device__ __forceinline__ int swzt8(int r) {
 
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// word 3 of the buffer descriptors of the tile copies, output-gate loads and
+// h stores (32-bit data format; raw addressing, range-checked)
+constexpr int kWsBuf = 0x00020000;
 
 // Packed bf16 pairs (-1, 0) and (0, -1), the operands that pick one high
 // part out of a pair in split8_pk.  They are built in scalar registers from
@@ -116,6 +122,24 @@ __device__ __forceinline__ void split8_pk(const float *x, const SplitMasks &m, b
     }
     hi = bf16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
     lo = bf16x8{l[0][0], l[0][1], l[1][0], l[1][1], l[2][0], l[2][1], l[3][0], l[3][1]};
+}
+
+// One of four fragments, chosen by a wavefront-uniform index given as bit
+// masks m0, m1 (each 0 or all ones): two levels of bitwise selects, twelve
+// VALU instructions.  Masks rather than booleans, because a select on a
+// uniform boolean is turned into a branch, which splits the MFMA run.
+__device__ __forceinline__ bf16x8 pick4(const bf16x8 &f0, const bf16x8 &f1, const bf16x8 &f2, const bf16x8 &f3,
+                                        unsigned m0, unsigned m1) {
+    const u32x4 a0 = __builtin_bit_cast(u32x4, f0), a1 = __builtin_bit_cast(u32x4, f1);
+    const u32x4 a2 = __builtin_bit_cast(u32x4, f2), a3 = __builtin_bit_cast(u32x4, f3);
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const unsigned lo = (m0 & a1[i]) | (~m0 & a0[i]);
+        const unsigned hi = (m0 & a3[i]) | (~m0 & a2[i]);
+        r[i] = (m1 & hi) | (~m1 & lo);
+    }
+    return __builtin_bit_cast(bf16x8, r);
 }
 
 // Swizzle of a tile with GPR granules per row (Q, K and V tiles alike).
@@ -160,8 +184,10 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     // gate tables (double buffered): u, r, s, floor, w [L] floats, w as bf16
     // high/low pairs [L], then scalars (m after, decay, sum f~)
     __shared__ __attribute__((aligned(16))) float gt[2][GTF];
-    __shared__ __attribute__((aligned(16))) float nsh[DKP];     // n' (true scale)
-    __shared__ __attribute__((aligned(16))) bf16 nhl[2][DKP];   // n' as bf16 high part, remainder
+    // n' (true scale) and as bf16 high part and remainder, double buffered
+    // (buffer c & 1 holds n' before chunk c)
+    __shared__ __attribute__((aligned(16))) float nsh[2][DKP];
+    __shared__ __attribute__((aligned(16))) bf16 nhl[2][2][DKP];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -233,10 +259,10 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                 Cr[at][bt][r] = (is_state && Cs) ? Cs[(size_t)crow(at, r) * dv + scol + 4 * bt] : 0.0f;
     for (int e = tid; e < DKP; e += Cfg::NTH) {
         const float x = ns ? ns[e] : 0.0f;
-        nsh[e] = x;
+        nsh[0][e] = x;
         const bf16 hi = (bf16)x;
-        nhl[0][e] = hi;
-        nhl[1][e] = (bf16)(x - (float)hi);
+        nhl[0][0][e] = hi;
+        nhl[0][1][e] = (bf16)(x - (float)hi);
     }
     float sigma = 1.0f;  // C' is held divided by sigma (state wavefronts)
 
@@ -244,55 +270,41 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     // ---- global -> LDS copies by the intra wavefronts.  Physical granule g
     // of a tile is (row, p) with p = g % gpr holding logical granule
     // p ^ swz(row); instruction k of wavefront s fills granules
-    // [(k NSW + s) 64, +64), rows k RPI + const.  Rows past the segment end
-    // are clamped to its last row (finite data; their gates zero them out).
-    // copy_part issues instruction k of a tile copy, copy_tile all of them.
-    // gpr_c: granules per row of the tile (its swizzle follows from it).
-    auto copy_part = [&](bf16 *dst, const bf16 *src, int ld, auto gpr_c, int tc, int k) {
-        constexpr unsigned GPR = decltype(gpr_c)::value;
-        constexpr unsigned RPI = NSW * 64 / GPR;
-        static_assert((L * GPR) % (NSW * 64) == 0 && RPI % 8 == 0, "copy shape");
-        unsigned ln = lane;
-        asm volatile("" : "+v"(ln));
-        const unsigned pgr = (unsigned)s * 64u + ln;
-        const unsigned row = k * RPI + pgr / GPR;
-        const unsigned gl = (pgr % GPR) ^ (unsigned)tswz<GPR>((int)row);
-        const unsigned rc = min(row, (unsigned)(t_end - 1 - tc));  // tc < t_end
-        __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)tc * ld + (rc * (unsigned)ld + gl * 8u)),
-                                         (lds_void *)(dst + (k * NSW + s) * 64 * 8), 16, 0, 0);
-    };
-    // Whole chunks: the per-lane part of instruction k's source offset is
-    // off[k % 2] plus a uniform (k - k % 2) RPI rows (the swizzle repeats
-    // every 16 rows, and 2 RPI is a multiple of 16), so a copy is a scalar
-    // base plus a 32-bit lane offset.  copy_offsets fills off[] once.
+    // [(k NSW + s) 64, +64), rows k RPI + const.  The per-lane part of
+    // instruction k's source offset is off[k % 2] (bytes; the swizzle repeats
+    // every 16 rows and 2 RPI is a multiple of 16) from a base (k - k % 2) RPI
+    // rows further, so each pair of instructions reads through one buffer
+    // descriptor (scalar registers: no per-lane 64-bit address arithmetic)
+    // whose range ends at the segment's last row.  Rows past it read as zero
+    // (finite; their gates zero them out).  The whole offset is the per-lane
+    // one: the range check covers it.  gpr_c: granules per row of the tile
+    // (its swizzle follows from it).
     auto copy_offsets = [&](auto gpr_c, int ld, unsigned *off) {
         constexpr unsigned GPR = decltype(gpr_c)::value;
         constexpr unsigned RPI = NSW * 64 / GPR;
-        static_assert((2 * RPI) % 16 == 0, "swizzle period");
+        static_assert((L * GPR) % (NSW * 64) == 0 && (2 * RPI) % 16 == 0, "copy shape, swizzle period");
         const unsigned pgr = (unsigned)s * 64u + (unsigned)lane;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const unsigned row = k * RPI + pgr / GPR;
-            off[k] = row * (unsigned)ld + ((pgr % GPR) ^ (unsigned)tswz<GPR>((int)row)) * 8u;
+            off[k] = 2u * (row * (unsigned)ld + ((pgr % GPR) ^ (unsigned)tswz<GPR>((int)row)) * 8u);
         }
     };
     auto copy_tile = [&](bf16 *dst, const bf16 *src, int ld, auto gpr_c, int tc, const unsigned *off) {
         constexpr int GPR = decltype(gpr_c)::value;
         constexpr int NI = L * GPR / (NSW * 64), RPI = NSW * 64 / GPR;
-        if (tc + L <= t_end) {
-            const bf16 *base = src + (size_t)tc * ld;
+        static_assert(NI % 2 == 0, "instructions in pairs");
 #pragma unroll
-            for (int k = 0; k < NI; ++k) {
-                // opaque per use: the compiler would otherwise hoist one 64-bit
-                // address per instruction out of the chunk loop
-                unsigned o = off[k & 1];
-                asm volatile("" : "+v"(o));
-                __builtin_amdgcn_global_load_lds((const void *)(base + (size_t)((k & ~1) * RPI) * ld + o),
-                                                 (lds_void *)(dst + (k * NSW + s) * 64 * 8), 16, 0, 0);
-            }
-        } else {
+        for (int k = 0; k < NI; k += 2) {
+            const int r0 = tc + k * RPI;
+            // (uniform; readfirstlane keeps the clamp's result in a scalar
+            // register, which the descriptor needs)
+            const int nb = __builtin_amdgcn_readfirstlane(max(0, min(2 * RPI, t_end - r0)) * ld * 2);
+            const auto rs = __builtin_amdgcn_make_buffer_rsrc((void *)(src + (size_t)r0 * ld), 0, nb, kWsBuf);
 #pragma unroll
-            for (int k = 0; k < NI; ++k) copy_part(dst, src, ld, gpr_c, tc, k);
+            for (int j = 0; j < 2; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + ((k + j) * NSW + s) * 64 * 8), 16,
+                                                         off[j], 0, 0, 0);
         }
     };
     static_assert(L * QG / (NSW * 64) == NKS, "one K or Q copy instruction per d_qk k-step");
@@ -369,12 +381,12 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     if (is_state) {
         // ========================= state wavefronts =========================
         const SplitMasks smask = split_masks();
-        // C'/sigma' += K^T ((w/sigma') (x) V) with sigma' = sigma * decay, n'
-        // likewise (true scale): the update with the chunk whose K and V tiles
-        // and gate table are given
-        auto update = [&](const bf16 *K, const bf16 *Vt, const float *G, float s_last) {
-                // ---- phase 2: C'/sigma' += K^T ((w/sigma') (x) V), sigma' =
-                // sigma * decay; n' likewise (true scale)
+        // C'/sigma' += K^T ((w/sigma') (x) V) with sigma' = sigma * decay, and
+        // n' (true scale) from buffer nb into nb ^ 1: the update with the chunk
+        // whose K and V tiles and gate table are given.  The loop over the row
+        // tiles of C' is one straight run of MFMAs: n' rides along without a
+        // branch (a branch per row tile doubles the update's time).
+        auto update = [&](const bf16 *K, const bf16 *Vt, const float *G, float s_last, int nb) {
                 sigma *= s_last;
                 if (sigma < kRenorm) {  // uniform: fold sigma back into the held state
     #pragma unroll
@@ -400,9 +412,20 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                     return cat8(tr_read(rowblock + kb0 + h + ((g ^ kx0) << 3)),
                                 tr_read(rowblock + kb1 + h + ((g ^ kx1) << 3)));
                 };
-                f32x4 nacc[NAT / 4];
+                // n' of row tiles s + 4 x: the old value (read now, used at the
+                // end), K^T w as MFMAs with w's high part and remainder in every
+                // column of the B operand (every lane gets K^T w for its rows);
+                // the row tile is picked from the last four fragments by selects
+                // on the wavefront index
+                unsigned sm0 = 0u - (unsigned)(s & 1), sm1 = 0u - (unsigned)((s >> 1) & 1);
+                asm volatile("" : "+s"(sm0), "+s"(sm1));
+                f32x4 nold[NAT / 4], nacc_h[NAT / 4], nacc_l[NAT / 4];
     #pragma unroll
-                for (int x = 0; x < NAT / 4; ++x) nacc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int x = 0; x < NAT / 4; ++x) {
+                    nold[x] = *reinterpret_cast<const f32x4 *>(&nsh[nb][crow(s + 4 * x, 0)]);
+                    nacc_h[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    nacc_l[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
     #pragma unroll
                 for (int js = 0; js < L / 32; ++js) {
                     const bf16 *k0 = K + 32 * js * DKP;
@@ -425,45 +448,46 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     #pragma unroll
                         for (int e = 0; e < 8; ++e) bw[bt][e] = (bf16)((float)vv[e] * w8[e]);
                     }
-                    // w (hi, lo) in every column of the operand: every lane gets K^T w
                     const bf16 *W2 = reinterpret_cast<const bf16 *>(&G[5 * LP]);
                     const bf16x8 bnh = *reinterpret_cast<const bf16x8 *>(W2 + 32 * js + 8 * g4);
                     const bf16x8 bnl = *reinterpret_cast<const bf16x8 *>(W2 + LP + 32 * js + 8 * g4);
-                    // K^T fragments fetched two row tiles ahead (ring of three)
-                    constexpr int AHEAD = 2;
-                    bf16x8 ak[AHEAD + 1];
+                    // K^T fragments fetched four row tiles ahead (the reads'
+                    // latency under load is several MFMA pairs), in a ring of
+                    // eight that still holds a group of four when it completes
+                    constexpr int AHEAD = 4;
+                    bf16x8 ak[8];
     #pragma unroll
                     for (int u = 0; u < AHEAD; ++u) ak[u] = kt_frag(k0, u);
     #pragma unroll
                     for (int at = 0; at < NAT; ++at) {
                         __builtin_amdgcn_sched_barrier(0);
-                        if (at + AHEAD < NAT) ak[(at + AHEAD) % (AHEAD + 1)] = kt_frag(k0, at + AHEAD);
-                        const bf16x8 &a0 = ak[at % (AHEAD + 1)];
+                        if (at + AHEAD < NAT) ak[(at + AHEAD) & 7] = kt_frag(k0, at + AHEAD);
+                        const bf16x8 &a0 = ak[at & 7];
     #pragma unroll
                         for (int bt = 0; bt < 2; ++bt) Cr[at][bt] = mfma(a0, bw[bt], Cr[at][bt]);
-                        if ((at & 3) == s) {
-                            nacc[at >> 2] = mfma(a0, bnh, nacc[at >> 2]);
-                            nacc[at >> 2] = mfma(a0, bnl, nacc[at >> 2]);
+                        if ((at & 3) == 3) {  // compile-time: the group at - 3 .. at is complete
+                            const bf16x8 fn = pick4(ak[(at - 3) & 7], ak[(at - 2) & 7], ak[(at - 1) & 7], a0, sm0, sm1);
+                            nacc_h[at >> 2] = mfma(fn, bnh, nacc_h[at >> 2]);
+                            nacc_l[at >> 2] = mfma(fn, bnl, nacc_l[at >> 2]);
                         }
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                // n' <- decay n' + K^T w for row tiles s + 4x (read after barrier Y)
+                // n' <- decay n' + K^T w into buffer nb ^ 1 (read after barrier Y)
                 if (l16 == 0) {
     #pragma unroll
                     for (int x = 0; x < NAT / 4; ++x) {
                         const int r0 = crow(s + 4 * x, 0);
-                        f32x4 *np = reinterpret_cast<f32x4 *>(&nsh[r0]);
-                        const f32x4 nn = *np * s_last + nacc[x];
-                        *np = nn;
+                        const f32x4 nn = nold[x] * s_last + (nacc_h[x] + nacc_l[x]);
+                        *reinterpret_cast<f32x4 *>(&nsh[nb ^ 1][r0]) = nn;
                         bf16x4 hi, lo;
     #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             hi[r] = (bf16)nn[r];
                             lo[r] = (bf16)(nn[r] - (float)hi[r]);
                         }
-                        *reinterpret_cast<bf16x4 *>(&nhl[0][r0]) = hi;
-                        *reinterpret_cast<bf16x4 *>(&nhl[1][r0]) = lo;
+                        *reinterpret_cast<bf16x4 *>(&nhl[nb ^ 1][0][r0]) = hi;
+                        *reinterpret_cast<bf16x4 *>(&nhl[nb ^ 1][1][r0]) = lo;
                     }
                 }
         };
@@ -474,7 +498,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                 const float *G = gt[c & 1];
                 const float m_next = G[6 * LP + 0], s_last = G[6 * LP + 1];
                 g_total += G[6 * LP + 2];
-                update(Ks[c & 1], vbuf(c), G, s_last);
+                update(Ks[c & 1], vbuf(c), G, s_last, c & 1);
                 m_prev = m_next;
                 role_sync<63>();  // K(c+1), V(c+1), gates of c+1 landed; K(c), V(c) free
             }
@@ -483,7 +507,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             const float *G = gt[c & 1];
             const float m_next = G[6 * LP + 0], s_last = G[6 * LP + 1];
 
-            // ---- phase 1: read-out O^T = C'^T Q^T and q.n'
+            // ---- phase 1: read-out O^T = C'^T Q^T
             {
                 f32x4 Ot[2][NT];
 #pragma unroll
@@ -528,9 +552,9 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             }
             role_sync<63>();  // (X) read-out in LDS; V(c) landed; Q(c) free
 
-            update(Ks[c & 1], Vs, G, s_last);
+            update(Ks[c & 1], Vs, G, s_last, c & 1);
             m_prev = m_next;
-            role_sync<63>();  // (Y) Q(c+1), K(c+1) landed; n' visible; V(c), Xch, q.n' free
+            role_sync<63>();  // (Y) Q(c+1), K(c+1) landed; n' after c written; V(c), Xch free
         }
 
         // ---- state out (n' and m from wavefront 0 of column block 0): the
@@ -556,7 +580,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                     for (int r = 0; r < 4; ++r)
                         Cdst[(size_t)crow(at, r) * dv + scol + 4 * bt] = Cr[at][bt][r] * sigma;
             if (tile == 0 && wave == 0) {
-                for (int e = lane; e < dk; e += 64) ndst[e] = nsh[e];
+                for (int e = lane; e < dk; e += 64) ndst[e] = nsh[nchunks & 1][e];
                 if (lane == 0) mdst[0] = m_prev;
             }
         }
@@ -608,13 +632,15 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             // ---- phase 1: copy V(c); S, P of this token tile; next gate
             // table; copy K(c+1)
             copy_tile(Vs, vg, dv, VGc{}, tc, vo);
-            uint4 orw[NHS];  // output-gate inputs: value columns 32 m + 8 g4 .. +8
-            {
-                const int t = min(tc + irow, t_end - 1);
+            // this chunk's rows of o~ and h: buffer descriptors whose range ends
+            // at the segment's last row (o~ past it reads as zero, h past it is
+            // not written)
+            const int nbo = __builtin_amdgcn_readfirstlane(min(L, t_end - tc) * dv * 2);
+            const auto ro = __builtin_amdgcn_make_buffer_rsrc((void *)(og + (size_t)tc * dv), 0, nbo, kWsBuf);
+            u32x4 orw[NHS];  // output-gate inputs: value columns 32 m + 8 g4 .. +8
 #pragma unroll
-                for (int m = 0; m < NHS; ++m)
-                    orw[m] = *reinterpret_cast<const uint4 *>(og + (size_t)t * dv + 32 * m + 8 * g4);
-            }
+            for (int m = 0; m < NHS; ++m)
+                orw[m] = __builtin_amdgcn_raw_buffer_load_b128(ro, 2u * (unsigned)(irow * dv + 32 * m + 8 * g4), 0, 0);
             if (more && wave == GW) load_gates(c + 1);
             // S^T tiles (jt, it) for jt <= it, k-step outermost so each Q
             // fragment serves all of them; each K fragment is refilled for the
@@ -634,8 +660,8 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             for (int ks = 0; ks < NKS; ++ks) {
                 bf16x8 fqn;
                 if (ks + 1 < NKS) fqn = qk_frag(qrow, ks + 1);
-                const bf16x8 nh = *reinterpret_cast<const bf16x8 *>(&nhl[0][32 * ks + 8 * g4]);
-                const bf16x8 nl = *reinterpret_cast<const bf16x8 *>(&nhl[1][32 * ks + 8 * g4]);
+                const bf16x8 nh = *reinterpret_cast<const bf16x8 *>(&nhl[c & 1][0][32 * ks + 8 * g4]);
+                const bf16x8 nl = *reinterpret_cast<const bf16x8 *>(&nhl[c & 1][1][32 * ks + 8 * g4]);
 #pragma unroll
                 for (int jt = 0; jt < NT; ++jt) {
                     if (jt <= it) {
@@ -676,7 +702,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             // waiting for them later, together with the copies)
 #pragma unroll
             for (int m = 0; m < NHS; ++m)
-                asm volatile("" : "+v"(orw[m].x), "+v"(orw[m].y), "+v"(orw[m].z), "+v"(orw[m].w));
+                asm volatile("" : "+v"(orw[m]));
             if (more) copy_tile(Ks[(c + 1) & 1], kg, DKP, QGc{}, tc + L, qko);
             // (X) V(c) landed (only the K copy may stay in flight)
             if (more)
@@ -714,21 +740,19 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             const int irow2 = 16 * it + (ln2 & 15);
             const float den = G[2 * LP + irow2] * qn + rowsum;
             const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), G[3 * LP + irow2]));
-            const int t = tc + irow2;
-            if (t < t_end) {
+            const auto rh = __builtin_amdgcn_make_buffer_rsrc((void *)(hg + (size_t)tc * dv), 0, nbo, kWsBuf);
 #pragma unroll
-                for (int m = 0; m < NHS; ++m) {
-                    const unsigned ow[4] = {orw[m].x, orw[m].y, orw[m].z, orw[m].w};
-                    bf16x8 hv;
+            for (int m = 0; m < NHS; ++m) {
+                bf16x8 hv;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const unsigned u = ow[e >> 1];
-                        const float ox = __uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16));
-                        const float a = acc[2 * m + (e >> 2)][e & 3];
-                        hv[e] = (bf16)(a * inv * __builtin_amdgcn_rcpf(1.0f + exp_e(-ox)));
-                    }
-                    *reinterpret_cast<bf16x8 *>(hg + (size_t)t * dv + 32 * m + 8 * g4) = hv;
+                for (int e = 0; e < 8; ++e) {
+                    const unsigned u = orw[m][e >> 1];
+                    const float ox = __uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16));
+                    const float a = acc[2 * m + (e >> 2)][e & 3];
+                    hv[e] = (bf16)(a * inv * __builtin_amdgcn_rcpf(1.0f + exp_e(-ox)));
                 }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hv), rh,
+                                                       2u * (unsigned)(irow2 * dv + 32 * m + 8 * g4), 0, 0);
             }
             // (Y) K(c+1), Q(c+1) landed (only this chunk's NHS h stores may stay in flight)
             if (more)
