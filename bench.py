@@ -497,12 +497,13 @@ def main():
                                              max(2, args.warmup // 20))
         rec["layer"] = {
             "workload": "mLSTM layer forward B=8 T=4096 d_model=4096 H=8 d_qk=256 d_v=512 chunk=64 bf16: "
-                        "per-head projections (hipBLASLt) + gate bias + chunkwise cell",
+                        "all-heads projections (hipBLASLt) + gate bias + chunkwise cell on strided rows",
             "ms_per_step": msl_, "tokens_per_s": wl.B * wl.T / msl_ * 1e3,
             "roofline": {"bound": "mfma", "achieved": (projf + cellf) / msl_ / 1e9,
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": (projf + cellf) / msl_ / 1e9 / PEAK_BF16_TFLOPS, "traffic": None,
-                         "kernel": "hipBLASLt GEMMs (4 per head + 2 gate) + gate_bias_kernel + mlstm_ws_kernel",
+                         "kernel": "hipBLASLt GEMMs (q, k, v, o~ over all heads + one gate GEMM) + "
+                                   "gate_bias_kernel + mlstm_ws_kernel",
                          "algorithmic_flops_per_step": projf + cellf,
                          "projection_flops": projf, "cell_flops": cellf}}
 

@@ -381,14 +381,16 @@ def lws(*args):
 def test_layer_workspace_query(lib):
     # B=2 T=70 d_model=64 H=3 d_qk=16 d_v=32 chunk 32 float32: 32 MiB for the
     # GEMMs, then q, k, v, o~, i~, f~ of the 3*2 cells (each padded to 256
-    # bytes), then the cell's own workspace
+    # bytes), W_i and W_f stacked [2H, d_model] (one gate GEMM), then the
+    # cell's own workspace
     s, n = lws(2, 70, 64, 3, 16, 32, 32, B.F32)
     cell = ctypes.c_size_t(0)
     assert B.lib().mlstm_fwd_chunkwise_workspace_size(3, 2, 70, 16, 32, 32, B.F32, ctypes.byref(cell)) == OK
     up = lambda x: (x + 255) // 256 * 256
     HBT = 3 * 2 * 70
     assert s == OK
-    assert n == (32 << 20) + 2 * up(HBT * 16 * 4) + 2 * up(HBT * 32 * 4) + 2 * up(HBT * 4) + up(cell.value)
+    assert n == ((32 << 20) + 2 * up(HBT * 16 * 4) + 2 * up(HBT * 32 * 4) + 2 * up(HBT * 4)
+                 + up(2 * 3 * 64 * 4) + up(cell.value))
     assert lws(2, 70, 60, 3, 16, 32, 32, B.F32)[0] == UNSUP    # d_model not a multiple of 8
     assert lws(2, 70, 64, 3, 24, 32, 32, B.F32)[0] == UNSUP    # d_qk
     assert lws(2, 70, 64, 3, 16, 32, 48, B.F32)[0] == UNSUP    # chunk

@@ -145,17 +145,28 @@ mlstm_status_t mlstm_fwd_chunkwise_workspace_size(int B, int H, int T, int d_qk,
                                                       MLSTM_VARIANT_AUTO, bytes);
 }
 
-mlstm_status_t mlstm_fwd_chunkwise_variant(const void *q, const void *k, const void *v,
-                                           const float *i_pre, const float *f_pre,
-                                           const void *o_pre, const float *C0, const float *n0,
-                                           const float *m0, void *h, float *C_T, float *n_T,
-                                           float *m_T, int B, int H, int T, int d_qk, int d_v,
-                                           int chunk, mlstm_dtype_t io, mlstm_variant_t variant,
-                                           void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace mlstm {
+
+// The chunkwise forward with the rows of q, k (lq) and of v, o~ (lv) in the
+// given layouts, NULL for dense.  Non-dense layouts are for callers inside the
+// library whose buffers hold B*H*T rows of each input in a strided order (the
+// layer's all-heads projections); they need the role-split kernel
+// (MLSTM_ERR_UNSUPPORTED otherwise).  The byte ranges checked for overlap are
+// B*H*T*d elements from each base, as for dense inputs.
+mlstm_status_t fwd_chunkwise_rows(const void *q, const void *k, const void *v, const float *i_pre,
+                                  const float *f_pre, const void *o_pre, const float *C0,
+                                  const float *n0, const float *m0, void *h, float *C_T, float *n_T,
+                                  float *m_T, int B, int H, int T, int d_qk, int d_v, int chunk,
+                                  mlstm_dtype_t io, mlstm_variant_t variant, void *workspace,
+                                  size_t workspace_bytes, void *stream, const RowLayout *lq,
+                                  const RowLayout *lv) {
     if (!q || !k || !v || !i_pre || !f_pre || !o_pre || !h) return MLSTM_ERR_NULL;
     Plan p;
     mlstm_status_t st = make_plan(B, H, T, d_qk, d_v, chunk, io, variant, &p);
     if (st != MLSTM_OK) return st;
+    if ((lq || lv) && !ws_kernel_selected(io == MLSTM_BF16, d_qk, d_v, p.kchunk)) return MLSTM_ERR_UNSUPPORTED;
     const int in0 = (C0 != nullptr) + (n0 != nullptr) + (m0 != nullptr);
     const int out0 = (C_T != nullptr) + (n_T != nullptr) + (m_T != nullptr);
     if ((in0 != 0 && in0 != 3) || (out0 != 0 && out0 != 3)) return MLSTM_ERR_STATE_ARGS;
@@ -199,6 +210,8 @@ mlstm_status_t mlstm_fwd_chunkwise_variant(const void *q, const void *k, const v
     a.h = h; a.CT = C_T; a.nT = n_T; a.mT = m_T;
     a.BH = (int)BH; a.T = T; a.dk = d_qk; a.dv = d_v;
     a.ntile = p.ntile; a.nseg = p.nseg; a.seg_len = p.seg_len;
+    a.lq = lq ? *lq : dense_rows(T, d_qk);
+    a.lv = lv ? *lv : dense_rows(T, d_v);
     const int bf = io == MLSTM_BF16;
     float *ws = static_cast<float *>(workspace);
     hipError_t e = hipSuccess;
@@ -227,6 +240,22 @@ mlstm_status_t mlstm_fwd_chunkwise_variant(const void *q, const void *k, const v
         }
     }
     return e == hipSuccess ? MLSTM_OK : MLSTM_ERR_HIP;
+}
+
+}  // namespace mlstm
+
+extern "C" {
+
+mlstm_status_t mlstm_fwd_chunkwise_variant(const void *q, const void *k, const void *v,
+                                           const float *i_pre, const float *f_pre,
+                                           const void *o_pre, const float *C0, const float *n0,
+                                           const float *m0, void *h, float *C_T, float *n_T,
+                                           float *m_T, int B, int H, int T, int d_qk, int d_v,
+                                           int chunk, mlstm_dtype_t io, mlstm_variant_t variant,
+                                           void *workspace, size_t workspace_bytes, void *stream) {
+    return fwd_chunkwise_rows(q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C_T, n_T, m_T, B, H, T,
+                              d_qk, d_v, chunk, io, variant, workspace, workspace_bytes, stream,
+                              nullptr, nullptr);
 }
 
 mlstm_status_t mlstm_fwd_chunkwise(const void *q, const void *k, const void *v, const float *i_pre,

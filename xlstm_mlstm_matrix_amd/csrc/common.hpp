@@ -30,6 +30,20 @@ template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
 
+// Where the input rows of a chunkwise call lie: the row of token t of pair p
+// starts (p / pdiv) * s_hi + (p % pdiv) * s_lo + t * ld elements from the base
+// pointer.  Dense [BH, T, d] rows are pdiv = 1, s_hi = T * d, s_lo = 0, ld = d.
+// Only the 64-token role-split kernel (mlstm_ws_kernel) reads other layouts;
+// the public entry points pass dense ones.
+struct RowLayout {
+    long long s_hi, s_lo;
+    int ld, pdiv;
+};
+__host__ __device__ inline RowLayout dense_rows(int T, int d) { return RowLayout{(long long)T * d, 0, d, 1}; }
+__host__ __device__ inline long long row_base(const RowLayout &l, int p) {
+    return (long long)(p / l.pdiv) * l.s_hi + (long long)(p % l.pdiv) * l.s_lo;
+}
+
 // Arguments of the chunkwise forward kernels (one struct, passed by value).
 struct FwdArgs {
     const void *q, *k, *v;         // [BH, T, d_qk] x2, [BH, T, d_v]   io dtype
@@ -45,6 +59,7 @@ struct FwdArgs {
     int nseg;                      // segments per sequence
     int ntile;                     // value-column tiles per sequence
     int nseg_out;                  // segments whose local state is produced (state-only pass)
+    RowLayout lq, lv;              // rows of q and k; of v and o (role-split kernel only)
 };
 
 // Layout of one segment state record in the workspace (float32):
@@ -133,5 +148,8 @@ bool prefill_supported(int io_bf16, int dk, int dv, int chunk);  // tiles fit in
 // chunk the kernels run with when the caller allows up to `chunk` tokens per
 // chunk: the largest of chunk, chunk/2, ..., 16 whose tiles fit (0: none)
 int prefill_kernel_chunk(int io_bf16, int dk, int dv, int chunk);
+// true when launch_fused runs the role-split kernel for this kernel chunk (the
+// only one that reads non-dense row layouts)
+bool ws_kernel_selected(int io_bf16, int dk, int dv, int chunk);
 
 }  // namespace mlstm

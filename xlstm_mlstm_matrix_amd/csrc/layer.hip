@@ -10,15 +10,23 @@
 //   i~ = W_i[h] . x + b_i[h],  f~ = W_f[h] . x + b_f[h]    (scalars)
 // then the chunkwise cell over each (head, batch) cell.
 //
-// Layout choice: cells are ordered head-major (cell p = h*B + b).  Then one
-// head's projection of every token of every batch is ONE plain GEMM with
-// M = d (the head's width), N = B*T tokens and K = d_model, whose
-// column-major result [d, B*T] is exactly the cell's row-major [B, T, d]
-// block of head h -- no permute pass.  The per-feature bias is hipBLASLt's
+// Layout choice: cells are ordered head-major (cell p = h*B + b).
+//  * Where the cell runs the 64-token role-split kernel (bf16, the 7B-layer
+//    heads), which reads strided input rows, each weight is ONE GEMM over all
+//    heads: M = H*d, N = B*T, K = d_model, column-major [H*d, B*T], so token
+//    b*T + t holds every head's features in one row of H*d; cell (h, b) reads
+//    the head-h part of rows b*T .. b*T + T - 1.  Four wide GEMMs run at a
+//    higher fraction of the MFMA peak than 4*H narrow ones (M = d).
+//  * Otherwise one head's projection of every token of every batch is one
+//    GEMM with M = d, N = B*T and K = d_model, whose column-major result
+//    [d, B*T] is exactly the cell's row-major [B, T, d] block of head h.
+// Neither needs a permute pass.  The per-feature bias is hipBLASLt's
 // bias epilogue (one value per output row).  The gate pre-activations of
 // head h are the GEMM [B*T, H] = x W_i^T (column-major, so each head's B*T
-// values are contiguous: the cell's gate layout), float32 out; their biases
-// are added by a small kernel.  The cell is mlstm_fwd_chunkwise with the
+// values are contiguous: the cell's gate layout), float32 out; with W_i and
+// W_f copied one after the other into the workspace, a single GEMM
+// [B*T, 2H] writes both and reads x once.  Their biases are added by a small
+// kernel.  The cell is mlstm_fwd_chunkwise with the
 // (batch, head) roles of its B and H swapped.
 //
 // The projections are plain library GEMMs (hipBLASLt, bf16 or fp32 inputs,
@@ -35,6 +43,16 @@
 #include "mlstm.h"
 
 namespace mlstm {
+
+// the chunkwise forward with strided input rows (api.cpp)
+mlstm_status_t fwd_chunkwise_rows(const void *q, const void *k, const void *v, const float *i_pre,
+                                  const float *f_pre, const void *o_pre, const float *C0,
+                                  const float *n0, const float *m0, void *h, float *C_T, float *n_T,
+                                  float *m_T, int B, int H, int T, int d_qk, int d_v, int chunk,
+                                  mlstm_dtype_t io, mlstm_variant_t variant, void *workspace,
+                                  size_t workspace_bytes, void *stream, const RowLayout *lq,
+                                  const RowLayout *lv);
+
 namespace {
 
 constexpr size_t kGemmWorkspace = size_t(32) << 20;  // hipBLASLt's share of the workspace
@@ -141,7 +159,9 @@ mlstm_status_t gemm_tn(int dev, int m, int n, int k, const void *A, const void *
 
 struct LayerPlan {
     size_t es, BT, nq, nv, ng;           // element size; tokens; q/k, v/o, gate element counts
-    size_t off_q, off_k, off_v, off_o, off_i, off_f, off_cell, cell_bytes, total;
+    size_t off_q, off_k, off_v, off_o, off_i, off_f, off_wg, off_cell, cell_bytes, total;
+    bool all_heads;                      // one GEMM per weight over all heads (strided rows)
+    bool one_gate_gemm;                  // W_i and W_f stacked: one gate GEMM
 };
 
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
@@ -166,9 +186,14 @@ mlstm_status_t layer_plan(int B, int T, int D, int H, int dk, int dv, int chunk,
     p->off_k = p->off_q + up256(p->nq * p->es);
     p->off_v = p->off_k + up256(p->nq * p->es);
     p->off_o = p->off_v + up256(p->nv * p->es);
+    // the gate pre-activations: [H][B*T] float32 each, i~ then f~; adjacent
+    // (one GEMM writes both) when f~ stays 16-byte aligned that way
+    p->all_heads = ws_kernel_selected(io == MLSTM_BF16, dk, dv, prefill_kernel_chunk(io == MLSTM_BF16, dk, dv, chunk));
+    p->one_gate_gemm = p->all_heads && p->ng % 4 == 0;
     p->off_i = p->off_o + up256(p->nv * p->es);
-    p->off_f = p->off_i + up256(p->ng * 4);
-    p->off_cell = p->off_f + up256(p->ng * 4);
+    p->off_f = p->off_i + (p->one_gate_gemm ? p->ng * 4 : up256(p->ng * 4));
+    p->off_wg = p->off_i + 2 * up256(p->ng * 4);           // W_i, W_f stacked [2H, D]
+    p->off_cell = p->off_wg + up256(2 * (size_t)H * D * p->es);
     p->cell_bytes = cell;
     p->total = p->off_cell + up256(cell);
     return MLSTM_OK;
@@ -254,8 +279,17 @@ mlstm_status_t mlstm_layer_fwd(const void *x, const void *W_q, const void *W_k, 
     const char *Wv = static_cast<const char *>(W_v), *Wo = static_cast<const char *>(W_o);
     const int N = (int)p.BT;
 
-    // projections: head hh of q is the column-major [d_qk, B*T] block at hh*B*T*d_qk
-    for (int hh = 0; hh < H; ++hh) {
+    if (p.all_heads) {
+        // one GEMM per weight: column-major [H*d, B*T], i.e. token n = b*T + t
+        // holds the features of every head in one row of H*d (the cell reads
+        // these strided rows directly)
+        if ((st = gemm_tn(dev, H * d_qk, N, d_model, Wq, x, q, ab, ab, b_q, ws, s))) return st;
+        if ((st = gemm_tn(dev, H * d_qk, N, d_model, Wk, x, k, ab, ab, b_k, ws, s))) return st;
+        if ((st = gemm_tn(dev, H * d_v, N, d_model, Wv, x, v, ab, ab, b_v, ws, s))) return st;
+        if ((st = gemm_tn(dev, H * d_v, N, d_model, Wo, x, o, ab, ab, b_o, ws, s))) return st;
+    }
+    // otherwise per head: head hh of q is the column-major [d_qk, B*T] block at hh*B*T*d_qk
+    for (int hh = 0; hh < (p.all_heads ? 0 : H); ++hh) {
         const size_t wq = (size_t)hh * d_qk * D * es, wv = (size_t)hh * d_v * D * es;
         const size_t oq = (size_t)hh * p.BT * d_qk * es, ov = (size_t)hh * p.BT * d_v * es;
         if ((st = gemm_tn(dev, d_qk, N, d_model, Wq + wq, x, q + oq, ab, ab, b_q + (size_t)hh * d_qk, ws, s)))
@@ -267,13 +301,32 @@ mlstm_status_t mlstm_layer_fwd(const void *x, const void *W_q, const void *W_k, 
         if ((st = gemm_tn(dev, d_v, N, d_model, Wo + wv, x, o + ov, ab, ab, b_o + (size_t)hh * d_v, ws, s)))
             return st;
     }
-    // gate pre-activations: [B*T, H] column-major = [H][B*T], float32
-    if ((st = gemm_tn(dev, N, H, d_model, x, W_i, gi, ab, HIP_R_32F, nullptr, ws, s))) return st;
-    if ((st = gemm_tn(dev, N, H, d_model, x, W_f, gf, ab, HIP_R_32F, nullptr, ws, s))) return st;
+    // gate pre-activations: [B*T, H] column-major = [H][B*T], float32; with
+    // W_i and W_f stacked, one GEMM [B*T, 2H] writes i~ and then f~ (x read once)
+    if (p.one_gate_gemm) {
+        char *wg = ws + p.off_wg;
+        const size_t wb = (size_t)H * D * es;
+        if (hipMemcpyAsync(wg, W_i, wb, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+            hipMemcpyAsync(wg + wb, W_f, wb, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return MLSTM_ERR_HIP;
+        if ((st = gemm_tn(dev, N, 2 * H, d_model, x, wg, gi, ab, HIP_R_32F, nullptr, ws, s))) return st;
+    } else {
+        if ((st = gemm_tn(dev, N, H, d_model, x, W_i, gi, ab, HIP_R_32F, nullptr, ws, s))) return st;
+        if ((st = gemm_tn(dev, N, H, d_model, x, W_f, gf, ab, HIP_R_32F, nullptr, ws, s))) return st;
+    }
     hipLaunchKernelGGL(gate_bias_kernel, dim3(1024), dim3(256), 0, s, gi, gf, b_i, b_f, p.BT, H);
     if (hipGetLastError() != hipSuccess) return MLSTM_ERR_HIP;
 
-    // the cell over the H*B head-major cells: its "B" is H and its "H" is B
+    // the cell over the H*B head-major cells: its "B" is H and its "H" is B;
+    // with all-heads projections, cell p = h*B + b reads the head-h part of
+    // rows b*T .. b*T + T - 1
+    if (p.all_heads) {
+        const RowLayout lq{d_qk, (long long)T * H * d_qk, H * d_qk, B};
+        const RowLayout lv{d_v, (long long)T * H * d_v, H * d_v, B};
+        return fwd_chunkwise_rows(q, k, v, gi, gf, o, C0, n0, m0, h, C_T, n_T, m_T, H, B, T, d_qk, d_v,
+                                  chunk, io, MLSTM_VARIANT_AUTO, ws + p.off_cell, p.cell_bytes, stream,
+                                  &lq, &lv);
+    }
     return mlstm_fwd_chunkwise(q, k, v, gi, gf, o, C0, n0, m0, h, C_T, n_T, m_T, H, B, T, d_qk, d_v,
                                chunk, io, ws + p.off_cell, p.cell_bytes, stream);
 }

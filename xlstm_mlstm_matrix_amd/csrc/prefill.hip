@@ -149,10 +149,14 @@ hipError_t ws_by_shape(const FwdArgs &a, int dkp, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+bool ws_kernel_selected(int io_bf16, int dk, int dv, int chunk) {
+    return io_bf16 && chunk == 64 && prefill_bv(io_bf16, dk, dv, chunk) == 128 && bf16_fast_path(chunk, dk, dv);
+}
+
 hipError_t launch_fused(const FwdArgs &a, int io_bf16, int chunk, int state_only, hipStream_t s) {
     const int dkp = prefill_dkp(a.dk);
     const int bv = prefill_bv(io_bf16, a.dk, a.dv, chunk);
-    if (io_bf16 && chunk == 64 && bv == 128 && bf16_fast_path(chunk, a.dk, a.dv))
+    if (ws_kernel_selected(io_bf16, a.dk, a.dv, chunk))
         return state_only ? ws_by_shape<true>(a, dkp, s) : ws_by_shape<false>(a, dkp, s);
     if (io_bf16 && bf16_fast_path(chunk, a.dk, a.dv)) {
         if (bv == 128)

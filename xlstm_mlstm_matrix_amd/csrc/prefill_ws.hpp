@@ -212,10 +212,12 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     const int nchunks = (t_end - t_begin + L - 1) / L;
     const int col0 = tile * BV;
 
-    const bf16 *qg = static_cast<const bf16 *>(a.q) + (size_t)bh * T * DKP;
-    const bf16 *kg = static_cast<const bf16 *>(a.k) + (size_t)bh * T * DKP;
-    const bf16 *vg = static_cast<const bf16 *>(a.v) + (size_t)bh * T * dv + col0;
-    const bf16 *og = static_cast<const bf16 *>(a.o) + (size_t)bh * T * dv + col0;
+    // input rows in the call's layout (ldq, ldv elements apart), h dense
+    const int ldq = a.lq.ld, ldv = a.lv.ld;
+    const bf16 *qg = static_cast<const bf16 *>(a.q) + row_base(a.lq, bh);
+    const bf16 *kg = static_cast<const bf16 *>(a.k) + row_base(a.lq, bh);
+    const bf16 *vg = static_cast<const bf16 *>(a.v) + row_base(a.lv, bh) + col0;
+    const bf16 *og = static_cast<const bf16 *>(a.o) + row_base(a.lv, bh) + col0;
     bf16 *hg = static_cast<bf16 *>(a.h) + (size_t)bh * T * dv + col0;
     const float *igg = a.ig + (size_t)bh * T;
     const float *fgg = a.fg + (size_t)bh * T;
@@ -587,12 +589,12 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     } else {
         // ========================= intra wavefronts =========================
         unsigned qko[2], vo[2];  // per-lane copy offsets of Q/K and V tiles
-        copy_offsets(QGc{}, DKP, qko);
-        copy_offsets(VGc{}, dv, vo);
+        copy_offsets(QGc{}, ldq, qko);
+        copy_offsets(VGc{}, ldv, vo);
         if constexpr (SO) {
             if (nchunks > 0) {
-                copy_tile(Ks[0], kg, DKP, QGc{}, t_begin, qko);
-                copy_tile(vbuf(0), vg, dv, VGc{}, t_begin, vo);
+                copy_tile(Ks[0], kg, ldq, QGc{}, t_begin, qko);
+                copy_tile(vbuf(0), vg, ldv, VGc{}, t_begin, vo);
                 if (wave == GW) {
                     load_gates(0);
                     gate_prep(m_prev, gt[0]);
@@ -603,8 +605,8 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                 if (c + 1 < nchunks) {
                     const int tn = t_begin + (c + 1) * L;
                     if (wave == GW) load_gates(c + 1);
-                    copy_tile(Ks[(c + 1) & 1], kg, DKP, QGc{}, tn, qko);
-                    copy_tile(vbuf(c + 1), vg, dv, VGc{}, tn, vo);
+                    copy_tile(Ks[(c + 1) & 1], kg, ldq, QGc{}, tn, qko);
+                    copy_tile(vbuf(c + 1), vg, ldv, VGc{}, tn, vo);
                     if (wave == GW) gate_prep(gt[c & 1][6 * LP + 0], gt[(c + 1) & 1]);
                 }
                 role_sync<0>();  // K(c+1), V(c+1) landed, gates of c+1 written
@@ -612,8 +614,8 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             return;
         }
         if (nchunks > 0) {
-            copy_tile(Qs, qg, DKP, QGc{}, t_begin, qko);
-            copy_tile(Ks[0], kg, DKP, QGc{}, t_begin, qko);
+            copy_tile(Qs, qg, ldq, QGc{}, t_begin, qko);
+            copy_tile(Ks[0], kg, ldq, QGc{}, t_begin, qko);
             if (wave == GW) {
                 load_gates(0);
                 gate_prep(m_prev, gt[0]);
@@ -631,16 +633,16 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
 
             // ---- phase 1: copy V(c); S, P of this token tile; next gate
             // table; copy K(c+1)
-            copy_tile(Vs, vg, dv, VGc{}, tc, vo);
+            copy_tile(Vs, vg, ldv, VGc{}, tc, vo);
             // this chunk's rows of o~ and h: buffer descriptors whose range ends
             // at the segment's last row (o~ past it reads as zero, h past it is
             // not written)
-            const int nbo = __builtin_amdgcn_readfirstlane(min(L, t_end - tc) * dv * 2);
-            const auto ro = __builtin_amdgcn_make_buffer_rsrc((void *)(og + (size_t)tc * dv), 0, nbo, kWsBuf);
+            const int nrow = __builtin_amdgcn_readfirstlane(min(L, t_end - tc));
+            const auto ro = __builtin_amdgcn_make_buffer_rsrc((void *)(og + (size_t)tc * ldv), 0, nrow * ldv * 2, kWsBuf);
             u32x4 orw[NHS];  // output-gate inputs: value columns 32 m + 8 g4 .. +8
 #pragma unroll
             for (int m = 0; m < NHS; ++m)
-                orw[m] = __builtin_amdgcn_raw_buffer_load_b128(ro, 2u * (unsigned)(irow * dv + 32 * m + 8 * g4), 0, 0);
+                orw[m] = __builtin_amdgcn_raw_buffer_load_b128(ro, 2u * (unsigned)(irow * ldv + 32 * m + 8 * g4), 0, 0);
             if (more && wave == GW) load_gates(c + 1);
             // S^T tiles (jt, it) for jt <= it, k-step outermost so each Q
             // fragment serves all of them; each K fragment is refilled for the
@@ -703,13 +705,13 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
 #pragma unroll
             for (int m = 0; m < NHS; ++m)
                 asm volatile("" : "+v"(orw[m]));
-            if (more) copy_tile(Ks[(c + 1) & 1], kg, DKP, QGc{}, tc + L, qko);
+            if (more) copy_tile(Ks[(c + 1) & 1], kg, ldq, QGc{}, tc + L, qko);
             // (X) V(c) landed (only the K copy may stay in flight)
             if (more)
                 role_sync<NKS>();
             else
                 role_sync<0>();
-            if (more) copy_tile(Qs, qg, DKP, QGc{}, tc + L, qko);  // every reader of Q(c) is past X
+            if (more) copy_tile(Qs, qg, ldq, QGc{}, tc + L, qko);  // every reader of Q(c) is past X
 
             // ---- phase 2: O^T of this token tile = scaled read-out + V^T P^T; h
             int vpo[NHS][2];  // V^T fragment offsets by (column tile / 2, read)
@@ -740,7 +742,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             const int irow2 = 16 * it + (ln2 & 15);
             const float den = G[2 * LP + irow2] * qn + rowsum;
             const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), G[3 * LP + irow2]));
-            const auto rh = __builtin_amdgcn_make_buffer_rsrc((void *)(hg + (size_t)tc * dv), 0, nbo, kWsBuf);
+            const auto rh = __builtin_amdgcn_make_buffer_rsrc((void *)(hg + (size_t)tc * dv), 0, nrow * dv * 2, kWsBuf);
 #pragma unroll
             for (int m = 0; m < NHS; ++m) {
                 bf16x8 hv;
