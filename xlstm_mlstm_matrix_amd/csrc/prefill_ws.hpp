@@ -164,10 +164,10 @@ __device__ __forceinline__ void role_sync() {
 }
 
 // SO (state only): the segment scan's first pass -- each segment's local
-// state from the zero state, no output.  The state wavefronts run the update
-// alone; the intra wavefronts copy K and V (both double buffered, the second V
-// buffer in the unused exchange area) and prepare the gates, one barrier per
-// chunk.
+// state from the zero state, no output.  The state wavefronts run the C'
+// update alone; the intra wavefronts copy K and V (both double buffered, the
+// second V buffer in the unused exchange area), prepare the gates and update
+// n', one barrier per chunk.
 template <int DKP, bool SO>
 __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     using Cfg = WsCfg<DKP>;
@@ -376,6 +376,50 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     // k index in the S accumulator order (V^T of V^T P^T): rows 32 js + 4 g4 + te (+16)
     const int prow0 = 4 * g4 + te, prow1 = prow0 + 16;
 
+    // n' <- decay n' + K^T w (true scale) from buffer nb into nb ^ 1, for the
+    // row tiles s + 4 x, by wavefront s of the intra role: the state-only
+    // pass's update of n', run beside the state wavefronts' C' update (which
+    // reads the same K tile).  MFMAs with w's high part and remainder in every
+    // column of the B operand, on K^T fragments read per k-step.
+    auto nprime_intra = [&](const bf16 *K, const float *G, float s_last, int nb) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int lte = (ln & 15) >> 2, ltq = ln & 3, lg4 = ln >> 4;
+        const int krow0 = 8 * lg4 + lte, krow1 = krow0 + 4;
+        const int kb0 = krow0 * QG * 8, kb1 = krow1 * QG * 8;
+        const int kx0 = qswz(krow0) ^ ltq, kx1 = qswz(krow1) ^ ltq;
+        const bf16 *W2 = reinterpret_cast<const bf16 *>(&G[5 * LP]);
+        constexpr int NX = NAT / 4;
+        f32x4 nh[NX], nl[NX];
+#pragma unroll
+        for (int x = 0; x < NX; ++x) nh[x] = nl[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int js = 0; js < L / 32; ++js) {
+            const bf16 *k0 = K + 32 * js * DKP;
+            bf16x8 af[NX];
+#pragma unroll
+            for (int x = 0; x < NX; ++x) {
+                const int at = 4 * x + s;
+                const int h = 4 * (at & 1), g = 4 * (at >> 1);
+                af[x] = cat8(tr_read(k0 + kb0 + h + ((g ^ kx0) << 3)), tr_read(k0 + kb1 + h + ((g ^ kx1) << 3)));
+            }
+            const bf16x8 bnh = *reinterpret_cast<const bf16x8 *>(W2 + 32 * js + 8 * lg4);
+            const bf16x8 bnl = *reinterpret_cast<const bf16x8 *>(W2 + LP + 32 * js + 8 * lg4);
+#pragma unroll
+            for (int x = 0; x < NX; ++x) nh[x] = mfma(af[x], bnh, nh[x]);
+#pragma unroll
+            for (int x = 0; x < NX; ++x) nl[x] = mfma(af[x], bnl, nl[x]);
+        }
+        if (l16 == 0) {
+#pragma unroll
+            for (int x = 0; x < NX; ++x) {
+                const int r0 = crow(s + 4 * x, 0);
+                *reinterpret_cast<f32x4 *>(&nsh[nb ^ 1][r0]) =
+                    *reinterpret_cast<const f32x4 *>(&nsh[nb][r0]) * s_last + (nh[x] + nl[x]);
+            }
+        }
+    };
+
     if (nchunks > 0) block_sync<0>();  // gate tables zeroed, n' written
 
     // Each role runs its own chunk loop; both execute the same sequence of
@@ -419,12 +463,14 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                 // column of the B operand (every lane gets K^T w for its rows);
                 // the row tile is picked from the last four fragments by selects
                 // on the wavefront index
+                // (full pass only: in the state-only pass the otherwise idle
+                // intra wavefronts update n', with nprime_intra)
                 unsigned sm0 = 0u - (unsigned)(s & 1), sm1 = 0u - (unsigned)((s >> 1) & 1);
                 asm volatile("" : "+s"(sm0), "+s"(sm1));
                 f32x4 nold[NAT / 4], nacc_h[NAT / 4], nacc_l[NAT / 4];
     #pragma unroll
                 for (int x = 0; x < NAT / 4; ++x) {
-                    nold[x] = *reinterpret_cast<const f32x4 *>(&nsh[nb][crow(s + 4 * x, 0)]);
+                    if constexpr (!SO) nold[x] = *reinterpret_cast<const f32x4 *>(&nsh[nb][crow(s + 4 * x, 0)]);
                     nacc_h[x] = f32x4{0.f, 0.f, 0.f, 0.f};
                     nacc_l[x] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
@@ -467,7 +513,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                         const bf16x8 &a0 = ak[at & 7];
     #pragma unroll
                         for (int bt = 0; bt < 2; ++bt) Cr[at][bt] = mfma(a0, bw[bt], Cr[at][bt]);
-                        if ((at & 3) == 3) {  // compile-time: the group at - 3 .. at is complete
+                        if (!SO && (at & 3) == 3) {  // compile-time: the group at - 3 .. at is complete
                             const bf16x8 fn = pick4(ak[(at - 3) & 7], ak[(at - 2) & 7], ak[(at - 1) & 7], a0, sm0, sm1);
                             nacc_h[at >> 2] = mfma(fn, bnh, nacc_h[at >> 2]);
                             nacc_l[at >> 2] = mfma(fn, bnl, nacc_l[at >> 2]);
@@ -476,7 +522,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 // n' <- decay n' + K^T w into buffer nb ^ 1 (read after barrier Y)
-                if (l16 == 0) {
+                if (!SO && l16 == 0) {
     #pragma unroll
                     for (int x = 0; x < NAT / 4; ++x) {
                         const int r0 = crow(s + 4 * x, 0);
@@ -609,7 +655,9 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                     copy_tile(vbuf(c + 1), vg, ldv, VGc{}, tn, vo);
                     if (wave == GW) gate_prep(gt[c & 1][6 * LP + 0], gt[(c + 1) & 1]);
                 }
-                role_sync<0>();  // K(c+1), V(c+1) landed, gates of c+1 written
+                // n' with chunk c while its copies of chunk c + 1 are in flight
+                nprime_intra(Ks[c & 1], gt[c & 1], gt[c & 1][6 * LP + 1], c & 1);
+                role_sync<0>();  // K(c+1), V(c+1) landed, gates of c+1 and n' after c written
             }
             return;
         }
