@@ -418,6 +418,11 @@ def main():
         "ms_per_step": ms,
         "ms_per_step_median": r["median_ms"],
         "clock_settle": {"ms": r["settle_ms"], "steps": r["settle_steps"]},
+        # the headline's two fractions side by side: algorithmic flops over the
+        # bf16 MFMA peak, algorithmic bytes over the HBM peak (the kernel is
+        # bound by HBM: 136 flop per byte, below the ridge)
+        "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+        "hbm_frac": gbs / PEAK_HBM_GBS,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
