@@ -61,6 +61,19 @@ def test_layer_7b_heads_short(T):
     compare(run_gpu(d, w.chunk), run_oracle(d, "bf16"), "bf16", f"layer 7b heads T={T}")
 
 
+@pytest.mark.parametrize("H,B,T", [(1, 1, 77), (3, 1, 33)])
+def test_layer_7b_heads_odd_token_count(H, B, T):
+    """The 7B layer's heads with H*B*T not a multiple of 4: the projections
+    still run over all heads, but the gate pre-activations take two GEMMs
+    (one [B*T, 2H] GEMM would leave f~ misaligned behind i~); with a random
+    initial state."""
+    w = I.layer_workload("layer_7b_bf16", B=B, T=T, d_model=256, H=H,
+                         init_state={"C0": ("normal", 0.0, 0.1), "n0": ("normal", 0.0, 0.1),
+                                     "m0": ("uniform", -1.0, 1.0)})
+    d = I.gen_layer(w)
+    compare(run_gpu(d, w.chunk), run_oracle(d, "bf16"), "bf16", f"layer 7b heads H={H} B={B} T={T}")
+
+
 def test_layer_full_size_sampled():
     """The 7B layer workload at full size (B=8 T=4096 d_model=4096 H=8, the
     configuration the benchmark times); the oracle follows every head of two
