@@ -128,6 +128,31 @@ def test_segscan_with_initial_state_f32():
     PT.compare_fwd(PT.run_gpu_fwd(d, 32, variant="segscan"), PT.run_oracle(d), "f32", "segscan f32 + state")
 
 
+@pytest.mark.parametrize("dk,dv,T,with_state", [(256, 512, 748, False), (256, 512, 837, True),
+                                                (128, 256, 1100, False), (64, 128, 900, True)])
+def test_segscan_multi_chunk_segments(dk, dv, T, with_state):
+    """The segmented schedule with several chunks per segment and a ragged last
+    one.  Sixteen pairs give the planner enough column-block workgroups that it
+    cuts 4 to 6 segments of 3 or 4 chunks each.  The state-only pass then walks
+    several chunks per segment (the other segmented cases have 2, or 128 at the
+    long-context size), and the combine chains 3 to 5 local states.  Checked from
+    the zero state and from a random one."""
+    pairs = [(b, h) for b in range(2) for h in range(8)]
+    w, d = case("prefill_7b_bf16", pairs=pairs, T=T, d_qk=dk, d_v=dv)
+    if with_state:
+        rng = np.random.default_rng(2000 + T)
+        P = len(pairs)
+        d["C0"] = torch.from_numpy(rng.normal(0.0, 0.05, (P, dk, dv))).float()
+        d["n0"] = torch.from_numpy(rng.normal(0.0, 0.05, (P, dk))).float()
+        d["m0"] = torch.from_numpy(rng.uniform(-1.0, 1.0, P)).float()
+    kc, nseg = binding.schedule(1, len(pairs), T, dk, dv, 64, binding.BF16, "segscan")
+    cps = -(-T // (64 * nseg))  # chunks per segment: segments are whole chunks, nseg of them cover T
+    print(f"[case] segscan dk={dk} dv={dv} T={T} segments={nseg} chunks/segment={cps}", flush=True)
+    assert kc == 64 and nseg >= 4 and cps >= 3
+    PT.compare_fwd(PT.run_gpu_fwd(d, 64, variant="segscan"), PT.run_oracle(d), "bf16",
+                   f"segscan dk={dk} dv={dv} T={T} state={with_state}")
+
+
 def test_state_carry():
     """fwd(x[:t0]) then fwd(x[t0:], state) equals fwd(x) and the oracle."""
     w, d = case("small_f32", pairs=[(0, 0), (1, 3)], T=700)
