@@ -20,10 +20,10 @@
 //  - one workgroup per pair (no workspace): the workgroup owns the pair's
 //    whole memory, so n and m are updated in place without any race;
 //  - row split (with a workspace): the pair's rows are cut into blocks of
-//    RPI*UNROLL rows, one workgroup each, so every thread issues all of its
-//    loads at once and the chip sees many short, independent streams (in-place
-//    streaming of 128 KiB per workgroup runs ~6% faster than 512 KiB here).
-//    Each block updates its own rows of C' and n' and writes its partial
+//    RPI*UNROLL rows (128 KiB at 256 x 512: short, independent streams run
+//    faster here than 512 KiB ones), which a fixed grid of workgroups walks,
+//    each thread keeping its UNROLL row loads in flight from one block into
+//    the next.  Each block updates its own rows of C' and n' and writes its partial
 //    read-out (a d_v vector and its part of n'^T q) to the workspace; a second,
 //    small launch sums the partials in block order and writes h and m'.  The
 //    kernel boundary orders the two, so no block waits on another and m is
