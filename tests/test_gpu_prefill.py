@@ -74,6 +74,28 @@ def test_chunk64_value_blocks(dk, dv, with_state, variant):
                    f"chunk 64 dk={dk} dv={dv} state={with_state} {variant}")
 
 
+@pytest.mark.parametrize("variant", ["fused", "segscan"])
+@pytest.mark.parametrize("dk,dv,io", [(16, 432, "bf16"), (32, 176, "f32"), (64, 320, "bf16"),
+                                      (16, 64, "f32"), (48, 96, "bf16"), (64, 512, "bf16")])
+def test_chunk128_small_heads(dk, dv, io, variant):
+    """Chunk 128 runs as such only where its tiles fit in LDS, at d_qk up to
+    64: a chunk then spans two 64-token parts of the gate scan, whose running
+    sum of f~ and prefix maximum of u carry from the first part into the
+    second.  Five whole chunks and a ragged last one, from a random state;
+    the segmented schedule cuts them into 3 segments."""
+    name = "small_f32" if io == "f32" else "prefill_7b_bf16"
+    T = 700
+    w, d = case(name, pairs=[(0, 1), (1, 0), (2, 3)], T=T, d_qk=dk, d_v=dv)
+    rng = np.random.default_rng(128 + dk + dv)
+    d["C0"] = torch.from_numpy(rng.normal(0.0, 0.05, (3, dk, dv))).float()
+    d["n0"] = torch.from_numpy(rng.normal(0.0, 0.05, (3, dk))).float()
+    d["m0"] = torch.from_numpy(rng.uniform(-1.0, 1.0, 3)).float()
+    kc, nseg = binding.schedule(1, 3, T, dk, dv, 128, binding.BF16 if io == "bf16" else binding.F32, variant)
+    assert kc == 128 and nseg == (3 if variant == "segscan" else 1)
+    PT.compare_fwd(PT.run_gpu_fwd(d, 128, variant=variant), PT.run_oracle(d), io,
+                   f"chunk 128 dk={dk} dv={dv} {io} {variant}")
+
+
 @pytest.mark.parametrize("dk", [64, 128, 256])
 @pytest.mark.parametrize("chunk", [32, 64])
 def test_readout_keeps_state_precision(dk, chunk):

@@ -322,7 +322,14 @@ __global__ __launch_bounds__(64 * NW, 1) void mlstm_chunk_kernel(FwdArgs a) {
     const int uqk = (L / 4) * nvq;
     const int uv = (L / 4) * nvv;
     uint4 rq[UQK][4], rk[UQK][4], rv[UV][4];
-    float gf = 0.0f, gi = -INFINITY;          // wavefront 0: this lane's token gates
+    // wavefront 0: the chunk's gates, token 64 h + lane in slot h
+    constexpr int NGH = (L + 63) / 64;
+    float gf[NGH], gi[NGH];
+#pragma unroll
+    for (int hh = 0; hh < NGH; ++hh) {
+        gf[hh] = 0.0f;
+        gi[hh] = -INFINITY;
+    }
 
     auto load_chunk = [&](int c) {
         const int tc = t_begin + c * L;
@@ -352,10 +359,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mlstm_chunk_kernel(FwdArgs a) {
             }
         }
         if (wave == 0) {
-            const int t = tc + lane;
-            const bool ok = lane < L && t < t_end;
-            gf = ok ? fgg[t] : 0.0f;
-            gi = ok ? igg[t] : -INFINITY;
+#pragma unroll
+            for (int hh = 0; hh < NGH; ++hh) {
+                const int tok = 64 * hh + lane, t = tc + tok;
+                const bool ok = tok < L && t < t_end;
+                gf[hh] = ok ? fgg[t] : 0.0f;
+                gi[hh] = ok ? igg[t] : -INFINITY;
+            }
         }
     };
     auto write_chunk = [&]() {
@@ -384,30 +394,51 @@ __global__ __launch_bounds__(64 * NW, 1) void mlstm_chunk_kernel(FwdArgs a) {
             }
         }
     };
-    // wavefront 0: gate quantities of the staged chunk (one token per lane)
+    // wavefront 0: gate quantities of the staged chunk, one token per lane in
+    // each 64-token part: the inclusive sums of f~ and the prefix maxima of
+    // u run across the parts through the carries of the previous part's last
+    // lane (tokens past the chunk or T have f~ = 0, i~ = -inf and leave both
+    // unchanged)
     auto gate_prep = [&](float m_before) {
-        float b = gf;
+        float bcarry = 0.0f, pmcarry = -INFINITY, r_last = 0.0f, b_last = 0.0f;
+        float uh[NGH];
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(b, off, 64);
-            if (lane >= off) b += y;
-        }
-        const float u = gi - b;
-        float pm = u;
+        for (int hh = 0; hh < NGH; ++hh) {
+            float b = gf[hh];
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(pm, off, 64);
-            if (lane >= off) pm = fmaxf(pm, y);
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(b, off, 64);
+                if (lane >= off) b += y;
+            }
+            b += bcarry;
+            const float u = gi[hh] - b;
+            float pm = u;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(pm, off, 64);
+                if (lane >= off) pm = fmaxf(pm, y);
+            }
+            pm = fmaxf(pm, pmcarry);
+            const float r = fmaxf(m_before, pm);
+            const int tok = 64 * hh + lane;
+            if (tok < L) {
+                g_u[tok] = u;
+                g_r[tok] = r;
+                g_s[tok] = exp_e(m_before - r);
+                g_fl[tok] = exp_e(-(b + r));
+            }
+            uh[hh] = u;
+            if (hh == (L - 1) / 64) {  // the part holding the chunk's last token
+                r_last = __shfl(r, (L - 1) % 64, 64);
+                b_last = __shfl(b, (L - 1) % 64, 64);
+            }
+            bcarry = __shfl(b, 63, 64);
+            pmcarry = __shfl(pm, 63, 64);
         }
-        const float r = fmaxf(m_before, pm);
-        const float r_last = __shfl(r, L - 1, 64);
-        const float b_last = __shfl(b, L - 1, 64);
-        if (lane < L) {
-            g_u[lane] = u;
-            g_r[lane] = r;
-            g_s[lane] = exp_e(m_before - r);
-            g_fl[lane] = exp_e(-(b + r));
-            g_w[lane] = exp_e(u - r_last);
+#pragma unroll
+        for (int hh = 0; hh < NGH; ++hh) {
+            const int tok = 64 * hh + lane;
+            if (tok < L) g_w[tok] = exp_e(uh[hh] - r_last);
         }
         if (lane == 0) {
             sc[0] = b_last + r_last;          // stabilizer after the chunk
