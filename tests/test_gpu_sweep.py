@@ -21,7 +21,11 @@ from xlstm_mlstm_matrix_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
 
-N_FWD, N_STEP, N_BWD = 24, 12, 10
+N_FWD, N_STEP, N_BWD = 48, 16, 12
+# draws kept from a wider run, each of which once failed: 183 (float32, d_qk
+# 176, chunk 32: the first token's q.k cancels ~7500-fold, beyond what
+# operands of ~16 bits resolve to 2e-3)
+EXTRA_FWD = [183]
 
 
 def _draw(seed):
@@ -52,7 +56,7 @@ def fwd_case(i):
     return rng, dict(io=io, dk=dk, dv=dv, T=T, chunk=chunk, variant=variant, P=P, state=state)
 
 
-@pytest.mark.parametrize("i", range(N_FWD))
+@pytest.mark.parametrize("i", list(range(N_FWD)) + EXTRA_FWD)
 def test_fwd_sweep(i):
     rng, c = fwd_case(i)
     print(f"[case] fwd sweep {i}: {c}", flush=True)

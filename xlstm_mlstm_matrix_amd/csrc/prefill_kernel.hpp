@@ -26,9 +26,10 @@
 // d_qk x BV slice of C' in registers for the whole sequence; each wavefront
 // owns BV/NW columns of it.  Per chunk:
 //   S^T = K Q^T (only the causal 16x16 tiles, spread over the wavefronts),
-//   O^T = C'^T Q^T, with C' converted to bf16 fragments straight from the
-//         MFMA accumulator layout (a permutation of the k index that the Q
-//         and K fragments follow too), so C' never goes through LDS;
+//   O^T = C'^T Q^T, with C' converted to bf16 high-part and remainder
+//         fragments straight from the MFMA accumulator layout (a
+//         permutation of the k index that the Q and K fragments follow too),
+//         so C' never goes through LDS;
 //   P   = S (x) decay, shared through LDS as bf16;  O^T += V^T P^T;
 //   h from O^T, the shared denominators and the output gate;
 //   C'  = decay * C' + K^T (w (x) V)   (MFMA accumulating into the registers).
@@ -36,10 +37,12 @@
 // contiguous) are written transposed from registers when the chunk is staged.
 // The next chunk's tiles are loaded into registers while the current chunk
 // computes and are written to LDS after it.  All MFMAs are
-// v_mfma_f32_16x16x32_bf16 with float32 accumulation; for float32 I/O every
-// operand is split into a bf16 high part and a bf16 remainder and three
-// MFMAs are issued (hi*hi + hi*lo + lo*hi), which keeps ~16 bits of each
-// operand.
+// v_mfma_f32_16x16x32_bf16 with float32 accumulation.  For float32 I/O every
+// operand is split into three bf16 parts (24 significant bits, as float32)
+// and six MFMAs are issued per product (every part product above 2^-24 of
+// it), so each product is float32-grade.  For bf16 I/O the read-out splits
+// C' into a high part and a remainder against the exact bf16 q (two MFMAs);
+// the other products take bf16 operands.
 #pragma once
 
 #include <type_traits>
@@ -79,7 +82,10 @@ struct PrefillCfg {
 // ---------------------------------------------------------------- fragments
 template <bool SPLIT> struct Frag;
 template <> struct Frag<false> { bf16x8 x; };
-template <> struct Frag<true> { bf16x8 hi, lo; };
+// float32 operand as three bf16 parts: x = hi + mid + lo to about 2^-25 |x|
+template <> struct Frag<true> { bf16x8 hi, mid, lo; };
+// float32 state against an exact bf16 operand: high part and remainder
+struct Frag2 { bf16x8 hi, lo; };
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -87,10 +93,21 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f3
 __device__ __forceinline__ f32x4 mma(const Frag<false> &a, const Frag<false> &b, f32x4 c) {
     return mfma(a.x, b.x, c);
 }
+// the six part products down to 2^-16 of the product (the three dropped ones,
+// mid*lo, lo*mid and lo*lo, are below 2^-24 of it): float32-grade products,
+// smallest terms first
 __device__ __forceinline__ f32x4 mma(const Frag<true> &a, const Frag<true> &b, f32x4 c) {
-    c = mfma(a.hi, b.hi, c);
+    c = mfma(a.lo, b.hi, c);
     c = mfma(a.hi, b.lo, c);
-    return mfma(a.lo, b.hi, c);
+    c = mfma(a.mid, b.mid, c);
+    c = mfma(a.mid, b.hi, c);
+    c = mfma(a.hi, b.mid, c);
+    return mfma(a.hi, b.hi, c);
+}
+// the float32 state against an exact bf16 B operand
+__device__ __forceinline__ f32x4 mma(const Frag2 &a, const Frag<false> &b, f32x4 c) {
+    c = mfma(a.hi, b.x, c);
+    return mfma(a.lo, b.x, c);
 }
 
 // 8 floats -> fragment (bf16, or bf16 high part + bf16 remainder)
@@ -101,7 +118,18 @@ __device__ __forceinline__ void set_frag(Frag<false> &f, const float *x) {
 __device__ __forceinline__ void set_frag(Frag<true> &f, const float *x) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        bf16 h = (bf16)x[e];
+        const bf16 h = (bf16)x[e];
+        const float r = x[e] - (float)h;  // exact
+        const bf16 md = (bf16)r;
+        f.hi[e] = h;
+        f.mid[e] = md;
+        f.lo[e] = (bf16)(r - (float)md);  // r - md exact
+    }
+}
+__device__ __forceinline__ void set_frag(Frag2 &f, const float *x) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bf16 h = (bf16)x[e];
         f.hi[e] = h;
         f.lo[e] = (bf16)(x[e] - (float)h);
     }
@@ -512,7 +540,10 @@ __global__ __launch_bounds__(64 * NW, 1) void mlstm_chunk_kernel(FwdArgs a) {
             for (int x = 0; x < MYT; ++x) St[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                F ac[NBT];
+                // C' in parts for either I/O dtype (three against float32 q,
+                // high part and remainder against bf16 q): a read-out through
+                // C' rounded to bf16 alone loses tokens whose C'^T q cancels
+                typename std::conditional<SPLIT, Frag<true>, Frag2>::type ac[NBT];
 #pragma unroll
                 for (int bt = 0; bt < NBT; ++bt) {
                     const float x[8] = {Cr[2 * ks][bt][0], Cr[2 * ks][bt][1], Cr[2 * ks][bt][2],
