@@ -1,5 +1,5 @@
-"""Seeded random-shape parity sweep of the forward, the recurrent step and the
-backward against the float64 oracle.
+"""Seeded random-shape parity sweep of the forward, the recurrent step, the
+backward, the layer forward and the sLSTM against the float64 oracles.
 
 The fixed cases elsewhere pick their shapes by hand (tile edges, the
 workloads' own sizes).  Here the head sizes, sequence length, chunk, I/O
@@ -17,11 +17,13 @@ import torch
 from tests import parity as PT
 from tests.test_gpu_backward import compare as bwd_compare, run_gpu as bwd_gpu, run_oracle as bwd_oracle
 from tests.test_gpu_step import compare_steps, oracle_steps, run_steps
+from tests.test_gpu_layer import compare as layer_compare, run_gpu as layer_gpu, run_oracle as layer_oracle
+from tests.test_gpu_slstm import compare as slstm_compare, run_gpu as slstm_gpu, run_oracle as slstm_oracle
 from xlstm_mlstm_matrix_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
 
-N_FWD, N_STEP, N_BWD = 48, 16, 12
+N_FWD, N_STEP, N_BWD, N_LAYER, N_SLSTM = 48, 16, 12, 12, 12
 # draws kept from a wider run, each of which once failed: 183 (float32, d_qk
 # 176, chunk 32: the first token's q.k cancels ~7500-fold, beyond what
 # operands of ~16 bits resolve to 2e-3)
@@ -121,3 +123,39 @@ def test_bwd_sweep(i):
         gpu = [gpu[0][:, 1:]] + list(gpu[1:])
         ref = [ref[0][:, 1:]] + ref[1:]
     bwd_compare(gpu, ref, io, f"bwd sweep {i}", state_grad=state)
+
+
+@pytest.mark.parametrize("i", range(N_LAYER))
+def test_layer_sweep(i):
+    rng = _draw(7700 + i)
+    io = ("f32", "bf16")[int(rng.integers(2))]
+    H = int(rng.integers(1, 5))
+    dk = 16 * int(rng.integers(1, 17))
+    dv = 16 * int(rng.integers(1, 33))
+    d_model = 8 * int(rng.integers(4, 65))
+    B = int(rng.integers(1, 4))
+    T = int(rng.integers(1, 301))
+    chunk = int(rng.choice([16, 32, 64, 128]))
+    state = bool(rng.integers(2))
+    print(f"[case] layer sweep {i}: io={io} B={B} T={T} d_model={d_model} H={H} dk={dk} dv={dv} "
+          f"chunk={chunk} state={state}", flush=True)
+    init = I.layer_workload("layer_small").init_state if state else None
+    w = I.layer_workload("layer_small", io=io, B=B, T=T, d_model=d_model, H=H, d_qk=dk, d_v=dv, chunk=chunk,
+                         init_state=init)
+    d = I.gen_layer(w)
+    layer_compare(layer_gpu(d, chunk), layer_oracle(d, io), io, f"layer sweep {i}")
+
+
+@pytest.mark.parametrize("i", range(N_SLSTM))
+def test_slstm_sweep(i):
+    rng = _draw(7900 + i)
+    io = ("f32", "bf16")[int(rng.integers(2))]
+    d = 16 * int(rng.integers(1, 9))
+    B = int(rng.integers(1, 4))
+    H = int(rng.integers(1, 5))
+    T = int(rng.integers(1, 301))
+    state = bool(rng.integers(2))
+    print(f"[case] slstm sweep {i}: io={io} B={B} H={H} T={T} d={d} state={state}", flush=True)
+    w = I.slstm_workload("slstm_small", io=io, B=B, H=H, T=T, d=d, state=state)
+    g = I.gen_slstm(w)
+    slstm_compare(slstm_gpu(g), slstm_oracle(g), io, f"slstm sweep {i}")
