@@ -44,6 +44,13 @@
  *    returns MLSTM_ERR_HIP.  No exception crosses the ABI.
  *  - Supported shapes: 1 <= d_qk <= 256 and 1 <= d_v <= 512, both multiples
  *    of 16; chunk in {16, 32, 64, 128}; any T >= 1; B, H >= 1.
+ *  - Gate values: i~ may be any float including -inf (an input gate of 0).
+ *    f~ must be finite for the chunkwise calls (forward and backward): they
+ *    work with in-chunk cumulative sums of f~, so f~ = -inf (a forget gate
+ *    of exactly 0) yields NaN, and very negative values lose float32
+ *    precision there (about ulp(sum of a chunk's f~) in every decay, ~1e-3
+ *    relative at f~ = -1e4).  A log-sigmoid of any finite float is finite.
+ *    mlstm_step takes each gate alone and accepts f~ = -inf.
  *  - chunk is the longest token block the caller allows between two state
  *    passes.  The chunkwise form computes the same recurrence for every
  *    block length, so where the tiles of the requested chunk do not fit in a
