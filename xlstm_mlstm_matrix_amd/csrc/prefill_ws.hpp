@@ -56,7 +56,7 @@ struct WsCfg {
     static constexpr int GTF = 6 * L + 8;             // gate table floats (as Bf16Cfg)
     static constexpr size_t LDS_BYTES = 2 * (3 * (size_t)L * DKP + (size_t)L * BV) +
                                         16 * (size_t)NT * NCT * 64 + 4 * (2 * (size_t)GTF + 2 * (size_t)DKP) +
-                                        2 * 2 * 2 * (size_t)DKP;
+                                        2 * 2 * 2 * (size_t)DKP + 2 * (size_t)L;
     static_assert(NT == NW - NSW, "one token tile per intra wavefront");
     static_assert(NAT % 4 == 0, "n' tiles spread over the state wavefronts");
     static_assert(QG >= 8, "swizzle needs 8 granules per row");
@@ -188,6 +188,8 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     // (buffer c & 1 holds n' before chunk c)
     __shared__ __attribute__((aligned(16))) float nsh[2][DKP];
     __shared__ __attribute__((aligned(16))) bf16 nhl[2][2][DKP];
+    // zeros: the B operand columns of the n' update other than its group's
+    __shared__ __attribute__((aligned(16))) bf16 nzero[L];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -223,6 +225,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     const float *fgg = a.fg + (size_t)bh * T;
 
     for (int e = tid; e < 2 * GTF; e += Cfg::NTH) (&gt[0][0])[e] = 0.0f;
+    for (int e = tid; e < L; e += Cfg::NTH) nzero[e] = (bf16)0.0f;
 
     // ---- initial state
     const size_t rec = seg_state_floats(dk, dv);
@@ -458,22 +461,20 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                     return cat8(tr_read(rowblock + kb0 + h + ((g ^ kx0) << 3)),
                                 tr_read(rowblock + kb1 + h + ((g ^ kx1) << 3)));
                 };
-                // n' of row tiles s + 4 x: the old value (read now, used at the
-                // end), K^T w as MFMAs with w's high part and remainder in every
-                // column of the B operand (every lane gets K^T w for its rows);
-                // the row tile is picked from the last four fragments by selects
-                // on the wavefront index
+                // n' of row tiles s + 4 x (x < NXG): K^T w as MFMAs whose B
+                // operand holds w (high part, then remainder) in column x only,
+                // zeros elsewhere, all groups into one pair of accumulators, so
+                // that lane (x, g4) ends with group x's rows 4 g4 .. 4 g4 + 3
+                // and the lanes x < NXG finish one group each; the old value is
+                // read now, used at the end.  The row tile is picked from the
+                // last four fragments by selects on the wavefront index.
                 // (full pass only: in the state-only pass the otherwise idle
                 // intra wavefronts update n', with nprime_intra)
+                constexpr int NXG = NAT / 4;
                 unsigned sm0 = 0u - (unsigned)(s & 1), sm1 = 0u - (unsigned)((s >> 1) & 1);
                 asm volatile("" : "+s"(sm0), "+s"(sm1));
-                f32x4 nold[NAT / 4], nacc_h[NAT / 4], nacc_l[NAT / 4];
-    #pragma unroll
-                for (int x = 0; x < NAT / 4; ++x) {
-                    if constexpr (!SO) nold[x] = *reinterpret_cast<const f32x4 *>(&nsh[nb][crow(s + 4 * x, 0)]);
-                    nacc_h[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    nacc_l[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
+                f32x4 nold = {0.f, 0.f, 0.f, 0.f}, nacc_h = {0.f, 0.f, 0.f, 0.f}, nacc_l = nacc_h;
+                if constexpr (!SO) nold = *reinterpret_cast<const f32x4 *>(&nsh[nb][crow(s + 4 * (l16 < NXG ? l16 : 0), 0)]);
     #pragma unroll
                 for (int js = 0; js < L / 32; ++js) {
                     const bf16 *k0 = K + 32 * js * DKP;
@@ -497,8 +498,16 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                         for (int e = 0; e < 8; ++e) bw[bt][e] = (bf16)((float)vv[e] * w8[e]);
                     }
                     const bf16 *W2 = reinterpret_cast<const bf16 *>(&G[5 * LP]);
-                    const bf16x8 bnh = *reinterpret_cast<const bf16x8 *>(W2 + 32 * js + 8 * g4);
-                    const bf16x8 bnl = *reinterpret_cast<const bf16x8 *>(W2 + LP + 32 * js + 8 * g4);
+                    bf16x8 bnh[NXG], bnl[NXG];
+                    if constexpr (!SO) {
+    #pragma unroll
+                        for (int x = 0; x < NXG; ++x) {
+                            const bool mine = l16 == x;
+                            const bf16 *sh = mine ? W2 : nzero, *sl = mine ? W2 + LP : nzero;
+                            bnh[x] = *reinterpret_cast<const bf16x8 *>(sh + 32 * js + 8 * g4);
+                            bnl[x] = *reinterpret_cast<const bf16x8 *>(sl + 32 * js + 8 * g4);
+                        }
+                    }
                     // K^T fragments fetched four row tiles ahead (the reads'
                     // latency under load is several MFMA pairs), in a ring of
                     // eight that still holds a group of four when it completes
@@ -515,28 +524,25 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                         for (int bt = 0; bt < 2; ++bt) Cr[at][bt] = mfma(a0, bw[bt], Cr[at][bt]);
                         if (!SO && (at & 3) == 3) {  // compile-time: the group at - 3 .. at is complete
                             const bf16x8 fn = pick4(ak[(at - 3) & 7], ak[(at - 2) & 7], ak[(at - 1) & 7], a0, sm0, sm1);
-                            nacc_h[at >> 2] = mfma(fn, bnh, nacc_h[at >> 2]);
-                            nacc_l[at >> 2] = mfma(fn, bnl, nacc_l[at >> 2]);
+                            nacc_h = mfma(fn, bnh[at >> 2], nacc_h);
+                            nacc_l = mfma(fn, bnl[at >> 2], nacc_l);
                         }
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 // n' <- decay n' + K^T w into buffer nb ^ 1 (read after barrier Y)
-                if (!SO && l16 == 0) {
+                if (!SO && l16 < NXG) {  // lane (x, g4): rows 4 g4 .. +3 of group x = l16
+                    const int r0 = crow(s + 4 * l16, 0);
+                    const f32x4 nn = nold * s_last + (nacc_h + nacc_l);
+                    *reinterpret_cast<f32x4 *>(&nsh[nb ^ 1][r0]) = nn;
+                    bf16x4 hi, lo;
     #pragma unroll
-                    for (int x = 0; x < NAT / 4; ++x) {
-                        const int r0 = crow(s + 4 * x, 0);
-                        const f32x4 nn = nold[x] * s_last + (nacc_h[x] + nacc_l[x]);
-                        *reinterpret_cast<f32x4 *>(&nsh[nb ^ 1][r0]) = nn;
-                        bf16x4 hi, lo;
-    #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            hi[r] = (bf16)nn[r];
-                            lo[r] = (bf16)(nn[r] - (float)hi[r]);
-                        }
-                        *reinterpret_cast<bf16x4 *>(&nhl[nb ^ 1][0][r0]) = hi;
-                        *reinterpret_cast<bf16x4 *>(&nhl[nb ^ 1][1][r0]) = lo;
+                    for (int r = 0; r < 4; ++r) {
+                        hi[r] = (bf16)nn[r];
+                        lo[r] = (bf16)(nn[r] - (float)hi[r]);
                     }
+                    *reinterpret_cast<bf16x4 *>(&nhl[nb ^ 1][0][r0]) = hi;
+                    *reinterpret_cast<bf16x4 *>(&nhl[nb ^ 1][1][r0]) = lo;
                 }
         };
         role_sync<63>();
