@@ -181,7 +181,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) bf16 Ks[2][L * DKP];  // K of even / odd chunks
     __shared__ __attribute__((aligned(16))) bf16 Vs[L * BV];
     __shared__ __attribute__((aligned(16))) f32x4 Xch[NT][NCT][64];  // scaled read-out, accumulator layout
-    // gate tables (double buffered): u, r, s, floor, w [L] floats, w as bf16
+    // gate tables (double buffered): u, r (times log2 e), s, floor, w [L] floats, w as bf16
     // high/low pairs [L], then scalars (m after, decay, sum f~)
     __shared__ __attribute__((aligned(16))) float gt[2][GTF];
     // n' (true scale) and as bf16 high part and remainder, double buffered
@@ -339,8 +339,9 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
         const float r_last = __shfl(r, L - 1, 64);
         const float b_last = __shfl(b, L - 1, 64);
         const float w = exp_e(u - r_last);
-        G[lane] = u;
-        G[LP + lane] = r;
+        // u and r in base-2 units: P's weights are then one exp2 of a difference
+        G[lane] = u * 1.4426950408889634f;
+        G[LP + lane] = r * 1.4426950408889634f;
         G[2 * LP + lane] = exp_e(m_before - r);
         G[3 * LP + lane] = exp_e(-(b + r));
         G[4 * LP + lane] = w;
@@ -742,7 +743,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int j = 16 * jt + 4 * g4 + r;
-                        pv[r] = (j <= irow) ? St[jt][r] * exp_e(u4[r] - ri) : 0.0f;
+                        pv[r] = (j <= irow) ? St[jt][r] * __builtin_amdgcn_exp2f(u4[r] - ri) : 0.0f;
                     }
                     rowsum += (pv[0] + pv[1]) + (pv[2] + pv[3]);
                     Pb[jt] = bf16x4{(bf16)pv[0], (bf16)pv[1], (bf16)pv[2], (bf16)pv[3]};
@@ -794,8 +795,9 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
             int ln2 = lane;
             asm volatile("" : "+v"(ln2));
             const int irow2 = 16 * it + (ln2 & 15);
+            // h = a sigmoid(o~) / d = a / (d + d e^{-o~}): one reciprocal per value
             const float den = G[2 * LP + irow2] * qn + rowsum;
-            const float inv = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), G[3 * LP + irow2]));
+            const float dd = fmaxf(fabsf(den), G[3 * LP + irow2]);
             const auto rh = __builtin_amdgcn_make_buffer_rsrc((void *)(hg + (size_t)tc * dv), 0, nrow * dv * 2, kWsBuf);
 #pragma unroll
             for (int m = 0; m < NHS; ++m) {
@@ -805,7 +807,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                     const unsigned u = orw[m][e >> 1];
                     const float ox = __uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16));
                     const float a = acc[2 * m + (e >> 2)][e & 3];
-                    hv[e] = (bf16)(a * inv * __builtin_amdgcn_rcpf(1.0f + exp_e(-ox)));
+                    hv[e] = (bf16)(a * __builtin_amdgcn_rcpf(fmaf(dd, exp_e(-ox), dd)));
                 }
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hv), rh,
                                                        2u * (unsigned)(irow2 * dv + 32 * m + 8 * g4), 0, 0);
