@@ -91,33 +91,20 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // h stores (32-bit data format; raw addressing, range-checked)
 constexpr int kWsBuf = 0x00020000;
 
-// Packed bf16 pairs (-1, 0) and (0, -1), the operands that pick one high
-// part out of a pair in split8_pk.  They are built in scalar registers from
-// their bit patterns behind an opaque move: folded into an inline constant of
-// the dot-product instruction, the first of them reads back as a different
-// pair on gfx950 (wrong remainders for every even value).
-struct SplitMasks {
-    bf16x2 neg_lo, neg_hi;
-};
-__device__ __forceinline__ SplitMasks split_masks() {
-    unsigned lo = 0x0000bf80u, hi = 0xbf800000u;
-    asm volatile("" : "+s"(lo), "+s"(hi));
-    return {__builtin_bit_cast(bf16x2, lo), __builtin_bit_cast(bf16x2, hi)};
-}
-
-// Split 8 floats into bf16 high parts (round to nearest even, converted in
-// pairs) and bf16 remainders.  The remainder x - hi is exact in float32; it
-// comes from a bf16 dot product of the packed high parts with (-1, 0) or
-// (0, -1) accumulated onto x, one instruction per value.
-__device__ __forceinline__ void split8_pk(const float *x, const SplitMasks &m, bf16x8 &hi, bf16x8 &lo) {
-    const bf16x2 neg_lo = m.neg_lo, neg_hi = m.neg_hi;
+// Split 8 floats into bf16 high parts and bf16 remainders, both rounded to
+// nearest even and converted in pairs.  The remainder x - hi is exact in
+// float32: the high parts are unpacked by a shift and a mask and subtracted.
+// Six instructions per pair, two of them conversions (on gfx950 conversion and
+// dot-product instructions make no progress while the matrix core runs the
+// other wavefront's MFMAs on this SIMD; plain ALU instructions do).
+__device__ __forceinline__ void split8_rr(const float *x, bf16x8 &hi, bf16x8 &lo) {
     bf16x2 h[4], l[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const f32x2 v = {x[2 * p], x[2 * p + 1]};
         h[p] = __builtin_convertvector(v, bf16x2);
-        const f32x2 r = {__builtin_amdgcn_fdot2_f32_bf16(h[p], neg_lo, v.x, false),
-                         __builtin_amdgcn_fdot2_f32_bf16(h[p], neg_hi, v.y, false)};
+        const unsigned hb = __builtin_bit_cast(unsigned, h[p]);
+        const f32x2 r = {v.x - __uint_as_float(hb << 16), v.y - __uint_as_float(hb & 0xffff0000u)};
         l[p] = __builtin_convertvector(r, bf16x2);
     }
     hi = bf16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
@@ -430,7 +417,6 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
     // barriers (one after the prologue, two per chunk).
     if (is_state) {
         // ========================= state wavefronts =========================
-        const SplitMasks smask = split_masks();
         // C'/sigma' += K^T ((w/sigma') (x) V) with sigma' = sigma * decay, and
         // n' (true scale) from buffer nb into nb ^ 1: the update with the chunk
         // whose K and V tiles and gate table are given.  The loop over the row
@@ -584,7 +570,7 @@ __global__ __launch_bounds__(512, 1) void mlstm_ws_kernel(FwdArgs a) {
                         const float x[8] = {Cr[2 * kk][bt][0],     Cr[2 * kk][bt][1],     Cr[2 * kk][bt][2],
                                             Cr[2 * kk][bt][3],     Cr[2 * kk + 1][bt][0], Cr[2 * kk + 1][bt][1],
                                             Cr[2 * kk + 1][bt][2], Cr[2 * kk + 1][bt][3]};
-                        split8_pk(x, smask, ach[bt], acl[bt]);
+                        split8_rr(x, ach[bt], acl[bt]);
                     }
 #pragma unroll
                     for (int t = 0; t < NT; ++t)
